@@ -1,0 +1,200 @@
+/*
+ * dllm.h - C ABI of the Flash-Cache per-layer denoising-step library (gfx950).
+ *
+ * Pages cited:
+ *   [FD]  "Flash-dLLM: IO-Aware KV Caching and Parallel Decoding for Fast,
+ *         Memory-Efficient Diffusion LLMs" (paper summary page): sections
+ *         核心方法 (core method), 方法步骤详情 (Algorithm 2, formula (2)),
+ *         研究动机 (motivation), 技术新颖性 (novelty).
+ *   [AIP] "Flash-dLLM 是什麼？擴散語言模型推論快 11 倍" (aiposthub explainer):
+ *         Flash-Cache, selective refresh and Flash-Verify sections.
+ *
+ * One layer of one denoising step is
+ *     dllm_map_slots            logical position -> flat cache row of each query row
+ *     dllm_qkv_rope_cachewrite  x W^T, rotary embedding, q out, K/V into the cache
+ *     dllm_sched_attention      paged bidirectional attention + formula (2) term
+ * and after the last layer of the step
+ *     dllm_topk_tracked         next step's tracked positions
+ * dllm_build_block_table sets up (and validates) the page table once.
+ *
+ * Conventions shared by every entry point:
+ *   - Ownership: the caller allocates and owns every buffer; the library never
+ *     allocates or frees device memory and keeps no state between calls.  The
+ *     workspace of a call is caller memory whose size comes from the matching
+ *     *_workspace() query; it must be zero-filled before its first use, every
+ *     call returns it with its counters at zero again, and two calls in flight
+ *     at once must not share one workspace.
+ *   - Pointers named "host" are host memory; every other pointer is device
+ *     memory of the current HIP device.  All device work is enqueued on
+ *     `stream` and is asynchronous unless stated; buffers must stay valid until
+ *     the stream has executed the work.
+ *   - Errors: the return value is the only error channel.  Argument errors the
+ *     host can see return before any work is enqueued and leave every output
+ *     untouched.  Device-side indices that are out of range (a page id outside
+ *     the pool, a slot outside the cache) are never dereferenced: the affected
+ *     key is treated as hidden, the affected row is not written.
+ *   - Dtypes: DLLM_BF16 means x, W, the caches, q and o are bf16 (accumulation
+ *     in fp32); DLLM_F32 means they are all fp32.
+ *   - Layouts are row-major and dense.  A cache is [cache_rows, n_heads*head_dim]:
+ *     one row per token slot, head h in columns h*head_dim .. h*head_dim+head_dim-1
+ *     ([FD] 方法步骤详情 step 1: the flat per-layer cache of B*N_max rows).
+ *     Slot s lives in physical page s / page_size.
+ */
+#ifndef DLLM_H
+#define DLLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DLLM_OK = 0,
+    DLLM_ERR_INVALID_ARG = -1,   /* null pointer, negative size, inconsistent sizes */
+    DLLM_ERR_UNSUPPORTED = -2,   /* a shape or dtype this library has no kernel for */
+    DLLM_ERR_OUT_OF_RANGE = -3,  /* an index outside its table, pool or cache; a duplicate slot */
+    DLLM_ERR_HIP = -4            /* a HIP runtime call or launch failed */
+} dllm_status;
+
+typedef enum { DLLM_F32 = 0, DLLM_BF16 = 1 } dllm_dtype;
+
+/* Text for a status code (static storage). */
+const char* dllm_status_string(int status);
+/* Library ABI version, major * 100 + minor. */
+int dllm_version(void);
+
+/*
+ * a0, set-up: block table over one shared page pool, and optionally the cache
+ * slot of host-given query rows.  [FD] 核心方法 / 技术新颖性: a block table maps
+ * each sequence's query blocks to its KV blocks; [FD] 方法步骤详情 step 1: the
+ * cache is allocated once and never reallocated.
+ *
+ *   n_seq, page_size, pool_pages, max_pages  sizes (page_size > 0)
+ *   seq_pages  host int32[n_seq]     pages taken by each sequence (<= max_pages)
+ *   pool_perm  host int32[pool_pages] a permutation of 0..pool_pages-1; sequence
+ *              b takes the next seq_pages[b] entries of it, in order
+ *   page_table device int32[n_seq*max_pages] out: physical page of logical page j
+ *              of sequence b at [b*max_pages + j], -1 past the sequence's pages
+ *   n_rows, cu_q (host int32[n_seq+1]), q_logical (host int32[n_rows]), slot
+ *              (device int32[n_rows]): optional (all NULL / 0 or all set); the
+ *              slot of row r of sequence b is page_table[b][l/page_size]*page_size
+ *              + l%page_size with l = q_logical[r]
+ * Errors: INVALID_ARG for null/negative/inconsistent arguments or a cu_q that is
+ * not non-decreasing from 0 to n_rows; OUT_OF_RANGE when sum(seq_pages) >
+ * pool_pages, seq_pages[b] > max_pages, pool_perm is not a bijection, a logical
+ * position lies beyond its sequence's pages, or two rows share one slot.
+ * Blocking: returns after the copies to the device have completed.
+ */
+int dllm_build_block_table(int n_seq, int page_size, int pool_pages, int max_pages,
+                           const int32_t* seq_pages, const int32_t* pool_perm,
+                           int32_t* page_table,
+                           int n_rows, const int32_t* cu_q, const int32_t* q_logical,
+                           int32_t* slot, hipStream_t stream);
+
+/*
+ * a0, per step, on the device: cache slot of each query row from its logical
+ * position (same formula as above).  cu_q int32[n_seq+1], q_logical int32[n_rows],
+ * page_table int32[n_seq*max_pages] are device arrays; slot int32[n_rows] out.
+ * A row whose logical position is negative, beyond max_pages*page_size, on a -1
+ * table entry or on a page >= pool_pages gets slot -1 (the cache write then
+ * skips it).  Duplicate slots are not detected here (dllm_build_block_table
+ * checks host-side row sets).  Asynchronous.
+ */
+int dllm_map_slots(int n_seq, int n_rows, int page_size, int max_pages, int pool_pages,
+                   const int32_t* cu_q, const int32_t* q_logical, const int32_t* page_table,
+                   int32_t* slot, hipStream_t stream);
+
+/*
+ * a1-a3: fused QKV projection + rotary embedding + cache write.  [FD] 核心方法:
+ * one kernel projects, rotates and writes K/V straight into the preallocated
+ * flat cache with no intermediate tensors in memory; [FD] 研究动机: the unfused
+ * four-kernel pipeline is bound by memory traffic.
+ *
+ *   n_rows R (>= 0), d_model (input width, multiple of 64), n_heads H, head_dim D
+ *   (64 or 128; H*D a multiple of 128), rope_base > 0
+ *   x        [R, d_model]           layer input rows (query rows of this step)
+ *   w_qkv    [3*H*D, d_model]       out x in: rows 0..HD-1 give Q, HD..2HD-1 K,
+ *                                   2HD..3HD-1 V; head h is rows h*D..h*D+D-1 of each
+ *   pos      int32[R]               rotary position of each row
+ *   slot     int32[R]               cache row written by each row (-1: none)
+ *   q_out    [R, H*D]               out: rotated q
+ *   k_cache, v_cache [cache_rows, H*D]  rows slot[r] overwritten with rotated k
+ *                                   and with v; no other row is touched
+ * Rotary embedding is rotate-half: for i < D/2, theta_i = rope_base^(-2i/D) and
+ * the pair (t_i, t_{i+D/2}) turns by pos*theta_i.  Results are rounded once to
+ * the output dtype.  Slots of one call must be pairwise distinct.
+ * Errors: INVALID_ARG, UNSUPPORTED (D, H*D, d_model, dtype), INVALID_ARG when
+ * workspace_bytes is below dllm_qkv_rope_cachewrite_workspace().
+ */
+size_t dllm_qkv_rope_cachewrite_workspace(dllm_dtype dt, int n_rows, int d_model, int n_heads,
+                                          int head_dim);
+int dllm_qkv_rope_cachewrite(dllm_dtype dt, int n_rows, int d_model, int n_heads, int head_dim,
+                             float rope_base, const void* x, const void* w_qkv,
+                             const int32_t* pos, const int32_t* slot, void* q_out,
+                             void* k_cache, void* v_cache, int64_t cache_rows,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * a4-a5: block-table scheduled bidirectional attention over the paged cache,
+ * every sequence's query rows in one launch with no padding, plus one layer's
+ * term of the tracked-set score.  [FD] 核心方法 / 技术新颖性: variable-length
+ * query blocks aligned to their KV blocks through the block table, mixing
+ * cache-phase windows and full refreshes; [FD] 方法步骤详情 step 2 (attention
+ * over the full cache) and step 4 (formula (2)).
+ *
+ *   n_seq B, n_rows R, n_heads H, head_dim D (bf16: 128; f32: 64 or 128), page_size
+ *   (16), max_kv (host upper bound of kv_len, > 0)
+ *   q          [R, H*D]            rotated queries; rows of sequence b are
+ *                                  cu_q[b] .. cu_q[b+1]-1 (int32[B+1], device)
+ *   k_cache, v_cache [cache_rows, H*D]  written by dllm_qkv_rope_cachewrite
+ *   page_table int32[B*max_pages]  as built by dllm_build_block_table
+ *   kv_len     int32[B]            keys of sequence b: logical 0..kv_len[b]-1
+ *   mask_bits  uint32[mask_words] or NULL (all keys visible).  If set, row i
+ *              (0-based within sequence b) sees key j iff bit j%32 of word
+ *              mask_off[b] + i*ceil(kv_len[b]/32) + j/32 is 1; mask_off int64[B]
+ *   mass_count int32[B] or NULL    the first mass_count[b] (<= max_mass_rows <= 128)
+ *              rows of sequence b are the masked-window rows of formula (2)
+ *   mass_accum float[B*n_cap]      mass_accum[b*n_cap + i] += (1/(H*m_b)) *
+ *              sum over heads and window rows of the probability of key i,
+ *              m_b = mass_count[b]; keys i >= n_cap are not recorded
+ *   o          [R, H*D]            out: attention output
+ * Scores are q.k/sqrt(D); a row that sees no key outputs zeros.
+ * Errors: INVALID_ARG (also when workspace_bytes is below the query),
+ * UNSUPPORTED (dtype/D/page_size).
+ */
+size_t dllm_sched_attention_workspace(dllm_dtype dt, int n_seq, int n_rows, int n_heads,
+                                      int head_dim, int max_kv, int n_cap);
+int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_heads, int head_dim,
+                         int page_size, int max_kv, const void* q, const int32_t* cu_q,
+                         const void* k_cache, const void* v_cache, int64_t cache_rows,
+                         const int32_t* page_table, int max_pages, const int32_t* kv_len,
+                         const uint32_t* mask_bits, const int64_t* mask_off, int64_t mask_words,
+                         const int32_t* mass_count, int max_mass_rows, float* mass_accum,
+                         int n_cap, void* o, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
+ * a6: per-sequence top-k of the accumulated score over eligible positions.
+ * [FD] 方法步骤详情 step 4: the top-k decoded tokens by formula (2), with the
+ * newly decoded tokens, form the next tracked set (the caller adds the new
+ * ones; `eligible` excludes them).
+ *
+ *   mass     float[B*n_cap]   scores (read; zeroed afterwards if clear_mass != 0)
+ *   eligible uint8[B*n_cap]   nonzero = candidate
+ *   idx      int32[B*k]       out: positions, highest score first, ties to the
+ *                             lower position, -1 padding
+ *   val      float[B*k]       out: their scores (0 padding)
+ *   count    int32[B]         out: min(k, number of candidates)
+ * Limits: 1 <= k <= 256, n_cap <= 8192.
+ */
+int dllm_topk_tracked(int n_seq, int n_cap, int k, float* mass, const uint8_t* eligible,
+                      int32_t* idx, float* val, int32_t* count, int clear_mass,
+                      hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DLLM_H */

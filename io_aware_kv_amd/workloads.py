@@ -25,6 +25,8 @@ Workloads (all synthetic, random-init; LLaDA-8B-shaped where stated):
   llada_b32  32 layers with distinct weights; 32 sequences of 2048 (prompt 1536
              + gen 512); cache-phase steps of 72 rows per sequence and full
              refresh steps of 2048 rows per sequence.
+  tiny_bf16  1 layer, d_model 256, 2 heads x 128, RoPE base 1e4, bf16; shaped
+             like tiny_f32 (a quick check of the bf16 kernels).
 
 Seeds: numpy PCG64 seeded with [1000 * workload_id + stream, ...]; streams are
 1 = weights (per layer), 2 = x (per step and layer), 3 = pool permutation,
@@ -41,7 +43,8 @@ import numpy as np
 PAGE = 16          # tokens per KV page
 BLOCK = 32         # generation block (decode granularity) of these workloads
 
-WORKLOAD_IDS = {"tiny_f32": 1, "llada_b1": 2, "mixed_b8": 3, "verify_b4": 4, "llada_b32": 5}
+WORKLOAD_IDS = {"tiny_f32": 1, "llada_b1": 2, "mixed_b8": 3, "verify_b4": 4, "llada_b32": 5,
+                "tiny_bf16": 6}
 
 
 @dataclass(frozen=True)
@@ -158,6 +161,9 @@ def make_workload(name: str, heavy: bool = False) -> Workload:
     len_rng = _rng(wid, 5)
     if name == "tiny_f32":
         shape = LayerShape(256, 4, 64, 1e4, "f32", 1, 8)
+        seqs = [_cache_seq(pos_rng, 128, 64, 1, 4, 32 + 4 + 8) for _ in range(2)]
+    elif name == "tiny_bf16":
+        shape = LayerShape(256, 2, 128, 1e4, "bf16", 1, 8)
         seqs = [_cache_seq(pos_rng, 128, 64, 1, 4, 32 + 4 + 8) for _ in range(2)]
     elif name == "llada_b1":
         shape = LayerShape(4096, 32, 128, 5e5, "bf16", 1, 32)

@@ -1,0 +1,134 @@
+"""CPU checks of the C-ABI library: it loads, exports every entry point that
+include/dllm.h declares, rejects bad arguments before touching the device,
+and its workspace queries are pure functions of the shapes.  No compute call
+is made (there is no GPU here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from io_aware_kv_amd import dllm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dllm.LIB_PATH):
+        from io_aware_kv_amd import build
+        build.build()
+    return dllm.load()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "dllm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dllm_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(dllm.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert dllm.version() == 100
+    assert dllm.status_string(0) == "ok"
+    assert "duplicate" in dllm.status_string(-3)
+
+
+NULL = None
+
+
+def bbt(lib, n_seq, page_size, pool_pages, max_pages, seq_pages, perm, table, n_rows=0, cu=None,
+        lg=None, slot=None):
+    arr = lambda a: None if a is None else np.ascontiguousarray(a, dtype=np.int32)
+    sp, pp, cu_, lg_ = arr(seq_pages), arr(perm), arr(cu), arr(lg)
+    ptr = lambda a: None if a is None else a.ctypes.data
+    return lib.dllm_build_block_table(n_seq, page_size, pool_pages, max_pages, ptr(sp), ptr(pp),
+                                      table, n_rows, ptr(cu_), ptr(lg_), slot, None)
+
+
+def test_block_table_errors_before_any_device_work(lib):
+    fake = ctypes.c_void_p(0x1000)     # never dereferenced: every case fails validation first
+    E_ARG, E_RANGE = -1, -3
+    assert bbt(lib, 2, 16, 4, 2, [3, 1], [0, 1, 2, 3], fake) == E_RANGE      # > max_pages
+    assert bbt(lib, 2, 16, 4, 4, [3, 2], [0, 1, 2, 3], fake) == E_RANGE      # > pool
+    assert bbt(lib, 1, 16, 4, 4, [2], [0, 1, 1, 3], fake) == E_RANGE         # not a bijection
+    assert bbt(lib, 1, 16, 4, 4, [2], [0, 1, 2, 4], fake) == E_RANGE
+    assert bbt(lib, 1, 16, 4, 4, [-1], [0, 1, 2, 3], fake) == E_ARG
+    assert bbt(lib, 1, 0, 4, 4, [1], [0, 1, 2, 3], fake) == E_ARG
+    assert bbt(lib, 1, 16, 4, 4, [1], [0, 1, 2, 3], None) == E_ARG          # null table
+    # rows: logical beyond the sequence, duplicate slot, bad cu_q
+    assert bbt(lib, 1, 16, 4, 4, [1], [0, 1, 2, 3], fake, 1, [0, 1], [16], fake) == E_RANGE
+    assert bbt(lib, 1, 16, 4, 4, [1], [0, 1, 2, 3], fake, 2, [0, 2], [3, 3], fake) == E_RANGE
+    assert bbt(lib, 1, 16, 4, 4, [1], [0, 1, 2, 3], fake, 2, [0, 1], [3, 4], fake) == E_ARG
+    assert bbt(lib, 2, 16, 4, 4, [1, 1], [0, 1, 2, 3], fake, 2, [0, 2, 1], [3, 4], fake) == E_ARG
+
+
+def test_kernel_entry_points_reject_bad_shapes(lib):
+    fake = ctypes.c_void_p(0x1000)
+    f = lib.dllm_qkv_rope_cachewrite
+    args = lambda dt, R, d, H, D, base: (dt, R, d, H, D, base, fake, fake, fake, fake, fake, fake, fake,
+                                          1024, fake, 1 << 30, None)
+    assert f(*args(1, 8, 4096, 32, 96, 5e5)) == -2          # head_dim 96
+    assert f(*args(1, 8, 4000, 32, 128, 5e5)) == -2         # d_model not a multiple of 64
+    assert f(*args(1, 8, 4096, 3, 64, 5e5)) == -2           # H*D not a multiple of 128
+    assert f(*args(7, 8, 4096, 32, 128, 5e5)) == -2         # dtype
+    assert f(*args(1, -1, 4096, 32, 128, 5e5)) == -1
+    assert f(*args(1, 8, 4096, 32, 128, 0.0)) == -1         # rope base
+    assert f(1, 8, 4096, 32, 128, 5e5, None, fake, fake, fake, fake, fake, fake, 1024, fake, 1 << 30,
+             None) == -1                                     # null x
+    need = lib.dllm_qkv_rope_cachewrite_workspace(1, 72, 4096, 32, 128)
+    assert need > 0
+    assert f(1, 72, 4096, 32, 128, 5e5, fake, fake, fake, fake, fake, fake, fake, 1024, fake, need - 1,
+             None) == -1                                     # workspace too small
+    assert f(*args(1, 0, 4096, 32, 128, 5e5)) == 0           # empty: nothing to do
+
+    a = lib.dllm_sched_attention
+    def att(dt=1, n_seq=1, R=8, H=32, D=128, page=16, max_kv=512, mask=None, off=None, words=0,
+            mass=None, max_mass=0, macc=None, n_cap=512, ws=1 << 30, max_pages=32):
+        return a(dt, n_seq, R, H, D, page, max_kv, fake, fake, fake, fake, 1 << 16, fake, max_pages,
+                 fake, mask, off, words, mass, max_mass, macc, n_cap, fake, fake, ws, None)
+    assert att(D=64) == -2                                   # bf16 kernel is D = 128
+    assert att(page=32) == -2
+    assert att(max_kv=0) == -1
+    assert att(n_seq=2000) == -2
+    assert att(mask=fake, off=None, words=0) == -1           # mask without offsets
+    assert att(mass=fake, macc=None) == -1                   # half of the mass arguments
+    assert att(mass=fake, macc=fake, max_mass=200) == -2     # more than 128 window rows
+    assert att(ws=16) == -1
+    assert att(max_pages=5000) == -2
+    assert att(dt=0, D=64, max_kv=10000) == -2               # fp32 path key limit
+
+    t = lib.dllm_topk_tracked
+    assert t(1, 512, 0, fake, fake, fake, fake, fake, 0, None) == -1
+    assert t(1, 512, 300, fake, fake, fake, fake, fake, 0, None) == -2
+    assert t(1, 9000, 32, fake, fake, fake, fake, fake, 0, None) == -2
+    assert t(1, 512, 32, None, fake, fake, fake, fake, 0, None) == -1
+    assert lib.dllm_map_slots(0, 8, 16, 4, 4, fake, fake, fake, fake, None) == -1
+
+
+def test_workspace_queries_are_pure_and_monotone(lib):
+    q = lib.dllm_qkv_rope_cachewrite_workspace
+    assert q(1, 72, 4096, 32, 128) == q(1, 72, 4096, 32, 128)
+    assert q(0, 72, 256, 4, 64) == 0                          # fp32 path needs none
+    assert q(1, 65536, 4096, 32, 128) == 0                    # enough tiles: no split-K
+    w = lib.dllm_sched_attention_workspace
+    assert w(1, 1, 72, 32, 128, 512, 512) > 0
+    assert w(1, 32, 2304, 32, 128, 2048, 2048) >= 32 * 32 * 2048 * 4   # per-head mass partials
+    assert w(1, 1, 72, 32, 128, 512, 512) == w(1, 1, 72, 32, 128, 512, 512)
+
+
+def test_pack_mask_layout():
+    rng = np.random.default_rng(0)
+    vis = [rng.random((3, 70)) < 0.5, rng.random((2, 33)) < 0.5]
+    bits, off = dllm.pack_mask(vis)
+    assert off.tolist() == [0, 3 * 3]
+    for b, v in enumerate(vis):
+        words = (v.shape[1] + 31) // 32
+        for i in range(v.shape[0]):
+            for j in range(v.shape[1]):
+                w = int(bits[off[b] + i * words + j // 32])
+                assert ((w >> (j % 32)) & 1) == int(v[i, j])

@@ -1,0 +1,100 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Step 0 of every workload is a full refresh (every position queried and
+written); step 1 is the workload's own step (cache phase, mixed batch or
+verify views).  Integer outputs (page table, slots, cache placement, top-k)
+are compared bit for bit; floating outputs within the tolerances in
+tests/parity.py; cache rows a step must not write are compared bit for bit
+against the sentinel they held.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from io_aware_kv_amd import workloads as W
+from parity import (MASS_TOL, TOL, Case, check_topk, close, device_bits, device_values, log)
+
+pytestmark = pytest.mark.gpu
+
+_CASES = {}
+
+
+def case(name, heavy=False):
+    key = (name, heavy)
+    if key not in _CASES:
+        _CASES[key] = Case(name, heavy)
+    return _CASES[key]
+
+
+def run_gpu_step(c: Case, step: int, gpu):
+    import torch
+    from io_aware_kv_amd.runner import FlashCacheRunner
+    wl = c.wl
+    rows = c.rows0 if step == 0 else c.rows1
+    x_raw = c.x0_raw if step == 0 else c.x1_raw
+    run = FlashCacheRunner(wl, device=gpu, layers=1)
+    if step == 0:
+        run.k_cache[0].copy_(run.to_device_array(c.k_init_raw))
+        run.v_cache[0].copy_(run.to_device_array(c.v_init_raw))
+    else:
+        run.k_cache[0].copy_(run.to_device_array(c.to_cache_raw(c.k1_in)))
+        run.v_cache[0].copy_(run.to_device_array(c.to_cache_raw(c.v1_in)))
+    k_before = device_bits(run.k_cache[0])
+    v_before = device_bits(run.v_cache[0])
+    st = run.upload_step(rows)
+    x = run.to_device_array(x_raw)
+    w = run.to_device_array(c.w_raw)
+    run.layer_step(st, x, w, 0)
+    mass = run.mass.cpu().numpy().copy()
+    run.topk(clear_mass=True)
+    torch.cuda.synchronize()
+    return {"run": run, "st": st, "k_before": k_before, "v_before": v_before, "mass": mass,
+            "page_table": run.page_table.cpu().numpy().reshape(wl.n_seq, wl.max_pages),
+            "slot": st.slot.cpu().numpy(), "q": device_values(st.q), "o": device_values(st.o),
+            "k_cache": device_values(run.k_cache[0]), "v_cache": device_values(run.v_cache[0]),
+            "k_bits": device_bits(run.k_cache[0]), "v_bits": device_bits(run.v_cache[0]),
+            "idx": run.top_idx.cpu().numpy(), "val": run.top_val.cpu().numpy(),
+            "cnt": run.top_cnt.cpu().numpy(), "mass_after": run.mass.cpu().numpy()}
+
+
+def compare_step(c: Case, g: dict, step: int, exact_topk: bool = False):
+    out = c.out0 if step == 0 else c.out1
+    top = c.top0 if step == 0 else c.top1
+    atol, rtol = TOL[c.kind]
+    # integer outputs, bit-exact
+    assert np.array_equal(g["page_table"], c.table.astype(np.int32))
+    assert np.array_equal(g["slot"], out["slots"].astype(np.int32))
+    written = np.zeros(g["k_bits"].shape[0], dtype=bool)
+    written[out["slots"]] = True
+    assert np.array_equal(g["k_bits"][~written], g["k_before"][~written]), "unwritten K rows changed"
+    assert np.array_equal(g["v_bits"][~written], g["v_before"][~written]), "unwritten V rows changed"
+    infos = [close(g["q"], out["q"], atol, rtol, "q_out"),
+             close(g["k_cache"][out["slots"]], out["k"], atol, rtol, "K rows"),
+             close(g["v_cache"][out["slots"]], out["v"], atol, rtol, "V rows"),
+             close(g["o"], out["o"], atol, rtol, "o")]
+    ma, mr = MASS_TOL[c.kind]
+    infos.append(close(g["mass"], out["mass"], ma, mr, "mass"))
+    assert not g["mass_after"].any(), "top-k did not clear the score"
+    check_topk(c, g["mass"], g["idx"], g["val"], g["cnt"], out["mass"], exact_set=exact_topk)
+    for i in infos:
+        log(f"   {c.wl.name} step{step} {i['what']}: max_abs={i['max_abs']:.3e} "
+            f"max/rms={i['max_over_rms']:.3e}")
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "tiny_bf16", "llada_b1", "mixed_b8", "verify_b4"])
+@pytest.mark.parametrize("step", [0, 1])
+def test_workload_step_parity(name, step, gpu):
+    log(f"[gpu] parity {name} step {step}")
+    c = case(name)
+    g = run_gpu_step(c, step, gpu)
+    compare_step(c, g, step)
+
+
+@pytest.mark.parametrize("name", ["llada_b1", "verify_b4"])
+def test_heavy_hitter_topk_exact(name, gpu):
+    """Planted heavy hitters (step-0 x rows scaled by 2) separate the top-k,
+    so the GPU's set must equal the oracle's exactly."""
+    log(f"[gpu] heavy-hitter top-k {name}")
+    c = case(name, heavy=True)
+    g = run_gpu_step(c, 0, gpu)
+    compare_step(c, g, 0, exact_topk=True)
