@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Benchmark of the Flash-Cache per-layer denoising step on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+slot map -> fused QKV + RoPE + cache write -> scheduled attention with the
+formula-(2) column mass -> top-k of the tracked set.  The default workload is
+the LLaDA-8B-shaped layer (d_model 4096, 32 heads x 128, bf16) with one
+sequence of 512 tokens in the cache phase: 72 refreshed rows (32 masked
+window + 8 newly decoded + 32 tracked).
+
+Metric: refreshed tokens/s per layer = rows refreshed per step / step time.
+Inputs are resident in HBM before timing starts.  To keep the 256 MB
+Infinity Cache from serving the weights and caches, the timed loop rotates
+over enough independent copies (weights, caches, inputs) to span >= 1 GiB.
+
+Prints ONE JSON line on stdout; diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="llada_b1", choices=["llada_b1", "mixed_b8", "verify_b4"])
+    p.add_argument("--rotate-gib", type=float, default=1.0)
+    p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="also run a plain device copy of this size (counter calibration)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from io_aware_kv_amd import dllm
+    from io_aware_kv_amd import workloads as W
+    from io_aware_kv_amd.runner import FlashCacheRunner
+
+    dllm.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = W.make_workload(args.workload)
+    sh = wl.shape
+    n_out = sh.n_heads * sh.head_dim
+
+    # ---- step 0 (full refresh) on the GPU fills the cache and picks the tracked rows ----
+    run = FlashCacheRunner(wl, device=dev, layers=1)
+    w_raw = W.weights(wl, 0)
+    w0 = run.to_device_array(w_raw)
+    rows0 = W.full_refresh_rows(wl)
+    st0 = run.upload_step(rows0)
+    x0 = run.to_device_array(W.activations(wl, rows0, 0))
+    run.layer_step(st0, x0, w0, 0)
+    run.topk(clear_mass=True)
+    idx = run.top_idx.cpu().numpy()
+    tracked = [idx[b][idx[b] >= 0] for b in range(wl.n_seq)]
+    rows1 = W.config_step_rows(wl, tracked)
+    R = rows1.n_rows
+    st = run.upload_step(rows1)
+    x1 = run.to_device_array(W.activations(wl, rows1, 1))
+    del st0, x0
+
+    # ---- buffer rotation over independent copies ----
+    per_copy = (w0.numel() * w0.element_size() + 2 * run.k_cache[0].numel() * run.k_cache[0].element_size()
+                + x1.numel() * x1.element_size())
+    copies = max(1, int(np.ceil(args.rotate_gib * (1 << 30) / per_copy)))
+    Ws, Ks, Vs, Xs = [w0], [run.k_cache[0]], [run.v_cache[0]], [x1]
+    for _ in range(copies - 1):
+        Ws.append(w0.clone()); Ks.append(run.k_cache[0].clone())
+        Vs.append(run.v_cache[0].clone()); Xs.append(x1.clone())
+    torch.cuda.synchronize()
+    eprint(f"[bench] {args.workload}: R={R} rows/step, {copies} copies x {per_copy / 2**20:.1f} MiB "
+           f"= {copies * per_copy / 2**30:.2f} GiB rotated")
+
+    def step(i):
+        c = i % copies
+        run.map_slots(st)
+        dllm.qkv_rope_cachewrite(Xs[c], Ws[c], st.pos, st.slot, st.q, Ks[c], Vs[c], sh.n_heads,
+                                 sh.head_dim, sh.rope_base, st.ws_qkv)
+        dllm.sched_attention(st.q, st.cu_q, Ks[c], Vs[c], run.page_table, wl.max_pages, st.kv_len, st.o,
+                             st.ws_attn, sh.n_heads, sh.head_dim, st.max_kv, mask_bits=st.mask_bits,
+                             mask_off=st.mask_off, mass_count=st.mass_count, max_mass_rows=st.max_mass,
+                             mass_accum=run.mass, n_cap=run.n_cap)
+        run.topk(clear_mass=True)
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- plain stream launches, HIP events around every kernel ----
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        c = i % copies
+        e = evs[i]
+        e[0].record(stream)
+        run.map_slots(st)
+        e[1].record(stream)
+        dllm.qkv_rope_cachewrite(Xs[c], Ws[c], st.pos, st.slot, st.q, Ks[c], Vs[c], sh.n_heads,
+                                 sh.head_dim, sh.rope_base, st.ws_qkv)
+        e[2].record(stream)
+        dllm.sched_attention(st.q, st.cu_q, Ks[c], Vs[c], run.page_table, wl.max_pages, st.kv_len, st.o,
+                             st.ws_attn, sh.n_heads, sh.head_dim, st.max_kv, mask_bits=st.mask_bits,
+                             mask_off=st.mask_off, mass_count=st.mass_count, max_mass_rows=st.max_mass,
+                             mass_accum=run.mass, n_cap=run.n_cap)
+        e[3].record(stream)
+        run.topk(clear_mass=True)
+        e[4].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    plain_ms = t_start.elapsed_time(t_end) / K
+    names = ["map_slots", "qkv_rope_cachewrite", "sched_attention", "topk_tracked"]
+    per = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)])) * 1e3
+           for j, n in enumerate(names)}
+    per_p50 = {n: float(np.median([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)])) * 1e3
+               for j, n in enumerate(names)}
+
+    # ---- captured hipGraph replay (one graph per copy) ----
+    graph_ms = None
+    if not args.no_graph:
+        graphs = []
+        cs = torch.cuda.Stream()
+        cs.wait_stream(stream)
+        with torch.cuda.stream(cs):
+            for c in range(copies):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cs):
+                    step(c)
+                graphs.append(g)
+        stream.wait_stream(cs)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % copies].replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for i in range(K):
+            graphs[i % copies].replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / K
+
+    step_ms = graph_ms if graph_ms is not None else plain_ms
+    value = R / (step_ms * 1e-3)
+
+    # ---- roofline of the dominant kernel (the weight-streaming projection) ----
+    d = sh.d_model
+    el = 2 if sh.dtype == "bf16" else 4
+    qkv_bytes = 3 * n_out * d * el + R * d * el + R * n_out * el + 2 * R * n_out * el
+    qkv_us = per["qkv_rope_cachewrite"]
+    achieved = qkv_bytes / (qkv_us * 1e-6) / 1e9
+    kv_keys = int(rows1.kv_len.sum())
+    attn_bytes = kv_keys * 2 * n_out * el + 2 * R * n_out * el
+    attn_flops = 0
+    for b in range(wl.n_seq):
+        rb = int(rows1.cu_q[b + 1] - rows1.cu_q[b])
+        vis = rows1.visible[b].sum() if rows1.visible is not None else rb * int(rows1.kv_len[b])
+        attn_flops += 4 * int(vis) * n_out
+    qkv_flops = 2 * R * d * 3 * n_out
+    b_qkv = max(qkv_bytes / (HBM_PEAK_GBS * 1e9), qkv_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+    b_att = max(attn_bytes / (HBM_PEAK_GBS * 1e9), attn_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+    step_bound_us = (b_qkv + b_att) * 1e6
+    kernels = {
+        "qkv_rope_cachewrite": {"us": qkv_us, "us_p50": per_p50["qkv_rope_cachewrite"],
+                                "alg_bytes": qkv_bytes, "alg_flops": qkv_flops,
+                                "bound": "hbm" if qkv_bytes / 8e12 >= qkv_flops / 2.5e15 else "mfma",
+                                "frac": b_qkv * 1e6 / qkv_us},
+        "sched_attention": {"us": per["sched_attention"], "us_p50": per_p50["sched_attention"],
+                            "alg_bytes": attn_bytes, "alg_flops": attn_flops,
+                            "bound": "hbm" if attn_bytes / 8e12 >= attn_flops / 2.5e15 else "mfma",
+                            "frac": b_att * 1e6 / per["sched_attention"]},
+        "map_slots": {"us": per["map_slots"]},
+        "topk_tracked": {"us": per["topk_tracked"]},
+    }
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "qkv_rope_cachewrite_llada_b1_traffic.json")
+    if args.workload == "llada_b1" and os.path.exists(tfile):
+        try:
+            tj = json.load(open(tfile))
+            traffic = tj.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    # ---- optional plain copy (calibrates the HBM byte counters) ----
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b_ = torch.empty_like(a)
+        for _ in range(3):
+            b_.copy_(a)
+        torch.cuda.synchronize()
+
+    # ---- CPU baseline: the oracle on host cores, bounded sample ----
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, rows1, args.cpu_seconds)
+
+    out = {
+        "metric": "refreshed tokens/s per layer (cache-update+attention)",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": sh.dtype,
+        "data": "synthetic",
+        "config": {"workload": describe(args.workload), "rows_per_step": R, "layers": 1,
+                   "batch": wl.n_seq, "d_model": sh.d_model, "heads": sh.n_heads, "head_dim": sh.head_dim,
+                   "kv_len": [int(k) for k in rows1.kv_len], "parallelism": "single GPU",
+                   "rotated_copies": copies, "timing": "hipGraph replay" if graph_ms else "stream launches"},
+        "plain_launch_ms_per_step": plain_ms,
+        "graph_ms_per_step": graph_ms,
+        "step_roofline_us": step_bound_us,
+        "step_roofline_frac": step_bound_us / (step_ms * 1e3),
+        "kernels": kernels,
+        "roofline": {"bound": "hbm", "kernel": "qkv_rope_cachewrite", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def describe(name):
+    return {
+        "llada_b1": "LLaDA-8B-shaped layer (d_model 4096, 32x128 heads, bf16), batch 1, context 512 "
+                    "(prompt 256 + gen 256), cache-phase step: 32 window + 8 new + 32 tracked rows",
+        "mixed_b8": "LLaDA-8B-shaped layer, batch 8 mixed: 6 cache-phase sequences (40-72 rows, context "
+                    "512-1024) + 2 full refreshes (512, 1024 rows)",
+        "verify_b4": "LLaDA-8B-shaped layer, batch 4, context 1024 + 32 view slots, verify step with "
+                     "16 draft + 16 mask views + 40 ordinary rows per sequence under the verify mask",
+    }[name]
+
+
+def cpu_baseline(wl, rows, seconds):
+    """The oracle, untouched, on this host's cores: the same step (projection,
+    RoPE, scatter, attention, formula-(2) term, top-k) on the same rows,
+    repeated for about `seconds`."""
+    import numpy as np
+    import oracle as O
+    from io_aware_kv_amd import workloads as W
+    sh = wl.shape
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    table = O.build_block_table(wl.seq_pages, wl.pool_perm, wl.pool_pages, wl.max_pages)
+    w = W.as_f64(wl, W.weights(wl, 0))
+    x = W.as_f64(wl, W.activations(wl, rows, 1))
+    n_out = sh.n_heads * sh.head_dim
+    kc = np.zeros((wl.pool_pages * W.PAGE, n_out))
+    vc = np.zeros_like(kc)
+    elig = wl.eligible().astype(bool)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        out = O.layer_step(x, w, rows.pos, rows.logical, rows.cu_q, rows.kv_len, rows.mass_count, kc, vc,
+                           table, sh.n_heads, sh.head_dim, sh.rope_base, W.PAGE, visible=rows.visible)
+        O.topk(out["mass"], elig, sh.top_k)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": rows.n_rows * reps / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} oracle steps of the same workload ({rows.n_rows} rows each, fp64 NumPy) "
+                      f"in {el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -57,9 +57,8 @@ def run_gpu_step(c: Case, step: int, gpu):
             "cnt": run.top_cnt.cpu().numpy(), "mass_after": run.mass.cpu().numpy()}
 
 
-def compare_step(c: Case, g: dict, step: int, exact_topk: bool = False):
+def compare_step(c: Case, g: dict, step: int, exact_topk: bool = False, o_scale: float = 1.0):
     out = c.out0 if step == 0 else c.out1
-    top = c.top0 if step == 0 else c.top1
     atol, rtol = TOL[c.kind]
     # integer outputs, bit-exact
     assert np.array_equal(g["page_table"], c.table.astype(np.int32))
@@ -71,7 +70,7 @@ def compare_step(c: Case, g: dict, step: int, exact_topk: bool = False):
     infos = [close(g["q"], out["q"], atol, rtol, "q_out"),
              close(g["k_cache"][out["slots"]], out["k"], atol, rtol, "K rows"),
              close(g["v_cache"][out["slots"]], out["v"], atol, rtol, "V rows"),
-             close(g["o"], out["o"], atol, rtol, "o")]
+             close(g["o"], out["o"], atol * o_scale, rtol * o_scale, "o")]
     ma, mr = MASS_TOL[c.kind]
     infos.append(close(g["mass"], out["mass"], ma, mr, "mass"))
     assert not g["mass_after"].any(), "top-k did not clear the score"
@@ -93,8 +92,11 @@ def test_workload_step_parity(name, step, gpu):
 @pytest.mark.parametrize("name", ["llada_b1", "verify_b4"])
 def test_heavy_hitter_topk_exact(name, gpu):
     """Planted heavy hitters (step-0 x rows scaled by 2) separate the top-k,
-    so the GPU's set must equal the oracle's exactly."""
+    so the GPU's set must equal the oracle's exactly.  Scaling x by 2 scales q
+    and k of those rows by 2 and their scores by 4, and the bf16 storage of q
+    and k moves a score in proportion to its size, so the o gate of this
+    variant is 4x the workload tolerance; every other output keeps its gate."""
     log(f"[gpu] heavy-hitter top-k {name}")
     c = case(name, heavy=True)
     g = run_gpu_step(c, 0, gpu)
-    compare_step(c, g, 0, exact_topk=True)
+    compare_step(c, g, 0, exact_topk=True, o_scale=4.0)
