@@ -20,10 +20,9 @@
  * Conventions shared by every entry point:
  *   - Ownership: the caller allocates and owns every buffer; the library never
  *     allocates or frees device memory and keeps no state between calls.  The
- *     workspace of a call is caller memory whose size comes from the matching
- *     *_workspace() query; it must be zero-filled before its first use, every
- *     call returns it with its counters at zero again, and two calls in flight
- *     at once must not share one workspace.
+ *     *_workspace() queries report the scratch memory a call needs (currently
+ *     0 bytes for every shape: each workgroup owns its outputs); a NULL
+ *     workspace is accepted when the query returns 0.
  *   - Pointers named "host" are host memory; every other pointer is device
  *     memory of the current HIP device.  All device work is enqueued on
  *     `stream` and is asynchronous unless stated; buffers must stay valid until
@@ -126,8 +125,7 @@ int dllm_map_slots(int n_seq, int n_rows, int page_size, int max_pages, int pool
  * Rotary embedding is rotate-half: for i < D/2, theta_i = rope_base^(-2i/D) and
  * the pair (t_i, t_{i+D/2}) turns by pos*theta_i.  Results are rounded once to
  * the output dtype.  Slots of one call must be pairwise distinct.
- * Errors: INVALID_ARG, UNSUPPORTED (D, H*D, d_model, dtype), INVALID_ARG when
- * workspace_bytes is below dllm_qkv_rope_cachewrite_workspace().
+ * Errors: INVALID_ARG, UNSUPPORTED (D, H*D, d_model, dtype).
  */
 size_t dllm_qkv_rope_cachewrite_workspace(dllm_dtype dt, int n_rows, int d_model, int n_heads,
                                           int head_dim);
@@ -157,13 +155,16 @@ int dllm_qkv_rope_cachewrite(dllm_dtype dt, int n_rows, int d_model, int n_heads
  *              mask_off[b] + i*ceil(kv_len[b]/32) + j/32 is 1; mask_off int64[B]
  *   mass_count int32[B] or NULL    the first mass_count[b] (<= max_mass_rows <= 128)
  *              rows of sequence b are the masked-window rows of formula (2)
- *   mass_accum float[B*n_cap]      mass_accum[b*n_cap + i] += (1/(H*m_b)) *
- *              sum over heads and window rows of the probability of key i,
- *              m_b = mass_count[b]; keys i >= n_cap are not recorded
+ *   mass_accum float[B*H*n_cap]    per-head running score: for each head h,
+ *              mass_accum[(b*H + h)*n_cap + i] += (1/(H*m_b)) * sum over the
+ *              window rows of head h's probability of key i (m_b =
+ *              mass_count[b]); keys i >= n_cap are not recorded.  Summed over
+ *              heads (dllm_topk_tracked does) and over layers (by calling once
+ *              per layer) this is formula (2)'s a_i.
  *   o          [R, H*D]            out: attention output
  * Scores are q.k/sqrt(D); a row that sees no key outputs zeros.
- * Errors: INVALID_ARG (also when workspace_bytes is below the query),
- * UNSUPPORTED (dtype/D/page_size).
+ * Errors: INVALID_ARG (also cache_rows < 16), UNSUPPORTED (dtype/D/page_size/
+ * n_seq > 1024/max_pages > 1024/bf16 score over more than 8704 keys).
  */
 size_t dllm_sched_attention_workspace(dllm_dtype dt, int n_seq, int n_rows, int n_heads,
                                       int head_dim, int max_kv, int n_cap);
@@ -182,17 +183,20 @@ int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_heads, int 
  * newly decoded tokens, form the next tracked set (the caller adds the new
  * ones; `eligible` excludes them).
  *
- *   mass     float[B*n_cap]   scores (read; zeroed afterwards if clear_mass != 0)
+ *   mass     float[B*H*n_cap] per-head scores as accumulated by
+ *                             dllm_sched_attention; the score of position i is
+ *                             the fp32 sum over h = 0..H-1 in that order (read;
+ *                             zeroed afterwards if clear_mass != 0)
  *   eligible uint8[B*n_cap]   nonzero = candidate
  *   idx      int32[B*k]       out: positions, highest score first, ties to the
  *                             lower position, -1 padding
  *   val      float[B*k]       out: their scores (0 padding)
  *   count    int32[B]         out: min(k, number of candidates)
- * Limits: 1 <= k <= 256, n_cap <= 8192.
+ * Limits: 1 <= k <= 256, n_cap <= 4096.
  */
-int dllm_topk_tracked(int n_seq, int n_cap, int k, float* mass, const uint8_t* eligible,
-                      int32_t* idx, float* val, int32_t* count, int clear_mass,
-                      hipStream_t stream);
+int dllm_topk_tracked(int n_seq, int n_heads, int n_cap, int k, float* mass,
+                      const uint8_t* eligible, int32_t* idx, float* val, int32_t* count,
+                      int clear_mass, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,7 @@ LIB = os.path.join(OUT_DIR, "libdllm.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", INCLUDE, "-I", CSRC]
 

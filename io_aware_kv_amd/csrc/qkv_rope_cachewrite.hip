@@ -7,20 +7,19 @@
 // no q/k/v intermediate crosses HBM; 研究动机: the unfused four-kernel chain
 // is bound by memory traffic.
 //
-// bf16 kernel (gfx950): C = x W^T on v_mfma_f32_16x16x32_bf16.  A workgroup
-// owns a BM x 128 output tile, i.e. one whole head of Q, K or V for D = 128
-// (two heads for D = 64), so every rotate-half pair (i, i + D/2) lies in the
-// tile.  Both operands have the contraction dimension contiguous in memory
-// (x rows, W rows), so 16-byte loads feed the MFMA fragments directly from
-// LDS.  When there are too few output tiles to fill 256 CUs (a cache-phase
-// step has R ~ 72 rows: 96 tiles), the K dimension is split across
-// workgroups; each writes an fp32 partial and the last one to finish a tile
-// sums the partials in split order (deterministic) and runs the epilogue.
-// The epilogue stages the tile in LDS, applies the rotation in fp32 with an
-// fp64-reduced angle, rounds once to bf16 and writes whole 16-byte row
-// segments of q_out or of the slot's cache row.
+// bf16 kernels (gfx950), C = x W^T on v_mfma_f32_16x16x32_bf16.  Both
+// operands have the contraction dimension contiguous in memory (x rows, W
+// rows), so 16-byte loads give MFMA fragments directly.  Every workgroup owns
+// whole rotate-half pairs (i, i + D/2) of one head, so the rotation happens in
+// the epilogue without leaving the workgroup: the fp32 tile is staged in LDS,
+// rotated with an fp64-reduced angle, rounded once to bf16 and written as
+// 16-byte row segments of q_out or of the slot's cache row.
+//   * R <= 128 (cache phase): qkv_skinny_kernel streams W once at HBM rate.
+//   * larger R (full refresh): qkv_bf16_kernel, LDS-tiled 128 x 128 tiles.
 #include <math.h>
 #include <stdlib.h>
+
+#include <utility>
 
 #include "common.h"
 
@@ -35,7 +34,7 @@ constexpr int kThreads = 256;     // 4 waves, 2 x 2 over the tile
 constexpr double kTwoPi = 6.283185307179586476925286766559;
 
 struct QkvArgs {
-    int R, d_model, head_dim, n_out, splits, kt_per_split, n_ktiles, n_ntiles;
+    int R, d_model, head_dim, n_out, n_ktiles;
     float rope_base;
     const uint16_t* x;
     const uint16_t* w;
@@ -45,8 +44,6 @@ struct QkvArgs {
     uint16_t* k_cache;
     uint16_t* v_cache;
     int64_t cache_rows;
-    float* partial;
-    int32_t* counters;
 };
 
 template <int BM>
@@ -56,14 +53,12 @@ __global__ __launch_bounds__(kThreads) void qkv_bf16_kernel(QkvArgs a) {
     static_assert(BM * kLDC * 4 <= 2 * kStage * 2, "epilogue tile must fit the stages");
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStage];
     __shared__ double s_theta[64];
-    __shared__ int s_last;
 
-    const int nt = blockIdx.x, mt = blockIdx.y, sp = blockIdx.z;
+    const int nt = blockIdx.x, mt = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int row0 = mt * BM, col0 = nt * kBN;
-    const int kt0 = sp * a.kt_per_split;
-    const int kt1 = min(kt0 + a.kt_per_split, a.n_ktiles);
+    const int kt0 = 0, kt1 = a.n_ktiles;
     const int half = a.head_dim >> 1;
 
     if (tid < half) s_theta[tid] = pow((double)a.rope_base, -2.0 * tid / a.head_dim);
@@ -78,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void qkv_bf16_kernel(QkvArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto gload = [&](int kt) {
+    auto gload = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < kACh; ++i) {
             int c = tid + i * kThreads, r = c >> 3, kc = c & 7;
@@ -94,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void qkv_bf16_kernel(QkvArgs a) {
             rb[i] = *(const u32x4*)(a.w + (int64_t)(col0 + r) * a.d_model + kt * kBK + kc * 8);
         }
     };
-    auto lstore = [&](int stage) {
+    auto lstore = [&](int stage) __attribute__((always_inline)) {
         uint16_t* As = smem + stage * kStage;
         uint16_t* Bs = As + BM * kLDA;
 #pragma unroll
@@ -154,30 +149,6 @@ __global__ __launch_bounds__(kThreads) void qkv_bf16_kernel(QkvArgs a) {
     __syncthreads();
 
     const int rows_valid = min(BM, a.R - row0);
-    if (a.splits > 1) {
-        // publish this split's partial, then let the last split finish the tile
-        const int tile = mt * a.n_ntiles + nt;
-        float* mine = a.partial + ((int64_t)tile * a.splits + sp) * BM * kBN;
-        for (int idx = tid; idx < rows_valid * (kBN / 4); idx += kThreads) {
-            int r = idx / (kBN / 4), c4 = idx % (kBN / 4);
-            *(f32x4*)(mine + r * kBN + c4 * 4) = *(const f32x4*)(Cs + r * kLDC + c4 * 4);
-        }
-        __threadfence();
-        __syncthreads();
-        if (tid == 0) s_last = (atomicAdd(&a.counters[tile], 1) == a.splits - 1);
-        __syncthreads();
-        if (!s_last) return;
-        __threadfence();
-        const float* base = a.partial + (int64_t)tile * a.splits * BM * kBN;
-        for (int idx = tid; idx < rows_valid * (kBN / 4); idx += kThreads) {
-            int r = idx / (kBN / 4), c4 = idx % (kBN / 4);
-            f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (int q = 0; q < a.splits; ++q) s += *(const f32x4*)(base + (int64_t)q * BM * kBN + r * kBN + c4 * 4);
-            *(f32x4*)(Cs + r * kLDC + c4 * 4) = s;
-        }
-        if (tid == 0) a.counters[tile] = 0;
-        __syncthreads();
-    }
 
     // ---- epilogue: rotate, round, write ----
     const int part = col0 / a.n_out;            // 0 = Q, 1 = K, 2 = V
@@ -223,6 +194,153 @@ __global__ __launch_bounds__(kThreads) void qkv_bf16_kernel(QkvArgs a) {
         }
         *(u32x4*)(dst + c_lo) = plo;
         *(u32x4*)(dst + c_hi) = phi;
+    }
+}
+
+// Skinny projection (R <= 128 rows: the cache phase).  Streaming W at full
+// HBM bandwidth is the whole game: W is 3*H*D x d_model and is read exactly
+// once.  Each workgroup owns 64 output columns of one (Q/K/V part, head): 32
+// "low" columns [j*32, j*32+32) and their rotation partners D/2 higher, so the
+// rotation stays inside the workgroup.  The 4 waves split the contraction into
+// quarters; each wave loads the x and W fragments of its quarter straight into
+// MFMA operand registers, a ring of DEPTH 32-wide k-steps (8 for R <= 80:
+// ~128 KB of W in flight per CU, what loaded HBM latency needs), so both
+// streams share one in-order wait counter at the same depth.  The four partial tiles
+// are summed in LDS in wave order (deterministic).  No split-K across
+// workgroups, so no cross-workgroup synchronisation.
+template <int J>
+struct Ic { static constexpr int value = J; };
+
+template <int MT, int kSkDepth>   // 16-row tiles covering R; k-steps in flight
+__global__ __launch_bounds__(256, 1) void qkv_skinny_kernel(QkvArgs a) {
+    constexpr int kLDC = 64 + 4;
+    __shared__ __attribute__((aligned(16))) float Cs[MT * 16 * kLDC];
+    __shared__ double s_theta[64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, ln = lane & 15;
+    const int D = a.head_dim, half = D >> 1;
+    const int groups_per_head = D / 64;
+    const int grp = blockIdx.x;                          // (part, head, j)
+    const int j = grp % groups_per_head;
+    const int ph = grp / groups_per_head;                // part * H + head
+    const int part = ph / (a.n_out / D);
+    const int head = ph % (a.n_out / D);
+    const int col_base = part * a.n_out + head * D;      // first W row of this head
+    const int R = a.R;
+    if (tid < half) s_theta[tid] = pow((double)a.rope_base, -2.0 * tid / D);
+
+    const int kq = a.d_model / 4;                        // this wave's contraction quarter
+    const int nsteps = kq / 32;
+    const uint16_t* xp[MT];
+    const uint16_t* wp[4];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        int row = m * 16 + ln;
+        row = row < R ? row : R - 1;                      // padding rows repeat a real row
+        xp[m] = a.x + (int64_t)row * a.d_model + wave * kq + g * 8;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        int col = col_base + (t >= 2 ? half : 0) + j * 32 + (t & 1) * 16 + ln;
+        wp[t] = a.w + (int64_t)col * a.d_model + wave * kq + g * 8;
+    }
+    bf16x8 ra[kSkDepth][MT], rb[kSkDepth][4];
+    f32x4 acc[MT][4];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto load = [&](auto S, int step) __attribute__((always_inline)) {
+        constexpr int sl = decltype(S)::value;
+        if (step < nsteps) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) rb[sl][t] = *(const bf16x8*)(wp[t] + step * 32);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) ra[sl][m] = *(const bf16x8*)(xp[m] + step * 32);
+        }
+    };
+    auto mma = [&](auto S) __attribute__((always_inline)) {
+        constexpr int sl = decltype(S)::value;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[sl][m], rb[sl][t], acc[m][t], 0, 0, 0);
+    };
+    // prologue: k-steps 0 .. DEPTH-2 in flight
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+        ((load(Ic<I>{}, I), __builtin_amdgcn_sched_barrier(0)), ...);
+    }(std::make_integer_sequence<int, kSkDepth - 1>{});
+    auto iter = [&](auto S, int step) __attribute__((always_inline)) {
+        constexpr int sl = decltype(S)::value;
+        load(Ic<(sl + kSkDepth - 1) % kSkDepth>{}, step + kSkDepth - 1);
+        __builtin_amdgcn_sched_barrier(0);      // issue order = prefetch order
+        mma(S);
+    };
+    for (int st = 0; st < nsteps; st += kSkDepth) {
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+            ((st + I < nsteps ? iter(Ic<I>{}, st + I) : void()), ...);
+        }(std::make_integer_sequence<int, kSkDepth>{});
+    }
+
+    // ---- sum the four quarter tiles in LDS, in wave order ----
+    for (int w = 0; w < 4; ++w) {
+        if (wave == w) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        int r = m * 16 + g * 4 + e;
+                        int c = (t >= 2 ? 32 : 0) + (t & 1) * 16 + ln;
+                        float v = acc[m][t][e];
+                        Cs[r * kLDC + c] = (w == 0) ? v : Cs[r * kLDC + c] + v;
+                    }
+        }
+        __syncthreads();
+    }
+
+    // ---- epilogue: rotate pairs, round, write ----
+    const int cpart = head * D + j * 32;                // low column within the part
+    for (int idx = tid; idx < R * 4; idx += 256) {
+        const int r = idx >> 2, q = idx & 3;             // 8-column piece q of the 32 low columns
+        float lo[8], hi[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            lo[e] = Cs[r * kLDC + q * 8 + e];
+            hi[e] = Cs[r * kLDC + 32 + q * 8 + e];
+        }
+        uint16_t* dst;
+        if (part == 0) {
+            dst = a.q_out + (int64_t)r * a.n_out;
+        } else {
+            int sl = a.slot[r];
+            if (sl < 0 || (int64_t)sl >= a.cache_rows) continue;
+            dst = (part == 1 ? a.k_cache : a.v_cache) + (int64_t)sl * a.n_out;
+        }
+        if (part < 2) {
+            const double p = (double)a.pos[r];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                double ang = p * s_theta[j * 32 + q * 8 + e];
+                ang -= rint(ang * (1.0 / kTwoPi)) * kTwoPi;
+                float sn, cs;
+                sincosf((float)ang, &sn, &cs);
+                float x0 = lo[e], x1 = hi[e];
+                lo[e] = x0 * cs - x1 * sn;
+                hi[e] = x1 * cs + x0 * sn;
+            }
+        }
+        u32x4 plo, phi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            plo[e] = pack_bf16x2(lo[2 * e], lo[2 * e + 1]);
+            phi[e] = pack_bf16x2(hi[2 * e], hi[2 * e + 1]);
+        }
+        *(u32x4*)(dst + cpart + q * 8) = plo;
+        *(u32x4*)(dst + cpart + half + q * 8) = phi;
     }
 }
 
@@ -274,32 +392,19 @@ __global__ void qkv_f32_kernel(int R, int d_model, int n_heads, int head_dim, fl
 }
 
 struct QkvPlan {
-    int bm, n_mtiles, n_ntiles, n_ktiles, splits, kt_per_split;
-    size_t partial_bytes, counter_bytes;
+    bool skinny;
+    int bm, n_mtiles, n_ntiles, n_ktiles;
 };
 
-// Split-K only when the output tiles cannot fill the chip.  DLLM_QKV_SPLITK
-// overrides the split count (a tuning knob; both the size query and the call
-// read it, so they agree).
+// Cache-phase row counts (R <= 128) take the weight-streaming kernel; larger
+// R takes the LDS-tiled kernel.  Neither splits K, so no workspace is needed.
 QkvPlan plan_bf16(int R, int d_model, int n_out) {
     QkvPlan p{};
+    p.skinny = R <= 128 && d_model % 128 == 0;
     p.bm = R <= 64 ? 64 : 128;
     p.n_mtiles = (R + p.bm - 1) / p.bm;
     p.n_ntiles = 3 * n_out / kBN;
     p.n_ktiles = d_model / kBK;
-    int tiles = p.n_mtiles * p.n_ntiles;
-    int want = 1;
-    if (tiles < 2 * kNumCu) want = (2 * kNumCu + tiles - 1) / tiles;
-    const char* env = getenv("DLLM_QKV_SPLITK");
-    if (env && atoi(env) > 0) want = atoi(env);
-    if (want > p.n_ktiles) want = p.n_ktiles;
-    if (want < 1) want = 1;
-    p.kt_per_split = (p.n_ktiles + want - 1) / want;
-    p.splits = (p.n_ktiles + p.kt_per_split - 1) / p.kt_per_split;
-    if (p.splits > 1) {
-        p.partial_bytes = (size_t)tiles * p.splits * p.bm * kBN * sizeof(float);
-        p.counter_bytes = ((size_t)tiles * sizeof(int32_t) + 255) / 256 * 256;
-    }
     return p;
 }
 
@@ -319,9 +424,7 @@ int check_shape(dllm_dtype dt, int n_rows, int d_model, int n_heads, int head_di
 extern "C" size_t dllm_qkv_rope_cachewrite_workspace(dllm_dtype dt, int n_rows, int d_model,
                                                      int n_heads, int head_dim) {
     if (check_shape(dt, n_rows, d_model, n_heads, head_dim) != DLLM_OK) return 0;
-    if (dt != DLLM_BF16 || n_rows == 0) return 0;
-    QkvPlan p = plan_bf16(n_rows, d_model, n_heads * head_dim);
-    return p.counter_bytes + p.partial_bytes;
+    return 0;      // no kernel of this entry point needs scratch memory
 }
 
 extern "C" int dllm_qkv_rope_cachewrite(dllm_dtype dt, int n_rows, int d_model, int n_heads,
@@ -349,18 +452,15 @@ extern "C" int dllm_qkv_rope_cachewrite(dllm_dtype dt, int n_rows, int d_model, 
         return DLLM_OK;
     }
     QkvPlan p = plan_bf16(n_rows, d_model, n_out);
-    DLLM_CHECK_ARG(workspace_bytes >= p.counter_bytes + p.partial_bytes);
-    if (p.splits > 1) DLLM_CHECK_ARG(workspace != nullptr);
+    (void)workspace;
+    (void)workspace_bytes;
     DLLM_CHECK_SUP(p.n_mtiles < 65536);
     QkvArgs a;
     a.R = n_rows;
     a.d_model = d_model;
     a.head_dim = head_dim;
     a.n_out = n_out;
-    a.splits = p.splits;
-    a.kt_per_split = p.kt_per_split;
     a.n_ktiles = p.n_ktiles;
-    a.n_ntiles = p.n_ntiles;
     a.rope_base = rope_base;
     a.x = (const uint16_t*)x;
     a.w = (const uint16_t*)w_qkv;
@@ -370,13 +470,25 @@ extern "C" int dllm_qkv_rope_cachewrite(dllm_dtype dt, int n_rows, int d_model, 
     a.k_cache = (uint16_t*)k_cache;
     a.v_cache = (uint16_t*)v_cache;
     a.cache_rows = cache_rows;
-    a.counters = (int32_t*)workspace;
-    a.partial = p.splits > 1 ? (float*)((char*)workspace + p.counter_bytes) : nullptr;
-    dim3 grid(p.n_ntiles, p.n_mtiles, p.splits);
-    if (p.bm == 64)
-        hipLaunchKernelGGL(qkv_bf16_kernel<64>, grid, dim3(kThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL(qkv_bf16_kernel<128>, grid, dim3(kThreads), 0, stream, a);
+    if (p.skinny) {
+        dim3 grid(3 * n_out / 64);
+        switch ((n_rows + 15) / 16) {
+            case 1: hipLaunchKernelGGL((qkv_skinny_kernel<1, 8>), grid, dim3(256), 0, stream, a); break;
+            case 2: hipLaunchKernelGGL((qkv_skinny_kernel<2, 8>), grid, dim3(256), 0, stream, a); break;
+            case 3: hipLaunchKernelGGL((qkv_skinny_kernel<3, 8>), grid, dim3(256), 0, stream, a); break;
+            case 4: hipLaunchKernelGGL((qkv_skinny_kernel<4, 8>), grid, dim3(256), 0, stream, a); break;
+            case 5: hipLaunchKernelGGL((qkv_skinny_kernel<5, 8>), grid, dim3(256), 0, stream, a); break;
+            case 6: hipLaunchKernelGGL((qkv_skinny_kernel<6, 6>), grid, dim3(256), 0, stream, a); break;
+            case 7: hipLaunchKernelGGL((qkv_skinny_kernel<7, 6>), grid, dim3(256), 0, stream, a); break;
+            default: hipLaunchKernelGGL((qkv_skinny_kernel<8, 6>), grid, dim3(256), 0, stream, a); break;
+        }
+    } else {
+        dim3 grid(p.n_ntiles, p.n_mtiles, 1);
+        if (p.bm == 64)
+            hipLaunchKernelGGL(qkv_bf16_kernel<64>, grid, dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL(qkv_bf16_kernel<128>, grid, dim3(kThreads), 0, stream, a);
+    }
     DLLM_CHECK_LAUNCH();
     return DLLM_OK;
 }

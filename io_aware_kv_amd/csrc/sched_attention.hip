@@ -12,21 +12,21 @@
 // averaged over heads and window rows.
 //
 // bf16 kernel (gfx950).  One launch covers every (sequence, head, 128-row
-// query tile, key split) item.  Items are decoded on the device from cu_q and
-// kv_len: each workgroup scans the per-sequence item counts (no host
-// round-trip), and consecutive items (same head and key range, next query
-// tile) are placed on the same XCD so they share its L2.  Eight waves own 16
-// query rows each; 64-key tiles of K and of V^T are gathered through the
-// block table into LDS.  S^T = K Q^T and O^T = V^T P^T run on
-// v_mfma_f32_16x16x32_bf16: the K rows fed to the first product are permuted
-// so that the P^T fragment a lane holds covers 8 consecutive keys, which makes
-// the V^T fragment one 16-byte LDS read.  Softmax is online in fp32 (base 2).
-// When a batch has too few items to fill the chip, keys are split across
-// workgroups and the last split of a tile merges the partials in split order.
-// The finalising workgroup of a sequence's first query tile then makes a
-// second pass over K for the masked-window rows (their log-sum-exp is final
-// only at that point), forms each key's column mass and, once all heads of the
-// sequence are in, adds the head-ordered sum into mass_accum (deterministic).
+// query tile) item.  Items are decoded on the device from cu_q and kv_len:
+// each workgroup scans the per-sequence item counts (no host round-trip), and
+// consecutive items (same head, next query tile) are placed on the same XCD so
+// they share its L2 copy of the head's keys.  Eight waves own 16 query rows
+// each and walk all keys of the sequence in 64-key tiles gathered through the
+// block table, three tiles in flight in registers ahead of a double-buffered
+// LDS tile.  S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_16x16x32_bf16;
+// the K rows fed to the first product are permuted so that the P^T fragment a
+// lane holds covers 8 consecutive keys, and the matching V^T fragment is read
+// from the row-major V tile with the gfx950 LDS transpose read.  Softmax is
+// online in fp32 (base 2).  The workgroup of a sequence's first query tile
+// then re-reads the keys for the masked-window rows (their log-sum-exp is
+// final only then) and adds this head's column mass to mass_accum[b][h][:],
+// which only it writes: no atomics, no cross-workgroup synchronisation, and
+// the reduction order is fixed.
 #include <math.h>
 
 #include "common.h"
@@ -47,7 +47,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;
 
 struct AttnArgs {
-    int n_seq, n_rows, H, n_out, max_kv, max_pages, n_cap, split_max, max_mass, pool_pages;
+    int n_seq, n_rows, H, n_out, max_kv, max_pages, n_cap, max_mass, pool_pages;
     int head_dim;
     float scale_log2;
     const uint16_t* q;
@@ -60,17 +60,12 @@ struct AttnArgs {
     const int64_t* mask_off;
     int64_t mask_words;
     const int32_t* mass_count;
-    float* mass_accum;
+    float* mass_accum;      // [n_seq, H, n_cap], this head's term added per layer
     uint16_t* o;
-    int32_t* cnt_tile;      // [max_items]
-    int32_t* cnt_mass;      // [n_seq]
-    float* mass_part;       // [n_seq, H, n_cap]
-    float* part_o;          // [max_items, QT, HD]
-    float* part_ml;         // [max_items, QT, 2]
 };
 
 struct SeqInfo {
-    int rows, kv, nqt, splits;
+    int rows, kv, nqt;
 };
 
 __device__ __forceinline__ SeqInfo seq_info(const AttnArgs& a, int b) {
@@ -83,10 +78,6 @@ __device__ __forceinline__ SeqInfo seq_info(const AttnArgs& a, int b) {
     kv = max(0, min(kv, min(a.max_kv, a.max_pages * 16)));
     s.kv = kv;
     s.nqt = (s.rows + kQT - 1) / kQT;
-    int ktiles = (kv + kKT - 1) / kKT;
-    int want = max(1, min(a.split_max, ktiles));
-    int per = ktiles > 0 ? (ktiles + want - 1) / want : 1;
-    s.splits = ktiles > 0 ? (ktiles + per - 1) / per : 1;    // every split gets keys
     return s;
 }
 
@@ -118,18 +109,36 @@ __device__ __forceinline__ int reg_key(int t, int g, int e) {
     return 32 * (t >> 1) + 8 * g + 4 * (t & 1) + e;
 }
 
-__global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sK[kKT * kLDK];
-    __shared__ __attribute__((aligned(16))) uint16_t sVt[kHD * kLDV];
+template <int J>
+struct Ic { static constexpr int value = J; };
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// gfx950 LDS transpose read: inside each 16-lane group, output lane j, element e
+// is element (j & 3) of the 8-byte piece addressed by lane 4e + (j >> 2).  With
+// lane s pointing at row (key) kbase + (s >> 2), column d0 + 4 (s & 3) of a
+// row-major [key][d] tile, lane j receives V[kbase + e][d0 + j], e = 0..3: the
+// V^T operand (d = lane, four consecutive keys) without a transposed copy.
+__device__ __forceinline__ s16x4 ds_read_tr(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+}
+
+constexpr int kRing = 4;            // register ring of K/V tiles (3 in flight)
+
+__global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKT * kLDK];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[2][kKT * kLDK];
     __shared__ int s_pref[kMaxSeq + 1];
     __shared__ int s_pages[kMaxPages];
     __shared__ float s_col[8][kKT];
-    __shared__ int s_total, s_flag;
+    __shared__ uint8_t s_tile_full[kMaxPages / 4];   // tile fully in range with valid pages
+    __shared__ int s_total;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, ln = lane & 15;
 
-    // ---- schedule: per-sequence item counts, prefix-summed by wave 0 ----
+    // ---- schedule: per-sequence item counts (query tiles x heads), prefix-summed by wave 0 ----
     if (wave == 0) {
         int base = 0;
         for (int c = 0; c < a.n_seq; c += 64) {
@@ -137,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
             int items = 0;
             if (b < a.n_seq) {
                 SeqInfo s = seq_info(a, b);
-                items = s.nqt * s.splits * a.H;
+                items = s.nqt * a.H;
             }
             int scan = items;
 #pragma unroll
@@ -155,8 +164,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
     }
     __syncthreads();
     // a malformed cu_q (not non-decreasing) can claim more items than were
-    // launched: then nothing runs (outputs unspecified, no access past the
-    // workspace)
+    // launched: then nothing runs (outputs unspecified, nothing out of bounds)
     const int total = s_total;
     if (total > (int)gridDim.x || (int)blockIdx.x >= total) return;
     const int item = xcd_remap(blockIdx.x, total);
@@ -168,81 +176,105 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
     const int b = lo;
     const SeqInfo si = seq_info(a, b);
     const int local = item - s_pref[b];
-    const int qt = local % si.nqt;
-    const int hs = local / si.nqt;
-    const int sp = hs % si.splits;
-    const int h = hs / si.splits;
+    const int qt = local % si.nqt;                      // consecutive items: next query tile, same head
+    const int h = local / si.nqt;
     const int seq_r0 = max(0, min(a.cu_q[b], a.n_rows));
     const int r0 = seq_r0 + qt * kQT;
     const int nr = min(kQT, si.rows - qt * kQT);
-    const int ktiles = (si.kv + kKT - 1) / kKT;
-    const int tiles_per = (ktiles + si.splits - 1) / si.splits;
-    const int k_lo = sp * tiles_per * kKT;
-    const int k_hi = min(si.kv, k_lo + tiles_per * kKT);
+    const int ntiles = (si.kv + kKT - 1) / kKT;
     const int npages = (si.kv + 15) / 16;
     for (int j = tid; j < npages; j += kThreads) {
         int p = a.page_table[(int64_t)b * a.max_pages + j];
         s_pages[j] = (p >= 0 && p < a.pool_pages) ? p : -1;
     }
     __syncthreads();
+    for (int t = tid; t < kMaxPages / 4; t += kThreads) {     // every slot: padded tiles read theirs
+        bool full = t < ntiles && (t + 1) * kKT <= si.kv;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) full = full && s_pages[min(t * 4 + q, npages - 1)] >= 0;
+        s_tile_full[t] = full ? 1 : 0;
+    }
+    __syncthreads();
 
     // ---- query fragments (B operand of S^T = K Q^T) ----
-    const int wrow = wave * 16;                 // this wave's first row within the tile
+    // Every global load below is unconditional (indices clamped to valid
+    // memory, the value selected afterwards): a load under a divergent branch
+    // makes the compiler wait for all outstanding loads, which would drain the
+    // prefetch ring.
+    const int wrow = wave * 16;
     const bool active = wrow < nr;
-    const int my_row = wrow + ln;               // row (within tile) this lane's column holds
+    const int my_row = wrow + ln;
     const bool row_ok = my_row < nr;
+    const int q_row = r0 + min(my_row, nr - 1);
     bf16x8 qf[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-        if (row_ok) {
-            qf[ks] = *(const bf16x8*)(a.q + (int64_t)(r0 + my_row) * a.n_out + h * kHD + ks * 32 + g * 8);
-        } else {
-            u32x4 z = {0u, 0u, 0u, 0u};
-            qf[ks] = __builtin_bit_cast(bf16x8, z);
-        }
+        u32x4 v = *(const u32x4*)(a.q + (int64_t)q_row * a.n_out + h * kHD + ks * 32 + g * 8);
+        u32x4 z = {0u, 0u, 0u, 0u};
+        qf[ks] = __builtin_bit_cast(bf16x8, row_ok ? v : z);
     }
     const bool has_mask = a.mask != nullptr;
-    const int64_t mrow_base = has_mask ? a.mask_off[b] + (int64_t)(qt * kQT + my_row) * ((si.kv + 31) / 32) : 0;
+    const int64_t mwords = (si.kv + 31) / 32;
+    const int64_t mrow_base = has_mask ? a.mask_off[b] + (int64_t)(qt * kQT + min(my_row, nr - 1)) * mwords : 0;
+    const int last_page = max(npages - 1, 0);
 
-    u32x4 rk[2], rv[2];
-    auto gload = [&](int kbase, bool with_v) {
+    // ---- K/V tile pipeline: 64 keys x 128 d, 16 B per thread per pass ----
+    // A prefetched value is never touched before its consumer (a select right
+    // after a load would make the compiler wait for it).  Keys past kv_len, or
+    // on a bad page, read the sequence's key 0 instead (a row the step reads
+    // anyway); the visibility bits give them probability exactly 0.
+    const int key0_page = npages > 0 ? s_pages[0] : -1;
+    const int64_t safe_row = key0_page >= 0 ? (int64_t)key0_page * 16 : 0;
+    u32x4 rk[kRing][2], rv[kRing][2];
+    uint32_t rmw[kRing][2];              // this lane's mask words for the tile (raw)
+    auto gload = [&](auto S, int t, bool with_v) __attribute__((always_inline)) {
+        constexpr int sl = decltype(S)::value;
+        {   // unconditional: tiles past the end load the safe row and are fully masked
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                int c = tid + i * kThreads;
+                int key = c >> 4, dc = c & 15;
+                int kg = t * kKT + key;
+                int page = s_pages[min(kg >> 4, last_page)];
+                bool ok = (kg < si.kv) & (page >= 0);
+                int64_t row = ok ? (int64_t)page * 16 + (kg & 15) : safe_row;
+                int64_t off = row * a.n_out + h * kHD + dc * 8;
+                rk[sl][i] = *(const u32x4*)(a.k + off);
+                if (with_v) rv[sl][i] = *(const u32x4*)(a.v + off);
+            }
+            if (has_mask) {
+                int64_t i0 = mrow_base + t * (kKT / 32);
+                rmw[sl][0] = a.mask[min(max(i0, (int64_t)0), a.mask_words - 1)];
+                rmw[sl][1] = a.mask[min(max(i0 + 1, (int64_t)0), a.mask_words - 1)];
+            }
+        }
+    };
+    // mask word validity of tile t for this lane (applied where the words are used)
+    auto mask_words_of = [&](auto S, int t, uint32_t& w0, uint32_t& w1) __attribute__((always_inline)) {
+        constexpr int sl = decltype(S)::value;
+        if (!has_mask) {
+            w0 = w1 = 0xffffffffu;
+            return;
+        }
+        int64_t i0 = mrow_base + t * (kKT / 32);
+        w0 = (row_ok && i0 >= 0 && i0 < a.mask_words) ? rmw[sl][0] : 0u;
+        w1 = (row_ok && i0 + 1 >= 0 && i0 + 1 < a.mask_words) ? rmw[sl][1] : 0u;
+    };
+    auto lstore = [&](auto S, int buf, bool with_v) __attribute__((always_inline)) {
+        constexpr int sl = decltype(S)::value;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             int c = tid + i * kThreads;
             int key = c >> 4, dc = c & 15;
-            int kg = kbase + key;
-            int page = (kg < si.kv) ? s_pages[kg >> 4] : -1;
-            u32x4 z = {0u, 0u, 0u, 0u};
-            rk[i] = z;
-            rv[i] = z;
-            if (page >= 0) {
-                int64_t off = ((int64_t)page * 16 + (kg & 15)) * a.n_out + h * kHD + dc * 8;
-                rk[i] = *(const u32x4*)(a.k + off);
-                if (with_v) rv[i] = *(const u32x4*)(a.v + off);
-            }
+            *(u32x4*)(&sK[buf][key * kLDK + dc * 8]) = rk[sl][i];
+            if (with_v) *(u32x4*)(&sV[buf][key * kLDK + dc * 8]) = rv[sl][i];
         }
     };
-    auto lstore = [&](bool with_v) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            int c = tid + i * kThreads;
-            int key = c >> 4, dc = c & 15;
-            *(u32x4*)(sK + key * kLDK + dc * 8) = rk[i];
-            if (with_v) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    sVt[(dc * 8 + 2 * e) * kLDV + key] = (uint16_t)(rv[i][e] & 0xffffu);
-                    sVt[(dc * 8 + 2 * e + 1) * kLDV + key] = (uint16_t)(rv[i][e] >> 16);
-                }
-            }
-        }
-    };
-    // S^T for one 64-key tile: 4 sub-tiles of 16 keys x this wave's 16 rows
-    auto scores = [&](f32x4 (&st)[4]) {
+    auto scores = [&](int buf, f32x4 (&st)[4]) __attribute__((always_inline)) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const uint16_t* krow = sK + perm_key(t, ln) * kLDK + g * 8;
+            const uint16_t* krow = &sK[buf][perm_key(t, ln) * kLDK + g * 8];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 bf16x8 kf = *(const bf16x8*)(krow + ks * 32);
@@ -250,147 +282,125 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
             }
         }
     };
-    // visibility of this lane's 16 scores in the tile starting at kbase
-    auto visible_bits = [&](int kbase) -> uint32_t {
+    // visibility of this lane's 16 scores in tile t (mask words come from the ring slot)
+    auto vis_bits = [&](int kbase, uint32_t w0, uint32_t w1) __attribute__((always_inline)) -> uint32_t {
         uint32_t bits = 0;
-        uint32_t w0 = 0xffffffffu, w1 = 0xffffffffu;
-        if (has_mask) {
-            w0 = w1 = 0u;
-            if (row_ok) {
-                int64_t i0 = mrow_base + kbase / 32;
-                if (i0 >= 0 && i0 < a.mask_words) w0 = a.mask[i0];
-                if (i0 + 1 >= 0 && i0 + 1 < a.mask_words) w1 = a.mask[i0 + 1];
-            }
-        }
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 int kk = reg_key(t, g, e);
                 int kg = kbase + kk;
-                bool ok = kg < k_hi && kg < si.kv && s_pages[kg >> 4] >= 0;
                 uint32_t w = (kk < 32) ? w0 : w1;
-                ok = ok && ((w >> (kk & 31)) & 1u);
+                bool ok = (kg < si.kv) & (s_pages[min(kg >> 4, last_page)] >= 0) & (((w >> (kk & 31)) & 1u) != 0);
                 bits |= (ok ? 1u : 0u) << (t * 4 + e);
             }
         return bits;
     };
 
-    // ---- main pass over this split's keys ----
     float m_run = kNegBig, l_run = 0.f;
     f32x4 acc[8];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nt_main = (k_hi - k_lo + kKT - 1) / kKT;
-    if (nt_main > 0) {
-        gload(k_lo, true);
-        lstore(true);
-    }
-    __syncthreads();
-    for (int t = 0; t < nt_main; ++t) {
-        const int kbase = k_lo + t * kKT;
-        if (t + 1 < nt_main) gload(kbase + kKT, true);
-        if (active) {
-            f32x4 st[4];
-            scores(st);
-            uint32_t vis = visible_bits(kbase);
-            float mx = kNegBig;
+    auto attend = [&](int buf, int t, uint32_t w0, uint32_t w1) __attribute__((always_inline)) {
+        const int kbase = t * kKT;
+        f32x4 st[4];
+        scores(buf, st);
+        // raw scores; the scale is folded into the exponent (c > 0 keeps the order)
+        const bool full = !has_mask && s_tile_full[t];
+        if (!full) {
+            const uint32_t vis = vis_bits(kbase, w0, w1);
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float s = st[tt][e] * a.scale_log2;
-                    s = ((vis >> (tt * 4 + e)) & 1u) ? s : -INFINITY;
-                    st[tt][e] = s;
-                    mx = fmaxf(mx, s);
-                }
-            mx = wave_max16(mx);
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = exp2f(m_run - m_new);
-            float rs = 0.f;
+                for (int e = 0; e < 4; ++e)
+                    st[tt][e] = ((vis >> (tt * 4 + e)) & 1u) ? st[tt][e] : -INFINITY;
+        }
+        float mx = -INFINITY;
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt)
+        for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float p = exp2f(st[tt][e] - m_new);
-                    st[tt][e] = p;
-                    rs += p;
-                }
-            rs = wave_sum16(rs);
-            l_run = l_run * alpha + rs;
-            m_run = m_new;
+            for (int e = 0; e < 4; ++e) mx = fmaxf(mx, st[tt][e]);
+        mx = wave_max16(mx);
+        const float m_new = fmaxf(m_run, mx * a.scale_log2);
+        float rs = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float p = __builtin_amdgcn_exp2f(fmaf(st[tt][e], a.scale_log2, -m_new));
+                st[tt][e] = p;
+                rs += p;
+            }
+        rs = wave_sum16(rs);
+        if (m_new != m_run) {                  // a row maximum moved: rescale that row
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
-            bf16x8 pf[2];
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                u32x4 u;
-                u[0] = pack_bf16x2(st[2 * c][0], st[2 * c][1]);
-                u[1] = pack_bf16x2(st[2 * c][2], st[2 * c][3]);
-                u[2] = pack_bf16x2(st[2 * c + 1][0], st[2 * c + 1][1]);
-                u[3] = pack_bf16x2(st[2 * c + 1][2], st[2 * c + 1][3]);
-                pf[c] = __builtin_bit_cast(bf16x8, u);
-            }
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    bf16x8 vf = *(const bf16x8*)(sVt + (dt * 16 + ln) * kLDV + c * 32 + g * 8);
-                    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[c], acc[dt], 0, 0, 0);
-                }
         }
+        l_run += rs;
+        m_run = m_new;
+        bf16x8 pf[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            u32x4 u;
+            u[0] = pack_bf16x2(st[2 * c][0], st[2 * c][1]);
+            u[1] = pack_bf16x2(st[2 * c][2], st[2 * c][3]);
+            u[2] = pack_bf16x2(st[2 * c + 1][0], st[2 * c + 1][1]);
+            u[3] = pack_bf16x2(st[2 * c + 1][2], st[2 * c + 1][3]);
+            pf[c] = __builtin_bit_cast(bf16x8, u);
+        }
+        // V^T fragments: source lane ln of group g points at key c*32 + 8g + 4*hf + (ln >> 2),
+        // column dt*16 + 4*(ln & 3)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const uint16_t* vbase = &sV[buf][(c * 32 + 8 * g + (ln >> 2)) * kLDK + 4 * (ln & 3)];
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                s16x4 lo4 = ds_read_tr(vbase + dt * 16);
+                s16x4 hi4 = ds_read_tr(vbase + 4 * kLDK + dt * 16);
+                typedef short s16x8 __attribute__((ext_vector_type(8)));
+                s16x8 v8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+                bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
+                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[c], acc[dt], 0, 0, 0);
+            }
+        }
+    };
+
+    // ---- main pass: all keys of the sequence, 3 tiles in flight ----
+    gload(Ic<0>{}, 0, true);
+    __builtin_amdgcn_sched_barrier(0);
+    gload(Ic<1>{}, 1, true);
+    __builtin_amdgcn_sched_barrier(0);
+    gload(Ic<2>{}, 2, true);
+    __builtin_amdgcn_sched_barrier(0);
+    lstore(Ic<0>{}, 0, true);
+    __syncthreads();
+    auto step_main = [&](auto S, int t) __attribute__((always_inline)) {
+        constexpr int sl = decltype(S)::value;            // t % kRing
+        uint32_t w0, w1;
+        mask_words_of(S, t, w0, w1);
+        gload(Ic<(sl + 3) % kRing>{}, t + 3, true);
+        __builtin_amdgcn_sched_barrier(0);      // keep the prefetch where it is issued
+        if (active) attend(t & 1, t, w0, w1);
         __syncthreads();
-        if (t + 1 < nt_main) lstore(true);
+        __builtin_amdgcn_sched_barrier(0);
+        lstore(Ic<(sl + 1) % kRing>{}, (t + 1) & 1, true);
         __syncthreads();
+    };
+    // the trip count is padded to whole rings so that no load sits under a
+    // branch (padded tiles see no key: alpha = 1, p = 0)
+    const int ntiles_pad = (ntiles + kRing - 1) / kRing * kRing;
+    for (int t = 0; t < ntiles_pad; t += kRing) {
+        step_main(Ic<0>{}, t);
+        step_main(Ic<1>{}, t + 1);
+        step_main(Ic<2>{}, t + 2);
+        step_main(Ic<3>{}, t + 3);
     }
 
-    // ---- merge key splits (last split of the tile finishes) ----
-    const int tile_item = s_pref[b] + (h * si.splits) * si.nqt + qt;   // split-0 item of this tile
-    if (si.splits > 1) {
-        float* po = a.part_o + (int64_t)item * kQT * kHD;
-        float* pml = a.part_ml + (int64_t)item * kQT * 2;
-        if (active) {
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-                *(f32x4*)(po + my_row * kHD + dt * 16 + g * 4) = acc[dt];
-            if (g == 0) {
-                pml[my_row * 2] = m_run;
-                pml[my_row * 2 + 1] = l_run;
-            }
-        }
-        __threadfence();
-        __syncthreads();
-        if (tid == 0) s_flag = (atomicAdd(&a.cnt_tile[tile_item], 1) == si.splits - 1);
-        __syncthreads();
-        if (!s_flag) return;
-        __threadfence();
-        if (active) {
-            float m = kNegBig;
-            for (int s = 0; s < si.splits; ++s) {
-                int it = s_pref[b] + (h * si.splits + s) * si.nqt + qt;
-                m = fmaxf(m, a.part_ml[(int64_t)it * kQT * 2 + my_row * 2]);
-            }
-            float l = 0.f;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (int s = 0; s < si.splits; ++s) {
-                int it = s_pref[b] + (h * si.splits + s) * si.nqt + qt;
-                float ms = a.part_ml[(int64_t)it * kQT * 2 + my_row * 2];
-                float ls = a.part_ml[(int64_t)it * kQT * 2 + my_row * 2 + 1];
-                float f = exp2f(ms - m);
-                l += ls * f;
-                const float* pos = a.part_o + (int64_t)it * kQT * kHD + my_row * kHD + g * 4;
-#pragma unroll
-                for (int dt = 0; dt < 8; ++dt) acc[dt] += *(const f32x4*)(pos + dt * 16) * f;
-            }
-            m_run = m;
-            l_run = l;
-        }
-        if (tid == 0) a.cnt_tile[tile_item] = 0;
-    }
-
-    // ---- final output ----
+    // ---- output ----
     if (row_ok) {
         const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
         uint16_t* orow = a.o + (int64_t)(r0 + my_row) * a.n_out + h * kHD + g * 4;
@@ -403,7 +413,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
         }
     }
 
-    // ---- formula (2): column mass of the masked-window rows ----
+    // ---- formula (2): this head's column mass from the masked-window rows ----
     if (qt != 0 || a.mass_accum == nullptr || a.mass_count == nullptr) return;
     int mb = a.mass_count[b];
     mb = max(0, min(mb, min(a.max_mass, min(si.rows, kQT))));
@@ -412,67 +422,66 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
     const bool mwave = wave < mass_waves;
     const bool mrow = my_row < mb;
     const float inv_l = (mrow && l_run > 0.f) ? 1.f / l_run : 0.f;
-    float* mpart = a.mass_part + ((int64_t)b * a.H + h) * a.n_cap;
-    const int nt_all = ktiles;
+    const float norm = 1.f / ((float)a.H * (float)mb);
+    float* macc = a.mass_accum + ((int64_t)b * a.H + h) * a.n_cap;
+    gload(Ic<0>{}, 0, false);
+    __builtin_amdgcn_sched_barrier(0);
+    gload(Ic<1>{}, 1, false);
+    __builtin_amdgcn_sched_barrier(0);
+    gload(Ic<2>{}, 2, false);
+    __builtin_amdgcn_sched_barrier(0);
+    lstore(Ic<0>{}, 0, false);
     __syncthreads();
-    gload(0, false);
-    lstore(false);
+    // column sums of this head accumulate in LDS (the V tiles are free now);
+    // the running score is read, updated and written once at the end
+    float* s_mass = reinterpret_cast<float*>(&sV[0][0]);
+    const int kmax = min(si.kv, a.n_cap);
+    constexpr int kMassLds = (int)(sizeof(sV) / sizeof(float));
+    for (int i = tid; i < kMassLds; i += kThreads) s_mass[i] = 0.f;
     __syncthreads();
-    for (int t = 0; t < nt_all; ++t) {
+    auto step_mass = [&](auto S, int t) __attribute__((always_inline)) {
+        constexpr int sl = decltype(S)::value;
+        const int buf = t & 1;
         const int kbase = t * kKT;
-        if (t + 1 < nt_all) gload(kbase + kKT, false);
+        uint32_t w0, w1;
+        mask_words_of(S, t, w0, w1);
+        gload(Ic<(sl + 3) % kRing>{}, t + 3, false);
+        __builtin_amdgcn_sched_barrier(0);
         if (mwave) {
             f32x4 st[4];
-            scores(st);
-            // visibility over the whole key range (not just one split)
-            uint32_t w0 = 0xffffffffu, w1 = 0xffffffffu;
-            if (has_mask) {
-                w0 = w1 = 0u;
-                if (row_ok) {
-                    int64_t i0 = mrow_base + kbase / 32;
-                    if (i0 >= 0 && i0 < a.mask_words) w0 = a.mask[i0];
-                    if (i0 + 1 >= 0 && i0 + 1 < a.mask_words) w1 = a.mask[i0 + 1];
-                }
-            }
+            scores(buf, st);
+            const bool full = !has_mask && s_tile_full[t];
+            const uint32_t vis = full ? 0xffffu : vis_bits(kbase, w0, w1);
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    int kk = reg_key(tt, g, e);
-                    int kg = kbase + kk;
-                    uint32_t w = (kk < 32) ? w0 : w1;
-                    bool ok = mrow && kg < si.kv && s_pages[kg >> 4] >= 0 && ((w >> (kk & 31)) & 1u);
-                    float p = ok ? exp2f(st[tt][e] * a.scale_log2 - m_run) * inv_l : 0.f;
-                    p = group_sum16(p);
-                    if (ln == 0) s_col[wave][kk] = p;
+                    bool ok = mrow && ((vis >> (tt * 4 + e)) & 1u);
+                    float p = __builtin_amdgcn_exp2f(fmaf(st[tt][e], a.scale_log2, -m_run)) * inv_l;
+                    p = row16_sum(ok ? p : 0.f);
+                    if (ln == 0) s_col[wave][reg_key(tt, g, e)] = p;
                 }
         }
         __syncthreads();
         if (tid < kKT) {
-            float s = 0.f;
-            for (int w = 0; w < mass_waves; ++w) s += s_col[w][tid];
-            int kg = kbase + tid;
-            if (kg < si.kv && kg < a.n_cap) mpart[kg] = s;
+            float sum = 0.f;
+            for (int w = 0; w < mass_waves; ++w) sum += s_col[w][tid];
+            const int kg = kbase + tid;
+            if (kg < kMassLds) s_mass[kg] += sum;
         }
-        if (t + 1 < nt_all) lstore(false);
+        __builtin_amdgcn_sched_barrier(0);
+        lstore(Ic<(sl + 1) % kRing>{}, (t + 1) & 1, false);
         __syncthreads();
+    };
+    if (kmax <= kMassLds) {
+        for (int t = 0; t < ntiles_pad; t += kRing) {
+            step_mass(Ic<0>{}, t);
+            step_mass(Ic<1>{}, t + 1);
+            step_mass(Ic<2>{}, t + 2);
+            step_mass(Ic<3>{}, t + 3);
+        }
+        for (int i = tid; i < kmax; i += kThreads) macc[i] += s_mass[i] * norm;
     }
-    // all heads of this sequence in: add the head-ordered sum into mass_accum
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_flag = (atomicAdd(&a.cnt_mass[b], 1) == a.H - 1);
-    __syncthreads();
-    if (!s_flag) return;
-    __threadfence();
-    const float norm = 1.f / ((float)a.H * (float)mb);
-    const int kmax = min(si.kv, a.n_cap);
-    const float* base = a.mass_part + (int64_t)b * a.H * a.n_cap;
-    for (int i = tid; i < kmax; i += kThreads) {
-        float s = 0.f;
-        for (int hh = 0; hh < a.H; ++hh) s += base[(int64_t)hh * a.n_cap + i];
-        a.mass_accum[(int64_t)b * a.n_cap + i] += s * norm;
-    }
-    if (tid == 0) a.cnt_mass[b] = 0;
 }
 
 // fp32 path (parity-sized shapes): one workgroup per (sequence, head) walks the
@@ -487,7 +496,6 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a, const
     __shared__ float s_colsum[kF32MaxKv];
     __shared__ float s_q[128];
     __shared__ float s_red[kF32Threads / 64];
-    __shared__ int s_flag;
     const int tid = threadIdx.x;
     const int b = blockIdx.x / a.H, h = blockIdx.x % a.H;
     const int D = a.head_dim;
@@ -557,63 +565,16 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a, const
         }
     }
     if (mb == 0 || si.kv == 0) return;
-    float* mpart = a.mass_part + ((int64_t)b * a.H + h) * a.n_cap;
     __syncthreads();
-    for (int j = tid; j < si.kv && j < a.n_cap; j += kF32Threads) mpart[j] = s_colsum[j];
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_flag = (atomicAdd(&a.cnt_mass[b], 1) == a.H - 1);
-    __syncthreads();
-    if (!s_flag) return;
-    __threadfence();
     const float norm = 1.f / ((float)a.H * (float)mb);
-    const float* base = a.mass_part + (int64_t)b * a.H * a.n_cap;
-    for (int i = tid; i < si.kv && i < a.n_cap; i += kF32Threads) {
-        float s = 0.f;
-        for (int hh = 0; hh < a.H; ++hh) s += base[(int64_t)hh * a.n_cap + i];
-        a.mass_accum[(int64_t)b * a.n_cap + i] += s * norm;
-    }
-    if (tid == 0) a.cnt_mass[b] = 0;
+    float* macc = a.mass_accum + ((int64_t)b * a.H + h) * a.n_cap;
+    for (int j = tid; j < si.kv && j < a.n_cap; j += kF32Threads) macc[j] += s_colsum[j] * norm;
 }
 
-struct AttnPlan {
-    int split_max, max_items;
-    size_t cnt_tile_bytes, cnt_mass_bytes, mass_part_bytes, part_o_bytes, part_ml_bytes;
-    size_t total() const {
-        return cnt_tile_bytes + cnt_mass_bytes + mass_part_bytes + part_o_bytes + part_ml_bytes;
-    }
-};
-
-size_t round256(size_t x) { return (x + 255) / 256 * 256; }
-
-AttnPlan plan(dllm_dtype dt, int n_seq, int n_rows, int n_heads, int head_dim, int max_kv,
-              int n_cap) {
-    AttnPlan p{};
-    if (dt == DLLM_BF16) {
-        int base_tiles = n_rows / kQT + n_seq;
-        int est = n_heads * (n_seq > (n_rows + kQT - 1) / kQT ? n_seq : (n_rows + kQT - 1) / kQT);
-        int s = 1;
-        if (est < 4 * kNumCu) s = (4 * kNumCu + est - 1) / est;
-        int ktiles = (max_kv + kKT - 1) / kKT;
-        if (s > ktiles) s = ktiles;
-        if (s > 16) s = 16;
-        if (s < 1) s = 1;
-        p.split_max = s;
-        p.max_items = n_heads * base_tiles * s;
-        p.cnt_tile_bytes = round256((size_t)p.max_items * sizeof(int32_t));
-        if (s > 1) {
-            p.part_o_bytes = round256((size_t)p.max_items * kQT * kHD * sizeof(float));
-            p.part_ml_bytes = round256((size_t)p.max_items * kQT * 2 * sizeof(float));
-        }
-    } else {
-        p.split_max = 1;
-        p.max_items = n_seq * n_heads;
-    }
-    p.cnt_mass_bytes = round256((size_t)n_seq * sizeof(int32_t));
-    p.mass_part_bytes = round256((size_t)n_seq * n_heads * n_cap * sizeof(float));
-    (void)head_dim;
-    return p;
-}
+// Items = (sequence, head, 128-row query tile); the launch is sized for the
+// worst case sum_b ceil(rows_b / 128) <= n_rows / 128 + n_seq, and surplus
+// workgroups exit after the schedule scan.
+int max_items(int n_seq, int n_rows, int n_heads) { return n_heads * (n_rows / kQT + n_seq); }
 
 int check_attn(dllm_dtype dt, int n_seq, int n_rows, int n_heads, int head_dim, int page_size,
                int max_kv, int n_cap) {
@@ -636,8 +597,8 @@ int check_attn(dllm_dtype dt, int n_seq, int n_rows, int n_heads, int head_dim, 
 extern "C" size_t dllm_sched_attention_workspace(dllm_dtype dt, int n_seq, int n_rows,
                                                  int n_heads, int head_dim, int max_kv,
                                                  int n_cap) {
-    if (check_attn(dt, n_seq, n_rows, n_heads, head_dim, 16, max_kv, n_cap) != DLLM_OK) return 0;
-    return plan(dt, n_seq, n_rows, n_heads, head_dim, max_kv, n_cap).total();
+    (void)dt; (void)n_seq; (void)n_rows; (void)n_heads; (void)head_dim; (void)max_kv; (void)n_cap;
+    return 0;      // every workgroup owns its outputs: no scratch memory
 }
 
 extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_heads,
@@ -651,7 +612,7 @@ extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_
                                     size_t workspace_bytes, hipStream_t stream) {
     int st = check_attn(dt, n_seq, n_rows, n_heads, head_dim, page_size, max_kv, n_cap);
     if (st != DLLM_OK) return st;
-    DLLM_CHECK_ARG(max_pages > 0 && cache_rows >= 0);
+    DLLM_CHECK_ARG(max_pages > 0 && cache_rows >= 16);
     DLLM_CHECK_SUP(max_pages <= kMaxPages);
     if (n_rows == 0) return DLLM_OK;
     DLLM_CHECK_ARG(q && cu_q && k_cache && v_cache && page_table && kv_len && o);
@@ -661,9 +622,11 @@ extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_
     if (want_mass) {
         DLLM_CHECK_ARG(n_cap > 0);
         DLLM_CHECK_SUP(max_mass_rows >= 0 && max_mass_rows <= kQT);
+        // the bf16 kernel sums a head's column mass in LDS: <= 8704 keys
+        if (dt == DLLM_BF16) DLLM_CHECK_SUP((max_kv < n_cap ? max_kv : n_cap) <= 8704);
     }
-    AttnPlan p = plan(dt, n_seq, n_rows, n_heads, head_dim, max_kv, n_cap);
-    DLLM_CHECK_ARG(workspace && workspace_bytes >= p.total());
+    (void)workspace;
+    (void)workspace_bytes;
 
     AttnArgs a{};
     a.n_seq = n_seq;
@@ -674,7 +637,6 @@ extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_
     a.max_kv = max_kv;
     a.max_pages = max_pages;
     a.n_cap = n_cap;
-    a.split_max = p.split_max;
     a.max_mass = want_mass ? max_mass_rows : 0;
     a.pool_pages = (int)(cache_rows / 16 < (1ll << 30) ? cache_rows / 16 : (1ll << 30));
     a.scale_log2 = kLog2e / sqrtf((float)head_dim);
@@ -690,20 +652,10 @@ extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_
     a.mass_count = want_mass ? mass_count : nullptr;
     a.mass_accum = want_mass ? mass_accum : nullptr;
     a.o = (uint16_t*)o;
-    char* ws = (char*)workspace;
-    a.cnt_tile = (int32_t*)ws;
-    ws += p.cnt_tile_bytes;
-    a.cnt_mass = (int32_t*)ws;
-    ws += p.cnt_mass_bytes;
-    a.mass_part = (float*)ws;
-    ws += p.mass_part_bytes;
-    a.part_o = p.part_o_bytes ? (float*)ws : nullptr;
-    ws += p.part_o_bytes;
-    a.part_ml = p.part_ml_bytes ? (float*)ws : nullptr;
-
     if (dt == DLLM_BF16) {
-        DLLM_CHECK_SUP(p.max_items > 0 && p.max_items < (1 << 30));
-        hipLaunchKernelGGL(attn_bf16_kernel, dim3(p.max_items), dim3(kThreads), 0, stream, a);
+        const int64_t items = (int64_t)n_heads * (n_rows / kQT + n_seq);
+        DLLM_CHECK_SUP(items > 0 && items < (1ll << 30));
+        hipLaunchKernelGGL(attn_bf16_kernel, dim3((unsigned)items), dim3(kThreads), 0, stream, a);
     } else {
         hipLaunchKernelGGL(attn_f32_kernel, dim3(n_seq * n_heads), dim3(kF32Threads), 0, stream,
                            a, (const float*)q, (const float*)k_cache, (const float*)v_cache,

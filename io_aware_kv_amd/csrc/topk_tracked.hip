@@ -5,7 +5,9 @@
 // the k decoded tokens with the largest formula-(2) score, together with the
 // newly decoded ones, are the next step's tracked set.
 //
-// One workgroup per sequence.  Each candidate becomes a 64-bit key whose high
+// One workgroup per sequence.  The score of position i is the sum over heads
+// (ascending head order, fp32) of the per-head accumulators the attention
+// kernel wrote.  Each candidate becomes a 64-bit key whose high
 // word orders scores descending and whose low word is the position, so an
 // ascending bitonic sort in LDS yields scores high-to-low with ties broken
 // towards the lower position; non-candidates sort last.
@@ -14,7 +16,7 @@
 namespace {
 
 constexpr int kThreads = 1024;
-constexpr int kMaxCap = 8192;
+constexpr int kMaxCap = 4096;
 constexpr int kMaxK = 256;
 
 __device__ __forceinline__ uint32_t order_desc(float f) {
@@ -23,14 +25,15 @@ __device__ __forceinline__ uint32_t order_desc(float f) {
     return ~asc;                                                  // descending in f
 }
 
-__global__ __launch_bounds__(kThreads) void topk_kernel(int n_cap, int k, float* mass,
+__global__ __launch_bounds__(kThreads) void topk_kernel(int n_heads, int n_cap, int k, float* mass,
                                                         const uint8_t* eligible, int32_t* idx,
                                                         float* val, int32_t* count,
                                                         int clear_mass) {
     __shared__ uint64_t keys[kMaxCap];
+    __shared__ float score[kMaxCap];
     __shared__ int s_cnt;
     const int b = blockIdx.x, tid = threadIdx.x;
-    float* mrow = mass + (int64_t)b * n_cap;
+    float* mseq = mass + (int64_t)b * n_heads * n_cap;
     const uint8_t* erow = eligible + (int64_t)b * n_cap;
     int n2 = 1;
     while (n2 < n_cap) n2 <<= 1;
@@ -39,9 +42,14 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(int n_cap, int k, float*
     int local = 0;
     for (int i = tid; i < n2; i += kThreads) {
         uint64_t key = ~0ull;
-        if (i < n_cap && erow[i]) {
-            key = ((uint64_t)order_desc(mrow[i]) << 32) | (uint32_t)i;
-            ++local;
+        if (i < n_cap) {
+            float sc = 0.f;
+            for (int hh = 0; hh < n_heads; ++hh) sc += mseq[(int64_t)hh * n_cap + i];
+            score[i] = sc;
+            if (erow[i]) {
+                key = ((uint64_t)order_desc(sc) << 32) | (uint32_t)i;
+                ++local;
+            }
         }
         keys[i] = key;
     }
@@ -67,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(int n_cap, int k, float*
         if (j < n) {
             int pos = (int)(keys[j] & 0xffffffffu);
             idx[(int64_t)b * k + j] = pos;
-            val[(int64_t)b * k + j] = mrow[pos];
+            val[(int64_t)b * k + j] = score[pos];
         } else {
             idx[(int64_t)b * k + j] = -1;
             val[(int64_t)b * k + j] = 0.f;
@@ -76,19 +84,19 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(int n_cap, int k, float*
     if (tid == 0) count[b] = n;
     if (clear_mass) {
         __syncthreads();
-        for (int i = tid; i < n_cap; i += kThreads) mrow[i] = 0.f;
+        for (int i = tid; i < n_heads * n_cap; i += kThreads) mseq[i] = 0.f;
     }
 }
 
 }  // namespace
 
-extern "C" int dllm_topk_tracked(int n_seq, int n_cap, int k, float* mass, const uint8_t* eligible,
-                                 int32_t* idx, float* val, int32_t* count, int clear_mass,
-                                 hipStream_t stream) {
-    DLLM_CHECK_ARG(n_seq > 0 && n_cap > 0 && k > 0);
+extern "C" int dllm_topk_tracked(int n_seq, int n_heads, int n_cap, int k, float* mass,
+                                 const uint8_t* eligible, int32_t* idx, float* val, int32_t* count,
+                                 int clear_mass, hipStream_t stream) {
+    DLLM_CHECK_ARG(n_seq > 0 && n_heads > 0 && n_cap > 0 && k > 0);
     DLLM_CHECK_SUP(k <= kMaxK && n_cap <= kMaxCap);
     DLLM_CHECK_ARG(mass && eligible && idx && val && count);
-    hipLaunchKernelGGL(topk_kernel, dim3(n_seq), dim3(kThreads), 0, stream, n_cap, k, mass,
+    hipLaunchKernelGGL(topk_kernel, dim3(n_seq), dim3(kThreads), 0, stream, n_heads, n_cap, k, mass,
                        eligible, idx, val, count, clear_mass);
     DLLM_CHECK_LAUNCH();
     return DLLM_OK;

@@ -58,7 +58,7 @@ def load() -> ctypes.CDLL:
     lib.dllm_sched_attention.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                          _i64, _vp, _i32, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _i32,
                                          _vp, _vp, _sz, _vp]
-    lib.dllm_topk_tracked.argtypes = [_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp]
+    lib.dllm_topk_tracked.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp]
     for name in ("dllm_build_block_table", "dllm_map_slots", "dllm_qkv_rope_cachewrite",
                  "dllm_sched_attention", "dllm_topk_tracked"):
         getattr(lib, name).restype = _i32
@@ -150,7 +150,7 @@ def sched_attention(q, cu_q, k_cache, v_cache, page_table, max_pages: int, kv_le
                     mass_count=None, max_mass_rows: int = 0, mass_accum=None, n_cap: int = 0,
                     page_size: int = PAGE, stream=None) -> None:
     dt = dtype_code(q)
-    ws_bytes = workspace.numel() * workspace.element_size()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     mask_words = 0 if mask_bits is None else mask_bits.numel()
     _check("dllm_sched_attention", load().dllm_sched_attention(
         dt, cu_q.numel() - 1, q.shape[0], n_heads, head_dim, page_size, max_kv, _ptr(q), _ptr(cu_q),
@@ -160,9 +160,10 @@ def sched_attention(q, cu_q, k_cache, v_cache, page_table, max_pages: int, kv_le
 
 
 def topk_tracked(mass, eligible, k: int, idx, val, count, clear_mass: bool = False, stream=None) -> None:
-    n_seq, n_cap = mass.shape
+    """mass: float32 [n_seq, n_heads, n_cap] per-head scores."""
+    n_seq, n_heads, n_cap = mass.shape
     _check("dllm_topk_tracked", load().dllm_topk_tracked(
-        n_seq, n_cap, k, _ptr(mass), _ptr(eligible), _ptr(idx), _ptr(val), _ptr(count),
+        n_seq, n_heads, n_cap, k, _ptr(mass), _ptr(eligible), _ptr(idx), _ptr(val), _ptr(count),
         1 if clear_mass else 0, _stream(stream)))
 
 

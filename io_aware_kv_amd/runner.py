@@ -63,7 +63,8 @@ class FlashCacheRunner:
             self.v_cache.append(torch.zeros(self.cache_rows, self.n_out, dtype=self.dtype, device=self.device))
         self.page_table = torch.empty(wl.n_seq * wl.max_pages, dtype=torch.int32, device=self.device)
         dllm.build_block_table(wl.seq_pages, wl.pool_perm, wl.pool_pages, wl.max_pages, self.page_table)
-        self.mass = torch.zeros(wl.n_seq, self.n_cap, dtype=torch.float32, device=self.device)
+        # formula (2) per-head running scores [B, H, n_cap]; top-k sums the heads
+        self.mass = torch.zeros(wl.n_seq, self.H, self.n_cap, dtype=torch.float32, device=self.device)
         self.eligible = torch.from_numpy(wl.eligible()).to(self.device)
         k = sh.top_k
         self.top_idx = torch.empty(wl.n_seq, k, dtype=torch.int32, device=self.device)

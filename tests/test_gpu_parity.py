@@ -26,6 +26,15 @@ def case(name, heavy=False):
     return _CASES[key]
 
 
+def head_sum(m):
+    """[B, H, n_cap] per-head scores -> [B, n_cap], summed in ascending head
+    order in fp32, the way dllm_topk_tracked forms its scores."""
+    out = np.zeros((m.shape[0], m.shape[2]), dtype=np.float32)
+    for h in range(m.shape[1]):
+        out = (out + m[:, h, :]).astype(np.float32)
+    return out
+
+
 def run_gpu_step(c: Case, step: int, gpu):
     import torch
     from io_aware_kv_amd.runner import FlashCacheRunner
@@ -45,7 +54,7 @@ def run_gpu_step(c: Case, step: int, gpu):
     x = run.to_device_array(x_raw)
     w = run.to_device_array(c.w_raw)
     run.layer_step(st, x, w, 0)
-    mass = run.mass.cpu().numpy().copy()
+    mass = head_sum(run.mass.cpu().numpy())
     run.topk(clear_mass=True)
     torch.cuda.synchronize()
     return {"run": run, "st": st, "k_before": k_before, "v_before": v_before, "mass": mass,
