@@ -20,9 +20,10 @@
  * Conventions shared by every entry point:
  *   - Ownership: the caller allocates and owns every buffer; the library never
  *     allocates or frees device memory and keeps no state between calls.  The
- *     *_workspace() queries report the scratch memory a call needs (currently
- *     0 bytes for every shape: each workgroup owns its outputs); a NULL
- *     workspace is accepted when the query returns 0.
+ *     *_workspace() queries report the scratch memory a call needs (a pure
+ *     function of the shape arguments; 0 for most shapes); a NULL workspace is
+ *     accepted when the query returns 0.  Workspace contents need no
+ *     initialisation, and two calls in flight at once must not share one.
  *   - Pointers named "host" are host memory; every other pointer is device
  *     memory of the current HIP device.  All device work is enqueued on
  *     `stream` and is asynchronous unless stated; buffers must stay valid until
@@ -162,7 +163,10 @@ int dllm_qkv_rope_cachewrite(dllm_dtype dt, int n_rows, int d_model, int n_heads
  *              heads (dllm_topk_tracked does) and over layers (by calling once
  *              per layer) this is formula (2)'s a_i.
  *   o          [R, H*D]            out: attention output
- * Scores are q.k/sqrt(D); a row that sees no key outputs zeros.
+ * Scores are q.k/sqrt(D); a row that sees no key outputs zeros.  When the
+ * batch has too few (sequence, head) pairs to fill the GPU, keys are split
+ * over workgroups and a second kernel merges them (workspace: per split, fp32
+ * partial outputs and row statistics).
  * Errors: INVALID_ARG (also cache_rows < 16), UNSUPPORTED (dtype/D/page_size/
  * n_seq > 1024/max_pages > 1024/bf16 score over more than 8704 keys).
  */

@@ -201,20 +201,27 @@ __global__ __launch_bounds__(kThreads) void qkv_bf16_kernel(QkvArgs a) {
 // HBM bandwidth is the whole game: W is 3*H*D x d_model and is read exactly
 // once.  Each workgroup owns 64 output columns of one (Q/K/V part, head): 32
 // "low" columns [j*32, j*32+32) and their rotation partners D/2 higher, so the
-// rotation stays inside the workgroup.  The 4 waves split the contraction into
-// quarters; each wave loads the x and W fragments of its quarter straight into
-// MFMA operand registers, a ring of DEPTH 32-wide k-steps (8 for R <= 80:
-// ~128 KB of W in flight per CU, what loaded HBM latency needs), so both
-// streams share one in-order wait counter at the same depth.  The four partial tiles
-// are summed in LDS in wave order (deterministic).  No split-K across
-// workgroups, so no cross-workgroup synchronisation.
+// rotation stays inside the workgroup; each of its 4 waves owns one 16-column
+// strip.  Both operands are read with coalesced 16-byte loads (16 lanes cover
+// one 256-byte row piece), DEPTH-1 K chunks ahead in a register ring, and
+// staged through a double-buffered LDS tile whose 16-byte slots are
+// XOR-swizzled by row, so the MFMA fragment reads are conflict-free.  A
+// sched_barrier pins the issue order so the in-order wait counter never waits
+// for a younger prefetch.  No split-K, so no cross-workgroup synchronisation.
+constexpr int kSkKC = 128;                 // K chunk (4 MFMA k-steps)
+
 template <int J>
 struct Ic { static constexpr int value = J; };
 
-template <int MT, int kSkDepth>   // 16-row tiles covering R; k-steps in flight
+template <int MT, int kDepth>   // 16-row tiles covering R; K chunks in flight + 1
 __global__ __launch_bounds__(256, 1) void qkv_skinny_kernel(QkvArgs a) {
+    constexpr int kRows = MT * 16;
+    constexpr int kXPer = kRows * (kSkKC / 8) / 256;      // x 16-byte pieces per thread
+    constexpr int kWPer = 64 * (kSkKC / 8) / 256;         // W pieces per thread (4)
     constexpr int kLDC = 64 + 4;
-    __shared__ __attribute__((aligned(16))) float Cs[MT * 16 * kLDC];
+    static_assert(kRows * (kSkKC / 8) % 256 == 0, "x chunk must split evenly");
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][kRows * kSkKC];
+    __shared__ __attribute__((aligned(16))) uint16_t ws[2][64 * kSkKC];
     __shared__ double s_theta[64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, ln = lane & 15;
@@ -227,82 +234,97 @@ __global__ __launch_bounds__(256, 1) void qkv_skinny_kernel(QkvArgs a) {
     const int head = ph % (a.n_out / D);
     const int col_base = part * a.n_out + head * D;      // first W row of this head
     const int R = a.R;
+    const int n_chunks = a.d_model / kSkKC;
     if (tid < half) s_theta[tid] = pow((double)a.rope_base, -2.0 * tid / D);
 
-    const int kq = a.d_model / 4;                        // this wave's contraction quarter
-    const int nsteps = kq / 32;
-    const uint16_t* xp[MT];
-    const uint16_t* wp[4];
+    // global pointers of this thread's pieces (row, 16-byte slot kc)
+    const uint16_t* xg[kXPer];
+    const uint16_t* wg[kWPer];
+    int xl[kXPer], wl[kWPer];                            // swizzled LDS offsets (halfwords)
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        int row = m * 16 + ln;
-        row = row < R ? row : R - 1;                      // padding rows repeat a real row
-        xp[m] = a.x + (int64_t)row * a.d_model + wave * kq + g * 8;
+    for (int i = 0; i < kXPer; ++i) {
+        int c = tid + i * 256, row = c >> 4, kc = c & 15;
+        int grow = row < R ? row : R - 1;                 // padding rows repeat a real row
+        xg[i] = a.x + (int64_t)grow * a.d_model + kc * 8;
+        xl[i] = row * kSkKC + ((kc ^ row) & 15) * 8;
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        int col = col_base + (t >= 2 ? half : 0) + j * 32 + (t & 1) * 16 + ln;
-        wp[t] = a.w + (int64_t)col * a.d_model + wave * kq + g * 8;
+    for (int i = 0; i < kWPer; ++i) {
+        int c = tid + i * 256, r = c >> 4, kc = c & 15;   // r: tile column 0..63
+        int wrow = col_base + (r >= 32 ? half : 0) + j * 32 + (r & 31);
+        wg[i] = a.w + (int64_t)wrow * a.d_model + kc * 8;
+        wl[i] = r * kSkKC + ((kc ^ r) & 15) * 8;
     }
-    bf16x8 ra[kSkDepth][MT], rb[kSkDepth][4];
-    f32x4 acc[MT][4];
+    u32x4 rx[kDepth][kXPer], rw[kDepth][kWPer];
+    f32x4 acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto load = [&](auto S, int c) __attribute__((always_inline)) {
+        constexpr int sl = decltype(S)::value;
+        const int cc = c < n_chunks ? c : n_chunks - 1;   // past the end: re-read the last chunk
+#pragma unroll
+        for (int i = 0; i < kWPer; ++i) rw[sl][i] = *(const u32x4*)(wg[i] + cc * kSkKC);
+#pragma unroll
+        for (int i = 0; i < kXPer; ++i) rx[sl][i] = *(const u32x4*)(xg[i] + cc * kSkKC);
+    };
+    auto store = [&](auto S, int buf) __attribute__((always_inline)) {
+        constexpr int sl = decltype(S)::value;
+#pragma unroll
+        for (int i = 0; i < kWPer; ++i) *(u32x4*)(&ws[buf][wl[i]]) = rw[sl][i];
+#pragma unroll
+        for (int i = 0; i < kXPer; ++i) *(u32x4*)(&xs[buf][xl[i]]) = rx[sl][i];
+    };
+    // this wave's 16 output columns: tile columns wave*16 .. wave*16+15
+    auto compute = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < kSkKC / 32; ++ks) {
+            const int kc = ks * 4 + g;
+            const int wr = wave * 16 + ln;
+            bf16x8 bw = *(const bf16x8*)(&ws[buf][wr * kSkKC + ((kc ^ wr) & 15) * 8]);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const int row = m * 16 + ln;
+                bf16x8 ax = *(const bf16x8*)(&xs[buf][row * kSkKC + ((kc ^ row) & 15) * 8]);
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bw, acc[m], 0, 0, 0);
+            }
+        }
+    };
+
+    // prologue: chunks 0 .. DEPTH-2 in flight, chunk 0 staged in LDS
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+        ((load(Ic<I>{}, I), __builtin_amdgcn_sched_barrier(0)), ...);
+    }(std::make_integer_sequence<int, kDepth - 1>{});
+    store(Ic<0>{}, 0);
+    __syncthreads();
+    // iteration c: issue chunk c+DEPTH-1, compute chunk c, stage chunk c+1.
+    // Loads, stores and barriers are unconditional (exact wait counts); only
+    // the LDS-only compute is skipped on the padded trip past the last chunk.
+    auto iter = [&](auto S, int c) __attribute__((always_inline)) {
+        constexpr int sl = decltype(S)::value;       // c % kDepth
+        load(Ic<(sl + kDepth - 1) % kDepth>{}, c + kDepth - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (c < n_chunks) compute(c & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        store(Ic<(sl + 1) % kDepth>{}, (c + 1) & 1);
+        __syncthreads();
+    };
+    const int n_pad = (n_chunks + kDepth - 1) / kDepth * kDepth;
+    for (int c0 = 0; c0 < n_pad; c0 += kDepth) {
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+            (iter(Ic<I>{}, c0 + I), ...);
+        }(std::make_integer_sequence<int, kDepth>{});
+    }
+
+    // ---- epilogue: fp32 tile [R_pad][64] in LDS, rotate pairs, write ----
+    float* Cs = reinterpret_cast<float*>(&xs[0][0]);
+    static_assert(kRows * kLDC * 4 <= (int)sizeof(xs), "epilogue tile must fit");
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    auto load = [&](auto S, int step) __attribute__((always_inline)) {
-        constexpr int sl = decltype(S)::value;
-        if (step < nsteps) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) rb[sl][t] = *(const bf16x8*)(wp[t] + step * 32);
-#pragma unroll
-            for (int m = 0; m < MT; ++m) ra[sl][m] = *(const bf16x8*)(xp[m] + step * 32);
-        }
-    };
-    auto mma = [&](auto S) __attribute__((always_inline)) {
-        constexpr int sl = decltype(S)::value;
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[sl][m], rb[sl][t], acc[m][t], 0, 0, 0);
-    };
-    // prologue: k-steps 0 .. DEPTH-2 in flight
-    [&]<int... I>(std::integer_sequence<int, I...>) {
-        ((load(Ic<I>{}, I), __builtin_amdgcn_sched_barrier(0)), ...);
-    }(std::make_integer_sequence<int, kSkDepth - 1>{});
-    auto iter = [&](auto S, int step) __attribute__((always_inline)) {
-        constexpr int sl = decltype(S)::value;
-        load(Ic<(sl + kSkDepth - 1) % kSkDepth>{}, step + kSkDepth - 1);
-        __builtin_amdgcn_sched_barrier(0);      // issue order = prefetch order
-        mma(S);
-    };
-    for (int st = 0; st < nsteps; st += kSkDepth) {
-        [&]<int... I>(std::integer_sequence<int, I...>) {
-            ((st + I < nsteps ? iter(Ic<I>{}, st + I) : void()), ...);
-        }(std::make_integer_sequence<int, kSkDepth>{});
-    }
-
-    // ---- sum the four quarter tiles in LDS, in wave order ----
-    for (int w = 0; w < 4; ++w) {
-        if (wave == w) {
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        int r = m * 16 + g * 4 + e;
-                        int c = (t >= 2 ? 32 : 0) + (t & 1) * 16 + ln;
-                        float v = acc[m][t][e];
-                        Cs[r * kLDC + c] = (w == 0) ? v : Cs[r * kLDC + c] + v;
-                    }
-        }
-        __syncthreads();
-    }
-
-    // ---- epilogue: rotate pairs, round, write ----
+        for (int e = 0; e < 4; ++e)
+            Cs[(m * 16 + g * 4 + e) * kLDC + wave * 16 + ln] = acc[m][e];
+    __syncthreads();
     const int cpart = head * D + j * 32;                // low column within the part
     for (int idx = tid; idx < R * 4; idx += 256) {
         const int r = idx >> 2, q = idx & 3;             // 8-column piece q of the 32 low columns
@@ -475,12 +497,12 @@ extern "C" int dllm_qkv_rope_cachewrite(dllm_dtype dt, int n_rows, int d_model, 
         switch ((n_rows + 15) / 16) {
             case 1: hipLaunchKernelGGL((qkv_skinny_kernel<1, 8>), grid, dim3(256), 0, stream, a); break;
             case 2: hipLaunchKernelGGL((qkv_skinny_kernel<2, 8>), grid, dim3(256), 0, stream, a); break;
-            case 3: hipLaunchKernelGGL((qkv_skinny_kernel<3, 8>), grid, dim3(256), 0, stream, a); break;
-            case 4: hipLaunchKernelGGL((qkv_skinny_kernel<4, 8>), grid, dim3(256), 0, stream, a); break;
-            case 5: hipLaunchKernelGGL((qkv_skinny_kernel<5, 8>), grid, dim3(256), 0, stream, a); break;
-            case 6: hipLaunchKernelGGL((qkv_skinny_kernel<6, 6>), grid, dim3(256), 0, stream, a); break;
-            case 7: hipLaunchKernelGGL((qkv_skinny_kernel<7, 6>), grid, dim3(256), 0, stream, a); break;
-            default: hipLaunchKernelGGL((qkv_skinny_kernel<8, 6>), grid, dim3(256), 0, stream, a); break;
+            case 3: hipLaunchKernelGGL((qkv_skinny_kernel<3, 6>), grid, dim3(256), 0, stream, a); break;
+            case 4: hipLaunchKernelGGL((qkv_skinny_kernel<4, 6>), grid, dim3(256), 0, stream, a); break;
+            case 5: hipLaunchKernelGGL((qkv_skinny_kernel<5, 6>), grid, dim3(256), 0, stream, a); break;
+            case 6: hipLaunchKernelGGL((qkv_skinny_kernel<6, 5>), grid, dim3(256), 0, stream, a); break;
+            case 7: hipLaunchKernelGGL((qkv_skinny_kernel<7, 5>), grid, dim3(256), 0, stream, a); break;
+            default: hipLaunchKernelGGL((qkv_skinny_kernel<8, 4>), grid, dim3(256), 0, stream, a); break;
         }
     } else {
         dim3 grid(p.n_ntiles, p.n_mtiles, 1);

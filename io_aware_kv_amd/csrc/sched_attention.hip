@@ -28,6 +28,7 @@
 // which only it writes: no atomics, no cross-workgroup synchronisation, and
 // the reduction order is fixed.
 #include <math.h>
+#include <stdlib.h>
 
 #include "common.h"
 
@@ -62,6 +63,9 @@ struct AttnArgs {
     const int32_t* mass_count;
     float* mass_accum;      // [n_seq, H, n_cap], this head's term added per layer
     uint16_t* o;
+    int splits;             // key splits per (sequence, head, query tile); 1 = fused path
+    float* part_o;          // split mode: [item][kQT][kHD] unnormalised outputs
+    float* part_ml;         // split mode: [item][kQT][2] running max (base 2) and sum
 };
 
 struct SeqInfo {
@@ -146,7 +150,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnArgs a) {
             int items = 0;
             if (b < a.n_seq) {
                 SeqInfo s = seq_info(a, b);
-                items = s.nqt * a.H;
+                items = s.nqt * a.H * a.splits;
             }
             int scan = items;
 #pragma unroll
@@ -177,11 +181,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnArgs a) {
     const SeqInfo si = seq_info(a, b);
     const int local = item - s_pref[b];
     const int qt = local % si.nqt;                      // consecutive items: next query tile, same head
-    const int h = local / si.nqt;
+    const int hs = local / si.nqt;
+    const int sp = hs % a.splits;                       // key split
+    const int h = hs / a.splits;
     const int seq_r0 = max(0, min(a.cu_q[b], a.n_rows));
     const int r0 = seq_r0 + qt * kQT;
     const int nr = min(kQT, si.rows - qt * kQT);
     const int ntiles = (si.kv + kKT - 1) / kKT;
+    const int tiles_per = (ntiles + a.splits - 1) / a.splits;
+    const int t_begin = min(sp * tiles_per, ntiles);    // this item's key tiles
+    const int t_end = min(t_begin + tiles_per, ntiles);
     const int npages = (si.kv + 15) / 16;
     for (int j = tid; j < npages; j += kThreads) {
         int p = a.page_table[(int64_t)b * a.max_pages + j];
@@ -236,7 +245,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnArgs a) {
                 int key = c >> 4, dc = c & 15;
                 int kg = t * kKT + key;
                 int page = s_pages[min(kg >> 4, last_page)];
-                bool ok = (kg < si.kv) & (page >= 0);
+                bool ok = (t < t_end) & (kg < si.kv) & (page >= 0);
                 int64_t row = ok ? (int64_t)page * 16 + (kg & 15) : safe_row;
                 int64_t off = row * a.n_out + h * kHD + dc * 8;
                 rk[sl][i] = *(const u32x4*)(a.k + off);
@@ -369,35 +378,52 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnArgs a) {
         }
     };
 
-    // ---- main pass: all keys of the sequence, 3 tiles in flight ----
-    gload(Ic<0>{}, 0, true);
+    // ---- main pass: this item's key tiles, 3 tiles in flight ----
+    gload(Ic<0>{}, t_begin, true);
     __builtin_amdgcn_sched_barrier(0);
-    gload(Ic<1>{}, 1, true);
+    gload(Ic<1>{}, t_begin + 1, true);
     __builtin_amdgcn_sched_barrier(0);
-    gload(Ic<2>{}, 2, true);
+    gload(Ic<2>{}, t_begin + 2, true);
     __builtin_amdgcn_sched_barrier(0);
     lstore(Ic<0>{}, 0, true);
     __syncthreads();
-    auto step_main = [&](auto S, int t) __attribute__((always_inline)) {
-        constexpr int sl = decltype(S)::value;            // t % kRing
+    // step i handles tile t_begin + i; ring slot and LDS buffer follow i
+    auto step_main = [&](auto S, int i) __attribute__((always_inline)) {
+        constexpr int sl = decltype(S)::value;            // i % kRing
+        const int t = t_begin + i;
         uint32_t w0, w1;
         mask_words_of(S, t, w0, w1);
         gload(Ic<(sl + 3) % kRing>{}, t + 3, true);
         __builtin_amdgcn_sched_barrier(0);      // keep the prefetch where it is issued
-        if (active) attend(t & 1, t, w0, w1);
+        if (active && t < t_end) attend(i & 1, t, w0, w1);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        lstore(Ic<(sl + 1) % kRing>{}, (t + 1) & 1, true);
+        lstore(Ic<(sl + 1) % kRing>{}, (i + 1) & 1, true);
         __syncthreads();
     };
     // the trip count is padded to whole rings so that no load sits under a
-    // branch (padded tiles see no key: alpha = 1, p = 0)
-    const int ntiles_pad = (ntiles + kRing - 1) / kRing * kRing;
-    for (int t = 0; t < ntiles_pad; t += kRing) {
-        step_main(Ic<0>{}, t);
-        step_main(Ic<1>{}, t + 1);
-        step_main(Ic<2>{}, t + 2);
-        step_main(Ic<3>{}, t + 3);
+    // branch (the padded steps only load and stage)
+    const int n_main = (t_end - t_begin + kRing - 1) / kRing * kRing;
+    for (int i = 0; i < n_main; i += kRing) {
+        step_main(Ic<0>{}, i);
+        step_main(Ic<1>{}, i + 1);
+        step_main(Ic<2>{}, i + 2);
+        step_main(Ic<3>{}, i + 3);
+    }
+
+    if (a.splits > 1) {
+        // split mode: publish the unnormalised partial; attn_finish_kernel
+        // merges the splits and forms the column mass
+        if (active) {
+            float* po = a.part_o + (int64_t)item * kQT * kHD + my_row * kHD + g * 4;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) *(f32x4*)(po + dt * 16) = acc[dt];
+            if (g == 0) {
+                a.part_ml[((int64_t)item * kQT + my_row) * 2] = m_run;
+                a.part_ml[((int64_t)item * kQT + my_row) * 2 + 1] = l_run;
+            }
+        }
+        return;
     }
 
     // ---- output ----
@@ -473,6 +499,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnArgs a) {
         lstore(Ic<(sl + 1) % kRing>{}, (t + 1) & 1, false);
         __syncthreads();
     };
+    const int ntiles_pad = (ntiles + kRing - 1) / kRing * kRing;
     if (kmax <= kMassLds) {
         for (int t = 0; t < ntiles_pad; t += kRing) {
             step_mass(Ic<0>{}, t);
@@ -481,6 +508,177 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnArgs a) {
             step_mass(Ic<3>{}, t + 3);
         }
         for (int i = tid; i < kmax; i += kThreads) macc[i] += s_mass[i] * norm;
+    }
+}
+
+// Split mode, second launch.  Items per sequence b: H * nqt merge items
+// (b, h, query tile) and, when formula (2) is requested, H * ntiles mass items
+// (b, h, key tile).  A merge item combines the key splits of its tile in split
+// order (fixed, so the result is deterministic) and writes o.  A mass item
+// rebuilds the masked-window rows' final log-sum-exp from the split partials,
+// recomputes those rows' scores against its 64 keys (S^T = K Q^T on MFMA) and
+// adds the column sums to mass_accum[b][h][its keys], which no other item
+// touches: no atomics and no cross-workgroup synchronisation.
+constexpr int kFinThreads = 256;
+
+__global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
+    __shared__ int s_pref[kMaxSeq + 1];
+    __shared__ int s_total;
+    __shared__ float s_lse[kQT];
+    __shared__ float s_csum[4][kKT];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, ln = lane & 15;
+    const bool want_mass = a.mass_accum != nullptr && a.mass_count != nullptr;
+    if (wave == 0) {
+        int base = 0;
+        for (int c = 0; c < a.n_seq; c += 64) {
+            int b = c + lane;
+            int items = 0;
+            if (b < a.n_seq) {
+                SeqInfo s = seq_info(a, b);
+                items = a.H * (s.nqt + (want_mass ? (s.kv + kKT - 1) / kKT : 0));
+            }
+            int scan = items;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                int t = __shfl_up(scan, off);
+                if (lane >= off) scan += t;
+            }
+            if (b < a.n_seq) s_pref[b + 1] = base + scan;
+            base += __shfl(scan, 63);
+        }
+        if (lane == 0) {
+            s_pref[0] = 0;
+            s_total = base;
+        }
+    }
+    __syncthreads();
+    const int total = s_total;
+    if (total > (int)gridDim.x || (int)blockIdx.x >= total) return;
+    const int item = xcd_remap(blockIdx.x, total);
+    int lo = 0, hi = a.n_seq - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (s_pref[mid] <= item) lo = mid; else hi = mid - 1;
+    }
+    const int b = lo;
+    const SeqInfo si = seq_info(a, b);
+    const int local = item - s_pref[b];
+    const int seq_r0 = max(0, min(a.cu_q[b], a.n_rows));
+    // split-mode item index of (b, h, split, qt) in the first launch
+    int first_items = 0;
+    {
+        // items of sequences before b in the first launch: recount (cheap, n_seq <= 1024)
+        for (int bb = lane; bb < b; bb += 64) first_items += seq_info(a, bb).nqt * a.H * a.splits;
+        for (int off = 32; off > 0; off >>= 1) first_items += __shfl_xor(first_items, off);
+    }
+    auto split_item = [&](int h, int spl, int qt) { return first_items + (h * a.splits + spl) * si.nqt + qt; };
+
+    if (local < a.H * si.nqt) {
+        // ---- merge item ----
+        const int qt = local % si.nqt, h = local / si.nqt;
+        const int r0 = seq_r0 + qt * kQT;
+        const int nr = min(kQT, si.rows - qt * kQT);
+        for (int idx = tid; idx < nr * (kHD / 8); idx += kFinThreads) {
+            const int r = idx / (kHD / 8), c8 = idx % (kHD / 8);
+            float m = -INFINITY;
+            for (int spl = 0; spl < a.splits; ++spl)
+                m = fmaxf(m, a.part_ml[((int64_t)split_item(h, spl, qt) * kQT + r) * 2]);
+            float l = 0.f, o8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int spl = 0; spl < a.splits; ++spl) {
+                const int64_t it = split_item(h, spl, qt);
+                const float ms = a.part_ml[(it * kQT + r) * 2];
+                const float f = exp2f(ms - m);
+                l += a.part_ml[(it * kQT + r) * 2 + 1] * f;
+                const float* po = a.part_o + (it * kQT + r) * kHD + c8 * 8;
+                f32x4 v0 = *(const f32x4*)po, v1 = *(const f32x4*)(po + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    o8[e] += v0[e] * f;
+                    o8[4 + e] += v1[e] * f;
+                }
+            }
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            u32x4 u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(o8[2 * e] * inv, o8[2 * e + 1] * inv);
+            *(u32x4*)(a.o + (int64_t)(r0 + r) * a.n_out + h * kHD + c8 * 8) = u;
+        }
+        return;
+    }
+
+    // ---- mass item: (h, key tile kt) of sequence b ----
+    const int ml = local - a.H * si.nqt;
+    const int ntiles = (si.kv + kKT - 1) / kKT;
+    const int kt = ml % ntiles, h = ml / ntiles;
+    int mb = a.mass_count[b];
+    mb = max(0, min(mb, min(a.max_mass, min(si.rows, kQT))));
+    if (mb == 0) return;
+    // final log-sum-exp (base 2) of each window row, merged over the splits
+    for (int r = tid; r < mb; r += kFinThreads) {
+        float m = -INFINITY;
+        for (int spl = 0; spl < a.splits; ++spl)
+            m = fmaxf(m, a.part_ml[((int64_t)split_item(h, spl, 0) * kQT + r) * 2]);
+        float l = 0.f;
+        for (int spl = 0; spl < a.splits; ++spl) {
+            const int64_t it = split_item(h, spl, 0);
+            l += a.part_ml[(it * kQT + r) * 2 + 1] * exp2f(a.part_ml[(it * kQT + r) * 2] - m);
+        }
+        s_lse[r] = l > 0.f ? m + __log2f(l) : INFINITY;      // a row that sees nothing adds 0
+    }
+    __syncthreads();
+    // wave w: keys kt*64 + 16w .. +15 (A operand, natural order) x window row tiles
+    const int kw = kt * kKT + wave * 16 + ln;               // this lane's key row for the A operand
+    const int pidx = min(kw, si.kv - 1) >> 4;
+    int page = a.page_table[(int64_t)b * a.max_pages + pidx];
+    const bool key_ok = kw < si.kv && page >= 0 && page < a.pool_pages;
+    const int64_t krow = key_ok ? (int64_t)page * 16 + (kw & 15) : 0;
+    bf16x8 kf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        kf[ks] = *(const bf16x8*)(a.k + krow * a.n_out + h * kHD + ks * 32 + g * 8);
+    const int rtiles = (mb + 15) / 16;
+    float csum[4] = {0.f, 0.f, 0.f, 0.f};                    // keys 16w + 4g + e
+    const bool has_mask = a.mask != nullptr;
+    const int64_t mwords = (si.kv + 31) / 32;
+    for (int rt = 0; rt < rtiles; ++rt) {
+        const int row = rt * 16 + ln;                        // this lane's window row (B operand / C column)
+        const int qrow = seq_r0 + min(row, mb - 1);
+        f32x4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            bf16x8 qf = *(const bf16x8*)(a.q + (int64_t)qrow * a.n_out + h * kHD + ks * 32 + g * 8);
+            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf, st, 0, 0, 0);
+        }
+        const float lse = row < mb ? s_lse[row] : INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int key = kt * kKT + wave * 16 + g * 4 + e;    // C layout: key 4g+e of the sub-tile
+            bool ok = row < mb && key < si.kv;
+            if (ok) {
+                int pg = a.page_table[(int64_t)b * a.max_pages + (key >> 4)];
+                ok = pg >= 0 && pg < a.pool_pages;
+            }
+            if (ok && has_mask) {
+                int64_t wi = a.mask_off[b] + (int64_t)row * mwords + key / 32;
+                ok = wi >= 0 && wi < a.mask_words && ((a.mask[wi] >> (key & 31)) & 1u);
+            }
+            float p = ok ? exp2f(fmaf(st[e], a.scale_log2, -lse)) : 0.f;
+            csum[e] += row16_sum(p);
+        }
+    }
+    if (ln == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_csum[wave][g * 4 + e] = csum[e];
+    }
+    __syncthreads();
+    if (tid < kKT) {
+        const int key = kt * kKT + tid;
+        if (key < si.kv && key < a.n_cap) {
+            const float norm = 1.f / ((float)a.H * (float)mb);
+            float* macc = a.mass_accum + ((int64_t)b * a.H + h) * a.n_cap;
+            macc[key] += s_csum[tid >> 4][tid & 15] * norm;
+        }
     }
 }
 
@@ -571,10 +769,42 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a, const
     for (int j = tid; j < si.kv && j < a.n_cap; j += kF32Threads) macc[j] += s_colsum[j] * norm;
 }
 
-// Items = (sequence, head, 128-row query tile); the launch is sized for the
-// worst case sum_b ceil(rows_b / 128) <= n_rows / 128 + n_seq, and surplus
-// workgroups exit after the schedule scan.
-int max_items(int n_seq, int n_rows, int n_heads) { return n_heads * (n_rows / kQT + n_seq); }
+// Items = (sequence, head, 128-row query tile[, key split]); the launch is
+// sized for the worst case sum_b ceil(rows_b / 128) <= n_rows / 128 + n_seq,
+// and surplus workgroups exit after the schedule scan.
+//
+// When batch x heads cannot fill the chip (one workgroup streams at most
+// ~50 GB/s), keys are split so that roughly 512 workgroups stream them, and a
+// second launch merges the splits and forms the column mass.
+// DLLM_ATTN_SPLITS overrides the split count (a tuning knob; the workspace
+// query reads it too, so the two agree).
+int choose_splits(dllm_dtype dt, int n_seq, int n_rows, int n_heads, int max_kv) {
+    if (dt != DLLM_BF16) return 1;
+    const int ktiles = (max_kv + kKT - 1) / kKT;
+    int s = 1;
+    const int qtiles = (n_rows + kQT - 1) / kQT;
+    const int est = n_heads * (n_seq > qtiles ? n_seq : qtiles);
+    if (est < kNumCu) {
+        s = (2 * kNumCu + est - 1) / est;
+        const int cap = ktiles / 2 > 1 ? ktiles / 2 : 1;     // at least two tiles per split
+        if (s > cap) s = cap;
+    }
+    const char* env = getenv("DLLM_ATTN_SPLITS");
+    if (env && atoi(env) > 0) s = atoi(env);
+    if (s > 16) s = 16;
+    if (s > ktiles) s = ktiles > 0 ? ktiles : 1;
+    return s < 1 ? 1 : s;
+}
+
+int64_t first_items(int n_seq, int n_rows, int n_heads, int splits) {
+    return (int64_t)n_heads * (n_rows / kQT + n_seq) * splits;
+}
+
+size_t split_workspace(int n_seq, int n_rows, int n_heads, int splits) {
+    if (splits <= 1) return 0;
+    const int64_t items = first_items(n_seq, n_rows, n_heads, splits);
+    return (size_t)items * kQT * (kHD + 2) * sizeof(float);
+}
 
 int check_attn(dllm_dtype dt, int n_seq, int n_rows, int n_heads, int head_dim, int page_size,
                int max_kv, int n_cap) {
@@ -597,8 +827,8 @@ int check_attn(dllm_dtype dt, int n_seq, int n_rows, int n_heads, int head_dim, 
 extern "C" size_t dllm_sched_attention_workspace(dllm_dtype dt, int n_seq, int n_rows,
                                                  int n_heads, int head_dim, int max_kv,
                                                  int n_cap) {
-    (void)dt; (void)n_seq; (void)n_rows; (void)n_heads; (void)head_dim; (void)max_kv; (void)n_cap;
-    return 0;      // every workgroup owns its outputs: no scratch memory
+    if (check_attn(dt, n_seq, n_rows, n_heads, head_dim, 16, max_kv, n_cap) != DLLM_OK) return 0;
+    return split_workspace(n_seq, n_rows, n_heads, choose_splits(dt, n_seq, n_rows, n_heads, max_kv));
 }
 
 extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_heads,
@@ -625,8 +855,9 @@ extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_
         // the bf16 kernel sums a head's column mass in LDS: <= 8704 keys
         if (dt == DLLM_BF16) DLLM_CHECK_SUP((max_kv < n_cap ? max_kv : n_cap) <= 8704);
     }
-    (void)workspace;
-    (void)workspace_bytes;
+    const int splits = choose_splits(dt, n_seq, n_rows, n_heads, max_kv);
+    const size_t ws_need = split_workspace(n_seq, n_rows, n_heads, splits);
+    DLLM_CHECK_ARG(workspace_bytes >= ws_need && (ws_need == 0 || workspace != nullptr));
 
     AttnArgs a{};
     a.n_seq = n_seq;
@@ -652,10 +883,23 @@ extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_
     a.mass_count = want_mass ? mass_count : nullptr;
     a.mass_accum = want_mass ? mass_accum : nullptr;
     a.o = (uint16_t*)o;
+    a.splits = splits;
+    if (splits > 1) {
+        const int64_t items = first_items(n_seq, n_rows, n_heads, splits);
+        a.part_o = (float*)workspace;
+        a.part_ml = a.part_o + items * kQT * kHD;
+    }
     if (dt == DLLM_BF16) {
-        const int64_t items = (int64_t)n_heads * (n_rows / kQT + n_seq);
+        const int64_t items = first_items(n_seq, n_rows, n_heads, splits);
         DLLM_CHECK_SUP(items > 0 && items < (1ll << 30));
         hipLaunchKernelGGL(attn_bf16_kernel, dim3((unsigned)items), dim3(kThreads), 0, stream, a);
+        if (splits > 1) {
+            DLLM_CHECK_LAUNCH();
+            int64_t fin = (int64_t)n_heads * (n_rows / kQT + n_seq);
+            if (want_mass) fin += (int64_t)n_heads * n_seq * ((max_kv + kKT - 1) / kKT);
+            DLLM_CHECK_SUP(fin < (1ll << 30));
+            hipLaunchKernelGGL(attn_finish_kernel, dim3((unsigned)fin), dim3(kFinThreads), 0, stream, a);
+        }
     } else {
         hipLaunchKernelGGL(attn_f32_kernel, dim3(n_seq * n_heads), dim3(kF32Threads), 0, stream,
                            a, (const float*)q, (const float*)k_cache, (const float*)v_cache,

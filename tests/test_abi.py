@@ -106,14 +106,19 @@ def test_kernel_entry_points_reject_bad_shapes(lib):
     assert lib.dllm_map_slots(0, 8, 16, 4, 4, fake, fake, fake, fake, None) == -1
 
 
-def test_workspace_queries_report_no_scratch(lib):
-    # every workgroup owns its outputs: no shape needs scratch memory
+def test_workspace_queries(lib):
+    # the projection never needs scratch; attention needs it only when keys are
+    # split (too few sequence x head pairs to fill the GPU), and then exactly
+    # the per-split partial outputs and row statistics
     q = lib.dllm_qkv_rope_cachewrite_workspace
     for shape in ((1, 72, 4096, 32, 128), (0, 88, 256, 4, 64), (1, 65536, 4096, 32, 128)):
         assert q(*shape) == 0
     w = lib.dllm_sched_attention_workspace
-    assert w(1, 1, 72, 32, 128, 512, 512) == 0
-    assert w(1, 32, 2304, 32, 128, 2048, 2048) == 0
+    assert w(1, 32, 2304, 32, 128, 2048, 2048) == 0          # 1024 pairs: fused path
+    assert w(0, 2, 88, 4, 64, 128, 128) == 0                 # fp32 path
+    small = w(1, 1, 72, 32, 128, 512, 512)                   # batch 1: keys split
+    assert small > 0 and small % (128 * 130 * 4) == 0
+    assert small == w(1, 1, 72, 32, 128, 512, 512)
 
 
 def test_pack_mask_layout():

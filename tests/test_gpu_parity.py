@@ -109,3 +109,15 @@ def test_heavy_hitter_topk_exact(name, gpu):
     c = case(name, heavy=True)
     g = run_gpu_step(c, 0, gpu)
     compare_step(c, g, 0, exact_topk=True, o_scale=4.0)
+
+
+@pytest.mark.parametrize("name,splits", [("tiny_bf16", "2"), ("llada_b1", "1"), ("llada_b1", "3"),
+                                         ("verify_b4", "1"), ("verify_b4", "5")])
+def test_attention_split_paths(name, splits, gpu, monkeypatch):
+    """Both attention paths (fused single launch, and key splits merged by a
+    second launch), including uneven splits, give the same parity."""
+    log(f"[gpu] attention with {splits} key splits on {name}")
+    monkeypatch.setenv("DLLM_ATTN_SPLITS", splits)
+    c = case(name)
+    g = run_gpu_step(c, 1, gpu)
+    compare_step(c, g, 1)
