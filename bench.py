@@ -204,11 +204,13 @@ def main():
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "qkv_rope_cachewrite_llada_b1_traffic.json")
     if args.workload == "llada_b1" and os.path.exists(tfile):
-        try:
-            tj = json.load(open(tfile))
-            traffic = tj.get("bytes_per_launch")
-        except Exception:
-            traffic = None
+        # counter-measured HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by
+        # a plain-copy calibration); only valid for the kernel source profiled
+        import hashlib
+        tj = json.load(open(tfile))
+        src = open(os.path.join(ROOT, tj["source"]), "rb").read()
+        if hashlib.sha256(src).hexdigest() == tj["source_sha256"]:
+            traffic = tj["bytes_per_launch"]
 
     # ---- optional plain copy (calibrates the HBM byte counters) ----
     if args.copy_probe_mib:
