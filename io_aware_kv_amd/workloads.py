@@ -338,3 +338,44 @@ def sentinel_cache(wl: Workload, rows: int, width: int, salt: int) -> np.ndarray
     r = _rng(wl.wid, 7, salt)
     v = r.uniform(-4.0, 4.0, size=(rows, width)).astype(np.float32)
     return v if wl.shape.dtype == "f32" else round_bf16_bits(v)
+
+
+# ---------------------------------------------------------------------------
+# Large workloads: draws on the device (torch's seeded generator), because
+# drawing ~10^8 normals per layer on the host would dominate every run.  The
+# oracle receives copies of the same device values.
+# ---------------------------------------------------------------------------
+
+def device_normal_bf16(shape, std: float, seed: int, device):
+    """N(0, std^2) drawn in fp32 with a seeded torch generator on `device`,
+    rounded once (RNE) to bf16."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    t = torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    return t.to(torch.bfloat16)
+
+
+def device_weights(wl: Workload, layer: int, device):
+    sh = wl.shape
+    n = sh.n_heads * sh.head_dim
+    return device_normal_bf16((3 * n, sh.d_model), 1.0 / np.sqrt(sh.d_model),
+                              (1000 * wl.wid + 1) * 4096 + layer, device)
+
+
+def device_activations(wl: Workload, rows: StepRows, step: int, layer: int, device):
+    return device_normal_bf16((rows.n_rows, wl.shape.d_model), 1.0,
+                              ((1000 * wl.wid + 2) * 64 + step) * 4096 + layer, device)
+
+
+def seeded_tracked(wl: Workload, step: int) -> List[np.ndarray]:
+    """Tracked positions chosen by a seeded draw among the eligible ones (used
+    where a step's row set must not depend on either side's top-k)."""
+    r = _rng(wl.wid, 8, step)
+    out = []
+    for s in wl.seqs:
+        cand = np.flatnonzero(s.eligible(wl.n_cap))
+        out.append(np.sort(r.choice(cand, size=min(wl.shape.top_k, len(cand)), replace=False)).astype(np.int32))
+    return out
