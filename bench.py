@@ -39,7 +39,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="llada_b1", choices=["llada_b1", "mixed_b8", "verify_b4"])
+    p.add_argument("--workload", default="llada_b1",
+                   choices=["llada_b1", "mixed_b8", "verify_b4", "llada_b32"])
     p.add_argument("--rotate-gib", type=float, default=1.0)
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -64,6 +65,8 @@ def main():
     dllm.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == "llada_b32":
+        return bench_layers(args, dev)
     wl = W.make_workload(args.workload)
     sh = wl.shape
     n_out = sh.n_heads * sh.head_dim
@@ -254,6 +257,137 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_layers(args, dev):
+    """32-layer batch-32 sweep: alternating full-refresh steps (2048 rows per
+    sequence per layer) and cache-phase steps (72 rows per sequence per layer),
+    one top-k per step after the last layer."""
+    import numpy as np
+    import torch
+    from io_aware_kv_amd import dllm
+    from io_aware_kv_amd import workloads as W
+    from io_aware_kv_amd.runner import FlashCacheRunner
+    wl = W.make_workload("llada_b32")
+    sh = wl.shape
+    L, n = sh.layers, sh.n_heads * sh.head_dim
+    run = FlashCacheRunner(wl, device=dev)
+    Ws = [W.device_weights(wl, l, dev) for l in range(L)]
+    rows = {"full": W.full_refresh_rows(wl)}
+    sts = {"full": run.upload_step(rows["full"])}
+    xs = {"full": [W.device_activations(wl, rows["full"], 0, l, dev) for l in range(L)]}
+
+    def step(kind, ev=None):
+        st = sts[kind]
+        run.map_slots(st)
+        for l in range(L):
+            if ev is not None:
+                ev[l][0].record()
+            run.cache_update(st, xs[kind][l], Ws[l], l)
+            if ev is not None:
+                ev[l][1].record()
+            run.attention(st, l)
+            if ev is not None:
+                ev[l][2].record()
+        run.topk(clear_mass=True)
+
+    step("full")
+    idx = run.top_idx.cpu().numpy()
+    rows["cache"] = W.config_step_rows(wl, [idx[b][idx[b] >= 0] for b in range(wl.n_seq)])
+    sts["cache"] = run.upload_step(rows["cache"])
+    xs["cache"] = [W.device_activations(wl, rows["cache"], 1, l, dev) for l in range(L)]
+    for _ in range(max(1, args.warmup // 10)):
+        step("cache")
+        step("full")
+    torch.cuda.synchronize()
+    K = max(2, min(args.steps, 10))
+    res = {}
+    for kind in ("full", "cache"):
+        evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(L)] for _ in range(K)]
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(K):
+            step(kind, evs[i])
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / K
+        qkv_us = float(np.mean([evs[i][l][0].elapsed_time(evs[i][l][1]) for i in range(K) for l in range(L)])) * 1e3
+        att_us = float(np.mean([evs[i][l][1].elapsed_time(evs[i][l][2]) for i in range(K) for l in range(L)])) * 1e3
+        R = rows[kind].n_rows
+        kv = rows[kind].kv_len.astype(np.int64)
+        cu = rows[kind].cu_q.astype(np.int64)
+        qkv_flops = 2 * R * sh.d_model * 3 * n
+        qkv_bytes = 3 * n * sh.d_model * 2 + R * 32 * 1024
+        att_flops = int(sum(4 * (cu[b + 1] - cu[b]) * kv[b] * n for b in range(wl.n_seq)))
+        att_bytes = int(kv.sum()) * 2 * n * 2 + 2 * R * n * 2
+        b_qkv = max(qkv_bytes / (HBM_PEAK_GBS * 1e9), qkv_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
+        b_att = max(att_bytes / (HBM_PEAK_GBS * 1e9), att_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
+        res[kind] = {"rows_per_layer": R, "ms_per_step": ms, "us_per_layer": ms * 1e3 / L,
+                     "tokens_per_s_per_layer": R / (ms * 1e-3 / L),
+                     "qkv_us": qkv_us, "qkv_bound_us": b_qkv, "qkv_frac": b_qkv / qkv_us,
+                     "qkv_bound": "mfma" if qkv_flops / 2.5e15 > qkv_bytes / 8e12 else "hbm",
+                     "attn_us": att_us, "attn_bound_us": b_att, "attn_frac": b_att / att_us,
+                     "attn_bound": "mfma" if att_flops / 2.5e15 > att_bytes / 8e12 else "hbm",
+                     "layer_roofline_frac": (b_qkv + b_att) / (ms * 1e3 / L)}
+        eprint(f"[bench] llada_b32 {kind}: {res[kind]}")
+    tot_rows = sum(res[k]["rows_per_layer"] for k in res)
+    tot_ms = sum(res[k]["ms_per_step"] for k in res)
+    value = tot_rows / (tot_ms * 1e-3 / L)
+    dom = res["full"]
+    out = {
+        "metric": "refreshed tokens/s per layer (cache-update+attention)",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": 2 * K, "warmup": args.warmup,
+        "ms_per_step": tot_ms / 2, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "LLaDA-8B-shaped 32-layer sweep (d_model 4096, 32x128 heads, bf16), batch 32, "
+                               "context 2048 (prompt 1536 + gen 512); alternating full-refresh (2048 rows/seq) and "
+                               "cache-phase (72 rows/seq) steps, top-32 once per step",
+                   "layers": L, "batch": wl.n_seq, "parallelism": "single GPU", "timing": "stream launches"},
+        "steps_detail": res,
+        "roofline": {"bound": "mfma", "kernel": "qkv_rope_cachewrite (full refresh)",
+                     "achieved": 2 * dom["rows_per_layer"] * sh.d_model * 3 * n / (dom["qkv_us"] * 1e-6) / 1e12,
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": dom["qkv_frac"], "traffic": None},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_b32(wl, rows["cache"], args.cpu_seconds),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_b32(wl, rows, seconds):
+    """The oracle on one sequence's cache-phase rows of one layer (72 rows over
+    2048 keys), repeated for about `seconds`; tokens/s scales linearly with
+    rows, sequences and layers, so this is the batch figure too."""
+    import numpy as np
+    import oracle as O
+    from io_aware_kv_amd import workloads as W
+    sh = wl.shape
+    n = sh.n_heads * sh.head_dim
+    r0, r1 = int(rows.cu_q[0]), int(rows.cu_q[1])
+    kv = int(rows.kv_len[0])
+    rng = np.random.default_rng(0)
+    w = rng.standard_normal((3 * n, sh.d_model)) / np.sqrt(sh.d_model)
+    x = rng.standard_normal((r1 - r0, sh.d_model))
+    pages = (kv + W.PAGE - 1) // W.PAGE
+    table = O.build_block_table([pages], list(range(pages)), pages, pages)
+    kc = np.zeros((pages * W.PAGE, n))
+    vc = np.zeros_like(kc)
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        O.layer_step(x, w, rows.pos[r0:r1], rows.logical[r0:r1], [0, r1 - r0], [kv], [int(rows.mass_count[0])],
+                     kc, vc, table, sh.n_heads, sh.head_dim, sh.rope_base, W.PAGE)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": (r1 - r0) * reps / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} oracle layer steps of one sequence's cache-phase rows ({r1 - r0} rows, {kv} keys, "
+                      f"fp64 NumPy) in {el:.1f} s; extrapolated linearly to the batch"}
 
 
 def describe(name):
