@@ -15,9 +15,12 @@
 // rotated with an fp64-reduced angle, rounded once to bf16 and written as
 // 16-byte row segments of q_out or of the slot's cache row.
 //   * R <= 128 (cache phase): qkv_skinny_kernel streams W once at HBM rate.
-//   * larger R (full refresh): qkv_bf16_kernel, LDS-tiled 128 x 128 tiles.
+//   * large R (full refresh): qkv_gemm_kernel, 256 x 256 tiles fed by
+//     direct-to-LDS copies.
+//   * in between: qkv_bf16_kernel, LDS-tiled 128 x 128 tiles.
 #include <math.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <utility>
 
@@ -366,6 +369,217 @@ __global__ __launch_bounds__(256, 1) void qkv_skinny_kernel(QkvArgs a) {
     }
 }
 
+// Full-refresh projection (large R): 256 x 256 output tiles, 4 waves each
+// owning a 128 x 128 sub-tile, i.e. 128 rows by one whole head of 128
+// columns.  The MFMA computes the transposed tile (W rows as its A operand),
+// so a lane's four accumulator values are four consecutive output columns of
+// one row: they pack into one 8-byte LDS write, and the rotate-half partner
+// (column c + 64) of each sits in the same lane four n-tiles further on.
+//
+// Operands reach LDS through 16-byte direct-to-LDS loads (no register
+// staging), NS stages of BK = 32 deep.  A direct-to-LDS load writes lane i's
+// 16 bytes to LDS offset base + 16 i, so the XOR swizzle that keeps the
+// fragment reads free of bank conflicts is applied on the source side: lane i
+// fetches the logical 16-byte slot that belongs at its physical place.
+//
+// Pipeline (one wave per SIMD, so every stall idles that SIMD's matrix
+// unit): the fragments of stage kt+1 are read from LDS while the 64 MFMAs of
+// stage kt run, and one of the wave's copy instructions for stage kt+NS is
+// issued after each group of 8 MFMAs rather than all at once, which would
+// fill the address queue and hold up the wave.  One barrier per stage both
+// publishes stage kt+1 and frees stage kt's buffer for the copy of kt+NS.
+//
+// Tiles are ordered in groups of 4 row tiles x all column tiles, column
+// major inside a group, so the 32 workgroups one XCD runs at a time cover
+// 4 x 8 tiles and share their x and W slices in that XCD's L2.
+constexpr int kGBM = 256, kGBN = 256, kGBK = 32, kGNS = 4;
+constexpr int kGroupM = 4;
+
+// Physical 16-byte slot of logical slot 0 in a 64-byte staged row: any 16
+// consecutive rows read at one logical slot hit 16 distinct bank groups (and
+// every 8 consecutive rows 8 distinct ones), so the fragment reads are free
+// of bank conflicts.
+__device__ __forceinline__ int gemm_swz(int row) { return ((row >> 2) ^ (row >> 1)) & 3; }
+
+// s_waitcnt immediate: vector-memory count vm, LDS/scalar count lgkm, no wait
+// on the export counter
+__device__ __forceinline__ constexpr int waitcnt_imm(int vm, int lgkm) {
+    return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
+}
+
+__global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(QkvArgs a, int n_mtiles, int n_ntiles) {
+    constexpr int BK = kGBK, NS = kGNS;
+    constexpr int kSlots = BK / 8;                      // 16-byte slots per staged row
+    constexpr int kRowsPerInst = 64 / kSlots;           // rows one 1 KiB copy instruction covers
+    constexpr int kInst = (kGBM + kGBN) / kRowsPerInst / 4;   // copy instructions per wave per stage
+    constexpr int kStage = (kGBM + kGBN) * BK;          // halfwords per stage
+    static_assert(NS * kStage == 4 * 128 * 128, "the epilogue reuses the stages as four 128 x 128 tiles");
+    static_assert(NS >= 2 && NS <= 4 && kInst == 8 && 2 * kInst < 64, "wait counts below");
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NS * kStage];
+    __shared__ double s_theta[64];
+    __shared__ int s_pos[kGBM], s_slot[kGBM];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, ln = lane & 15;
+    const int wm = wave >> 1, wn = wave & 1;
+    // ---- tile order: XCD-contiguous items, grouped 4 row tiles x all column tiles ----
+    const int item = xcd_remap(blockIdx.x, n_mtiles * n_ntiles);
+    const int per_group = kGroupM * n_ntiles;
+    const int first_m = (item / per_group) * kGroupM;
+    const int gm_sz = min(kGroupM, n_mtiles - first_m);
+    const int local = item % per_group;
+    const int mt = first_m + local % gm_sz, nt = local / gm_sz;
+    const int row0 = mt * kGBM, col0 = nt * kGBN;
+    if (tid < a.head_dim / 2) s_theta[tid] = pow((double)a.rope_base, -2.0 * tid / a.head_dim);
+    {
+        const int grow = min(row0 + tid, a.R - 1);      // blockDim.x == kGBM
+        s_pos[tid] = a.pos[grow];
+        s_slot[tid] = a.slot[grow];
+    }
+
+    // ---- copy sources: instruction j of a stage covers rows kRowsPerInst*j ..; x first, then W ----
+    const uint16_t* src[kInst];
+#pragma unroll
+    for (int i = 0; i < kInst; ++i) {
+        const int j = wave * kInst + i;
+        const int r = (j * kRowsPerInst) % kGBM + lane / kSlots;
+        const int kc = (lane % kSlots) ^ gemm_swz(r);
+        if (j * kRowsPerInst < kGBM) {
+            int grow = row0 + r;
+            grow = grow < a.R ? grow : a.R - 1;         // ragged tail: re-read a real row, never stored
+            src[i] = a.x + (int64_t)grow * a.d_model + kc * 8;
+        } else {
+            src[i] = a.w + (int64_t)(col0 + r) * a.d_model + kc * 8;
+        }
+    }
+    auto issue_one = [&](int stage, int kt, int i) __attribute__((always_inline)) {
+        const int j = wave * kInst + i;
+        __builtin_amdgcn_global_load_lds((const void*)(src[i] + kt * BK),
+                                         (__attribute__((address_space(3))) void*)(smem + stage * kStage + j * 512),
+                                         16, 0, 0);
+    };
+    // fragments: x rows (MFMA B operand, 16 tokens) and W rows (MFMA A operand, 16 features)
+    auto read_x = [&](int kt, int i) __attribute__((always_inline)) {
+        const int r = wm * 128 + i * 16 + ln;
+        return *(const bf16x8*)(smem + (kt % NS) * kStage + r * BK + ((g ^ gemm_swz(r)) % kSlots) * 8);
+    };
+    auto read_w = [&](int kt, int t) __attribute__((always_inline)) {
+        const int c = wn * 128 + t * 16 + ln;
+        return *(const bf16x8*)(smem + (kt % NS) * kStage + kGBM * BK + c * BK +
+                                ((g ^ gemm_swz(c)) % kSlots) * 8);
+    };
+    // This thread's copies of stage `next` have landed (later stages may stay
+    // in flight) and its fragment reads have returned; then meet the other
+    // waves.  A plain barrier: the fence of __syncthreads would also wait for
+    // the stages in flight.
+    const int n_kt = a.d_model / BK;
+    auto stage_barrier = [&](int next) __attribute__((always_inline)) {
+        const int ahead = min(NS - 2, n_kt - 1 - next);
+        if (NS >= 4 && ahead >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kInst, 0));
+        else if (NS >= 3 && ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_imm(kInst, 0));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+        __builtin_amdgcn_s_barrier();
+    };
+
+    // acc[i][t]: tokens wm*128 + 16 i + (lane % 16), features wn*128 + 16 t + 4 (lane / 16) + e
+    f32x4 acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+        if (s < n_kt)
+#pragma unroll
+            for (int i = 0; i < kInst; ++i) issue_one(s, s, i);
+    bf16x8 cx[8], cw[8];
+    stage_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) cw[t] = read_w(0, t);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cx[i] = read_x(0, i);
+    for (int kt = 0; kt < n_kt; ++kt) {
+        // After the last stage the reads below are of a stale buffer and go
+        // unused: kept unconditional so the fragment registers need no merge.
+        stage_barrier(kt + 1);
+        const bool more = kt + NS < n_kt;
+        bf16x8 nx[8], nw[8];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cw[t], cx[i], acc[i][t], 0, 0, 0);
+            if (more) issue_one(kt % NS, kt + NS, i);
+            nw[i] = read_w(kt + 1, i);
+            nx[i] = read_x(kt + 1, i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            cx[i] = nx[i];
+            cw[i] = nw[i];
+        }
+    }
+
+    // ---- epilogue: rotate in registers (pairs are n-tiles t and t+4), bf16, via LDS to rows ----
+    const int part = col0 / a.n_out;                    // 0 = Q, 1 = K, 2 = V (tiles never straddle parts)
+    const int cpart = col0 % a.n_out + wn * 128;        // first column of this wave's head within the part
+    if (part < 2) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const double th = s_theta[t * 16 + g * 4 + e];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    double ang = (double)s_pos[wm * 128 + i * 16 + ln] * th;
+                    ang -= rint(ang * (1.0 / kTwoPi)) * kTwoPi;
+                    // hardware sin/cos take revolutions; |rev| <= 1/2 after the fp64
+                    // reduction (library sincosf here would push the accumulators
+                    // out of registers)
+                    const float rev = (float)(ang * (1.0 / kTwoPi));
+                    const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
+                    const float x0 = acc[i][t][e], x1 = acc[i][t + 4][e];
+                    acc[i][t][e] = x0 * cs - x1 * sn;
+                    acc[i][t + 4][e] = x1 * cs + x0 * sn;
+                }
+            }
+    }
+    __syncthreads();                                    // every wave is done reading the stages
+    // this wave's 128 x 128 bf16 tile (32 KiB), rows of 16 pieces of 16 bytes,
+    // piece p of row r stored at piece p ^ (r % 16)
+    uint16_t* tile = smem + wave * (128 * 128);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int r = i * 16 + ln, c = t * 16 + g * 4;
+            uint2 v;
+            v.x = pack_bf16x2(acc[i][t][0], acc[i][t][1]);
+            v.y = pack_bf16x2(acc[i][t][2], acc[i][t][3]);
+            *(uint2*)(&tile[r * 128 + (((c >> 3) ^ (r & 15)) << 3) + (c & 7)]) = v;
+        }
+    __syncthreads();
+    // 128 rows x 16 pieces of 16 B; a pass covers 4 rows
+    for (int pass = 0; pass < 32; ++pass) {
+        const int r = pass * 4 + (lane >> 4), pc = lane & 15;
+        const int grow = row0 + wm * 128 + r;
+        if (grow >= a.R) break;
+        const u32x4 v = *(const u32x4*)(&tile[r * 128 + ((pc ^ (r & 15)) << 3)]);
+        uint16_t* dst;
+        if (part == 0) {
+            dst = a.q_out + (int64_t)grow * a.n_out;
+        } else {
+            const int sl = s_slot[wm * 128 + r];
+            if (sl < 0 || (int64_t)sl >= a.cache_rows) continue;
+            dst = (part == 1 ? a.k_cache : a.v_cache) + (int64_t)sl * a.n_out;
+        }
+        *(u32x4*)(dst + cpart + pc * 8) = v;
+    }
+}
+
 // fp32 path (parity-sized shapes): one thread per (row, Q/K/V part, head,
 // rotation pair) forms both columns of the pair, rotates and stores them.
 __global__ void qkv_f32_kernel(int R, int d_model, int n_heads, int head_dim, float rope_base,
@@ -413,19 +627,38 @@ __global__ void qkv_f32_kernel(int R, int d_model, int n_heads, int head_dim, fl
     dst[c_hi] = hi;
 }
 
+enum QkvKind { kSkinny, kTiled128, kGemm256 };
+
 struct QkvPlan {
-    bool skinny;
+    QkvKind kind;
     int bm, n_mtiles, n_ntiles, n_ktiles;
 };
 
-// Cache-phase row counts (R <= 128) take the weight-streaming kernel; larger
-// R takes the LDS-tiled kernel.  Neither splits K, so no workspace is needed.
-QkvPlan plan_bf16(int R, int d_model, int n_out) {
+// Cache-phase row counts (R <= 128) take the weight-streaming kernel.  Row
+// counts that give at least two 256 x 256 tiles per compute unit take the
+// large-tile kernel (head_dim 128, whole heads per wave); the rest take the
+// 128 x 128 LDS-tiled kernel.  None splits K, so no workspace is needed.
+// DLLM_QKV_KERNEL=tiled|gemm overrides the choice where the shape allows it.
+QkvPlan plan_bf16(int R, int d_model, int n_out, int head_dim) {
     QkvPlan p{};
-    p.skinny = R <= 128 && d_model % 128 == 0;
-    p.bm = R <= 64 ? 64 : 128;
-    p.n_mtiles = (R + p.bm - 1) / p.bm;
-    p.n_ntiles = 3 * n_out / kBN;
+    const bool gemm_ok = head_dim == 128 && n_out % kGBN == 0 && d_model % kGBK == 0;
+    const int64_t tiles256 = (int64_t)((R + kGBM - 1) / kGBM) * (3 * n_out / kGBN);
+    if (R <= 128 && d_model % 128 == 0) p.kind = kSkinny;
+    else if (gemm_ok && tiles256 >= 2 * kNumCu) p.kind = kGemm256;
+    else p.kind = kTiled128;
+    if (const char* e = getenv("DLLM_QKV_KERNEL")) {
+        if (!strcmp(e, "tiled")) p.kind = kTiled128;
+        else if (!strcmp(e, "gemm") && gemm_ok) p.kind = kGemm256;
+    }
+    if (p.kind == kGemm256) {
+        p.bm = kGBM;
+        p.n_mtiles = (R + kGBM - 1) / kGBM;
+        p.n_ntiles = 3 * n_out / kGBN;
+    } else {
+        p.bm = R <= 64 ? 64 : 128;
+        p.n_mtiles = (R + p.bm - 1) / p.bm;
+        p.n_ntiles = 3 * n_out / kBN;
+    }
     p.n_ktiles = d_model / kBK;
     return p;
 }
@@ -473,7 +706,7 @@ extern "C" int dllm_qkv_rope_cachewrite(dllm_dtype dt, int n_rows, int d_model, 
         DLLM_CHECK_LAUNCH();
         return DLLM_OK;
     }
-    QkvPlan p = plan_bf16(n_rows, d_model, n_out);
+    QkvPlan p = plan_bf16(n_rows, d_model, n_out, head_dim);
     (void)workspace;
     (void)workspace_bytes;
     DLLM_CHECK_SUP(p.n_mtiles < 65536);
@@ -492,7 +725,12 @@ extern "C" int dllm_qkv_rope_cachewrite(dllm_dtype dt, int n_rows, int d_model, 
     a.k_cache = (uint16_t*)k_cache;
     a.v_cache = (uint16_t*)v_cache;
     a.cache_rows = cache_rows;
-    if (p.skinny) {
+    if (p.kind == kGemm256) {
+        const int64_t tiles = (int64_t)p.n_mtiles * p.n_ntiles;
+        DLLM_CHECK_SUP(tiles < (1ll << 31));
+        hipLaunchKernelGGL(qkv_gemm_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, a,
+                           p.n_mtiles, p.n_ntiles);
+    } else if (p.kind == kSkinny) {
         dim3 grid(3 * n_out / 64);
         switch ((n_rows + 15) / 16) {
             case 1: hipLaunchKernelGGL((qkv_skinny_kernel<1, 8>), grid, dim3(256), 0, stream, a); break;

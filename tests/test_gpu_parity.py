@@ -121,3 +121,17 @@ def test_attention_split_paths(name, splits, gpu, monkeypatch):
     c = case(name)
     g = run_gpu_step(c, 1, gpu)
     compare_step(c, g, 1)
+
+
+@pytest.mark.parametrize("name,kernel", [("llada_b1", "gemm"), ("mixed_b8", "tiled"), ("tiny_bf16", "gemm")])
+def test_projection_kernel_paths(name, kernel, gpu, monkeypatch):
+    """The full-refresh projection has two tiled kernels (128 x 128 tiles, and
+    256 x 256 tiles for large row counts); forcing the one the shape would not
+    pick gives the same parity, ragged row tails included (512 rows is two
+    256-row tiles, 6297 rows leaves a tail of 153; tiny_bf16 is one row tile
+    by three column tiles over a contraction of 256)."""
+    log(f"[gpu] projection kernel {kernel} on {name}")
+    monkeypatch.setenv("DLLM_QKV_KERNEL", kernel)
+    c = case(name)
+    g = run_gpu_step(c, 0, gpu)
+    compare_step(c, g, 0)
