@@ -14,7 +14,8 @@
 // the epilogue without leaving the workgroup: the fp32 tile is staged in LDS,
 // rotated with an fp64-reduced angle, rounded once to bf16 and written as
 // 16-byte row segments of q_out or of the slot's cache row.
-//   * R <= 128 (cache phase): qkv_skinny_kernel streams W once at HBM rate.
+//   * R <= 128 (cache phase): qkv_stream_kernel streams W once, deep rings of
+//     direct-to-LDS copies keeping enough bytes in flight for HBM rate.
 //   * large R (full refresh): qkv_gemm_kernel, 256 x 256 tiles fed by
 //     direct-to-LDS copies.
 //   * in between: qkv_bf16_kernel, LDS-tiled 128 x 128 tiles.
@@ -22,7 +23,6 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include <utility>
 
 #include "common.h"
 
@@ -197,175 +197,6 @@ __global__ __launch_bounds__(kThreads) void qkv_bf16_kernel(QkvArgs a) {
         }
         *(u32x4*)(dst + c_lo) = plo;
         *(u32x4*)(dst + c_hi) = phi;
-    }
-}
-
-// Skinny projection (R <= 128 rows: the cache phase).  Streaming W at full
-// HBM bandwidth is the whole game: W is 3*H*D x d_model and is read exactly
-// once.  Each workgroup owns 64 output columns of one (Q/K/V part, head): 32
-// "low" columns [j*32, j*32+32) and their rotation partners D/2 higher, so the
-// rotation stays inside the workgroup; each of its 4 waves owns one 16-column
-// strip.  Both operands are read with coalesced 16-byte loads (16 lanes cover
-// one 256-byte row piece), DEPTH-1 K chunks ahead in a register ring, and
-// staged through a double-buffered LDS tile whose 16-byte slots are
-// XOR-swizzled by row, so the MFMA fragment reads are conflict-free.  A
-// sched_barrier pins the issue order so the in-order wait counter never waits
-// for a younger prefetch.  No split-K, so no cross-workgroup synchronisation.
-constexpr int kSkKC = 128;                 // K chunk (4 MFMA k-steps)
-
-template <int J>
-struct Ic { static constexpr int value = J; };
-
-template <int MT, int kDepth>   // 16-row tiles covering R; K chunks in flight + 1
-__global__ __launch_bounds__(256, 1) void qkv_skinny_kernel(QkvArgs a) {
-    constexpr int kRows = MT * 16;
-    constexpr int kXPer = kRows * (kSkKC / 8) / 256;      // x 16-byte pieces per thread
-    constexpr int kWPer = 64 * (kSkKC / 8) / 256;         // W pieces per thread (4)
-    constexpr int kLDC = 64 + 4;
-    static_assert(kRows * (kSkKC / 8) % 256 == 0, "x chunk must split evenly");
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][kRows * kSkKC];
-    __shared__ __attribute__((aligned(16))) uint16_t ws[2][64 * kSkKC];
-    __shared__ double s_theta[64];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 4, ln = lane & 15;
-    const int D = a.head_dim, half = D >> 1;
-    const int groups_per_head = D / 64;
-    const int grp = blockIdx.x;                          // (part, head, j)
-    const int j = grp % groups_per_head;
-    const int ph = grp / groups_per_head;                // part * H + head
-    const int part = ph / (a.n_out / D);
-    const int head = ph % (a.n_out / D);
-    const int col_base = part * a.n_out + head * D;      // first W row of this head
-    const int R = a.R;
-    const int n_chunks = a.d_model / kSkKC;
-    if (tid < half) s_theta[tid] = pow((double)a.rope_base, -2.0 * tid / D);
-
-    // global pointers of this thread's pieces (row, 16-byte slot kc)
-    const uint16_t* xg[kXPer];
-    const uint16_t* wg[kWPer];
-    int xl[kXPer], wl[kWPer];                            // swizzled LDS offsets (halfwords)
-#pragma unroll
-    for (int i = 0; i < kXPer; ++i) {
-        int c = tid + i * 256, row = c >> 4, kc = c & 15;
-        int grow = row < R ? row : R - 1;                 // padding rows repeat a real row
-        xg[i] = a.x + (int64_t)grow * a.d_model + kc * 8;
-        xl[i] = row * kSkKC + ((kc ^ row) & 15) * 8;
-    }
-#pragma unroll
-    for (int i = 0; i < kWPer; ++i) {
-        int c = tid + i * 256, r = c >> 4, kc = c & 15;   // r: tile column 0..63
-        int wrow = col_base + (r >= 32 ? half : 0) + j * 32 + (r & 31);
-        wg[i] = a.w + (int64_t)wrow * a.d_model + kc * 8;
-        wl[i] = r * kSkKC + ((kc ^ r) & 15) * 8;
-    }
-    u32x4 rx[kDepth][kXPer], rw[kDepth][kWPer];
-    f32x4 acc[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    auto load = [&](auto S, int c) __attribute__((always_inline)) {
-        constexpr int sl = decltype(S)::value;
-        const int cc = c < n_chunks ? c : n_chunks - 1;   // past the end: re-read the last chunk
-#pragma unroll
-        for (int i = 0; i < kWPer; ++i) rw[sl][i] = *(const u32x4*)(wg[i] + cc * kSkKC);
-#pragma unroll
-        for (int i = 0; i < kXPer; ++i) rx[sl][i] = *(const u32x4*)(xg[i] + cc * kSkKC);
-    };
-    auto store = [&](auto S, int buf) __attribute__((always_inline)) {
-        constexpr int sl = decltype(S)::value;
-#pragma unroll
-        for (int i = 0; i < kWPer; ++i) *(u32x4*)(&ws[buf][wl[i]]) = rw[sl][i];
-#pragma unroll
-        for (int i = 0; i < kXPer; ++i) *(u32x4*)(&xs[buf][xl[i]]) = rx[sl][i];
-    };
-    // this wave's 16 output columns: tile columns wave*16 .. wave*16+15
-    auto compute = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int ks = 0; ks < kSkKC / 32; ++ks) {
-            const int kc = ks * 4 + g;
-            const int wr = wave * 16 + ln;
-            bf16x8 bw = *(const bf16x8*)(&ws[buf][wr * kSkKC + ((kc ^ wr) & 15) * 8]);
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const int row = m * 16 + ln;
-                bf16x8 ax = *(const bf16x8*)(&xs[buf][row * kSkKC + ((kc ^ row) & 15) * 8]);
-                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bw, acc[m], 0, 0, 0);
-            }
-        }
-    };
-
-    // prologue: chunks 0 .. DEPTH-2 in flight, chunk 0 staged in LDS
-    [&]<int... I>(std::integer_sequence<int, I...>) {
-        ((load(Ic<I>{}, I), __builtin_amdgcn_sched_barrier(0)), ...);
-    }(std::make_integer_sequence<int, kDepth - 1>{});
-    store(Ic<0>{}, 0);
-    __syncthreads();
-    // iteration c: issue chunk c+DEPTH-1, compute chunk c, stage chunk c+1.
-    // Loads, stores and barriers are unconditional (exact wait counts); only
-    // the LDS-only compute is skipped on the padded trip past the last chunk.
-    auto iter = [&](auto S, int c) __attribute__((always_inline)) {
-        constexpr int sl = decltype(S)::value;       // c % kDepth
-        load(Ic<(sl + kDepth - 1) % kDepth>{}, c + kDepth - 1);
-        __builtin_amdgcn_sched_barrier(0);
-        if (c < n_chunks) compute(c & 1);
-        __builtin_amdgcn_sched_barrier(0);
-        store(Ic<(sl + 1) % kDepth>{}, (c + 1) & 1);
-        __syncthreads();
-    };
-    const int n_pad = (n_chunks + kDepth - 1) / kDepth * kDepth;
-    for (int c0 = 0; c0 < n_pad; c0 += kDepth) {
-        [&]<int... I>(std::integer_sequence<int, I...>) {
-            (iter(Ic<I>{}, c0 + I), ...);
-        }(std::make_integer_sequence<int, kDepth>{});
-    }
-
-    // ---- epilogue: fp32 tile [R_pad][64] in LDS, rotate pairs, write ----
-    float* Cs = reinterpret_cast<float*>(&xs[0][0]);
-    static_assert(kRows * kLDC * 4 <= (int)sizeof(xs), "epilogue tile must fit");
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            Cs[(m * 16 + g * 4 + e) * kLDC + wave * 16 + ln] = acc[m][e];
-    __syncthreads();
-    const int cpart = head * D + j * 32;                // low column within the part
-    for (int idx = tid; idx < R * 4; idx += 256) {
-        const int r = idx >> 2, q = idx & 3;             // 8-column piece q of the 32 low columns
-        float lo[8], hi[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            lo[e] = Cs[r * kLDC + q * 8 + e];
-            hi[e] = Cs[r * kLDC + 32 + q * 8 + e];
-        }
-        uint16_t* dst;
-        if (part == 0) {
-            dst = a.q_out + (int64_t)r * a.n_out;
-        } else {
-            int sl = a.slot[r];
-            if (sl < 0 || (int64_t)sl >= a.cache_rows) continue;
-            dst = (part == 1 ? a.k_cache : a.v_cache) + (int64_t)sl * a.n_out;
-        }
-        if (part < 2) {
-            const double p = (double)a.pos[r];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                double ang = p * s_theta[j * 32 + q * 8 + e];
-                ang -= rint(ang * (1.0 / kTwoPi)) * kTwoPi;
-                float sn, cs;
-                sincosf((float)ang, &sn, &cs);
-                float x0 = lo[e], x1 = hi[e];
-                lo[e] = x0 * cs - x1 * sn;
-                hi[e] = x1 * cs + x0 * sn;
-            }
-        }
-        u32x4 plo, phi;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            plo[e] = pack_bf16x2(lo[2 * e], lo[2 * e + 1]);
-            phi[e] = pack_bf16x2(hi[2 * e], hi[2 * e + 1]);
-        }
-        *(u32x4*)(dst + cpart + q * 8) = plo;
-        *(u32x4*)(dst + cpart + half + q * 8) = phi;
     }
 }
 
@@ -580,6 +411,200 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(QkvArgs a, int n_mtile
     }
 }
 
+// Cache-phase projection (R <= 128 rows).  Streaming W from HBM is the whole
+// cost (W is read exactly once), so what matters is the number of bytes in
+// flight: at ~2 us of memory latency the GPU needs ~11 MB outstanding to run
+// at HBM rate.  Each of 256-odd workgroups owns PP = 8 NT rotation pairs
+// (columns c and c + D/2 of one head, over the flattened Q/K/V pair list),
+// i.e. 2 PP rows of W.  Each of its 4 waves streams every fourth 32-wide K
+// chunk of both x (R_pad rows, from L2) and its W rows through a private
+// ring of NSW direct-to-LDS stages: no barriers in the main loop, and a ring
+// as deep as LDS allows.  The waves' partial sums meet once, in LDS, for the
+// rotation (one pow per pair, hardware sin/cos per element) and the 16-byte
+// stores.
+constexpr int kStreamLds = 144 * 1024;     // ring (and, after the loop, the partial sums)
+constexpr int kStreamMaxRows = 128;
+
+template <int MT, int NT>
+struct StreamCfg {
+    static constexpr int kRows = MT * 16 + NT * 16;          // staged rows: x (padded), then W lo, W hi
+    static constexpr int kInst = kRows / 16;                  // 1 KiB copies per stage (16 rows of 64 B)
+    static constexpr int kStage = kRows * 32;                 // halfwords per stage
+    static constexpr int kNsw = (kStreamLds / (4 * kRows * 64)) < 8 ? (kStreamLds / (4 * kRows * 64)) : 8;
+    static constexpr int kPP = NT * 8;                        // pairs per workgroup
+    static constexpr int kLdc = 2 * kPP + 4;                  // partial-sum row stride (floats)
+    static constexpr int kRing = 4 * kNsw * kStage;           // halfwords
+    static constexpr int kCs = 4 * MT * 16 * kLdc * 2 + kPP * 4;   // partial sums + pair frequencies, halfwords
+    static constexpr int kSmem = kRing > kCs ? kRing : kCs;
+    static_assert(kNsw >= 2 && kNsw * kInst < 64, "ring depth / wait count");
+    static_assert(kSmem * 2 <= kStreamLds, "LDS budget");
+};
+
+template <int MT, int NT>
+__global__ __launch_bounds__(256, 1) void qkv_stream_kernel(QkvArgs a, int n_pairs) {
+    using C = StreamCfg<MT, NT>;
+    constexpr int kPP = C::kPP, kInst = C::kInst, kNsw = C::kNsw, kStage = C::kStage;
+    constexpr int kPieces = kPP / 8;                       // 8-pair output pieces per row
+    constexpr int kItems = (kStreamMaxRows * kPieces + 255) / 256;   // epilogue items per thread
+    __shared__ __attribute__((aligned(16))) uint16_t smem[C::kSmem];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, ln = lane & 15;
+    const int D = a.head_dim, half = D >> 1, H = a.n_out / D;
+    const int p0 = blockIdx.x * kPP;
+    const int n_chunks = a.d_model / 32;
+    const int n_local = n_chunks / 4;                      // chunks of this wave: c = 4 j + wave
+
+    // Epilogue items (row, 8-pair piece) of this thread: idx = tid + 256 k.
+    // Their positions and slots are fetched now, older than every copy below.
+    int it_pos[kItems], it_slot[kItems];
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+        const int idx = tid + 256 * k;
+        const int r = min(idx / kPieces, a.R - 1);
+        it_pos[k] = a.pos[r];
+        it_slot[k] = a.slot[r];
+    }
+
+    // copy sources: instruction i covers staged rows 16 i .. 16 i + 15, lane -> row + lane / 4
+    const uint16_t* src[kInst];
+#pragma unroll
+    for (int i = 0; i < kInst; ++i) {
+        const int r = i * 16 + (lane >> 2);
+        const int kc = (lane & 3) ^ gemm_swz(r);
+        const uint16_t* row_ptr;
+        if (r < MT * 16) {
+            row_ptr = a.x + (int64_t)min(r, a.R - 1) * a.d_model;          // padding rows repeat a real row
+        } else {
+            const int wr = r - MT * 16;                                      // 0 .. 2 PP - 1
+            const int p = min(p0 + (wr % kPP), n_pairs - 1);                 // past the last pair: repeat it
+            const int hp = p / half, i_pair = p % half;
+            const int part = hp / H, head = hp % H;
+            const int64_t wrow = (int64_t)part * a.n_out + head * D + i_pair + (wr >= kPP ? half : 0);
+            row_ptr = a.w + wrow * a.d_model;
+        }
+        src[i] = row_ptr + kc * 8;
+    }
+    uint16_t* ring = smem + wave * (kNsw * kStage);
+    auto issue = [&](int slot, int j) __attribute__((always_inline)) {
+        const int c = 4 * min(j, n_local - 1) + wave;     // past the end: re-read the last chunk
+#pragma unroll
+        for (int i = 0; i < kInst; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(src[i] + c * 32),
+                                             (__attribute__((address_space(3))) void*)(ring + slot * kStage + i * 512),
+                                             16, 0, 0);
+    };
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < kNsw; ++s) issue(s, s);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(kNsw * kInst, 15));   // the item metadata only
+    __builtin_amdgcn_sched_barrier(0);
+
+    f32x4 acc[MT][NT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int j = 0; j < n_local; ++j) {
+        const int slot = j % kNsw;
+        // stage j landed (kNsw - 1 younger stages may stay in flight: one is issued per trip)
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm((kNsw - 1) * kInst, 15));
+        const uint16_t* st = ring + slot * kStage;
+        bf16x8 xf[MT], wf[NT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const int r = m * 16 + ln;
+            xf[m] = *(const bf16x8*)(st + r * 32 + ((g ^ gemm_swz(r)) & 3) * 8);
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int r = MT * 16 + t * 16 + ln;
+            wf[t] = *(const bf16x8*)(st + r * 32 + ((g ^ gemm_swz(r)) & 3) * 8);
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[m], wf[t], acc[m][t], 0, 0, 0);
+        // the slot's fragment reads have returned before its next copy lands
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+        __builtin_amdgcn_sched_barrier(0);
+        issue(slot, j + kNsw);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));        // drain the re-read stages
+    __syncthreads();
+
+    // ---- epilogue: per-wave fp32 partials [row][2 PP] in LDS, summed, rotated, stored ----
+    float* Cs = reinterpret_cast<float*>(smem);
+    constexpr int kLdc = C::kLdc, kRowsPad = MT * 16;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                Cs[(wave * kRowsPad + m * 16 + g * 4 + e) * kLdc + t * 16 + ln] = acc[m][t][e];
+    // rotation frequency of each pair: one pow per pair, in parallel
+    double* s_theta = reinterpret_cast<double*>(Cs + 4 * kRowsPad * kLdc);
+    if (tid < kPP) {
+        const int p = min(p0 + tid, n_pairs - 1);
+        s_theta[tid] = pow((double)a.rope_base, -2.0 * (p % half) / D);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+        const int idx = tid + 256 * k;
+        const int r = idx / kPieces, q = idx % kPieces;
+        const int p = p0 + q * 8;
+        if (r >= a.R || p >= n_pairs) continue;
+        float lo[8], hi[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float sl = 0.f, sh = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                sl += Cs[(w * kRowsPad + r) * kLdc + q * 8 + e];
+                sh += Cs[(w * kRowsPad + r) * kLdc + kPP + q * 8 + e];
+            }
+            lo[e] = sl;
+            hi[e] = sh;
+        }
+        const int hp = p / half, i0 = p % half;            // a piece never straddles a head (half % 8 == 0)
+        const int part = hp / H, head = hp % H;
+        uint16_t* dst;
+        if (part == 0) {
+            dst = a.q_out + (int64_t)r * a.n_out;
+        } else {
+            const int sl = it_slot[k];
+            if (sl < 0 || (int64_t)sl >= a.cache_rows) continue;
+            dst = (part == 1 ? a.k_cache : a.v_cache) + (int64_t)sl * a.n_out;
+        }
+        if (part < 2) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                double ang = (double)it_pos[k] * s_theta[q * 8 + e];
+                ang -= rint(ang * (1.0 / kTwoPi)) * kTwoPi;
+                // hardware sin/cos take revolutions; |rev| <= 1/2 after the fp64 reduction
+                const float rev = (float)(ang * (1.0 / kTwoPi));
+                const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
+                const float x0 = lo[e], x1 = hi[e];
+                lo[e] = x0 * cs - x1 * sn;
+                hi[e] = x1 * cs + x0 * sn;
+            }
+        }
+        u32x4 plo, phi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            plo[e] = pack_bf16x2(lo[2 * e], lo[2 * e + 1]);
+            phi[e] = pack_bf16x2(hi[2 * e], hi[2 * e + 1]);
+        }
+        *(u32x4*)(dst + head * D + i0) = plo;
+        *(u32x4*)(dst + head * D + i0 + half) = phi;
+    }
+}
+
 // fp32 path (parity-sized shapes): one thread per (row, Q/K/V part, head,
 // rotation pair) forms both columns of the pair, rotates and stores them.
 __global__ void qkv_f32_kernel(int R, int d_model, int n_heads, int head_dim, float rope_base,
@@ -634,10 +659,12 @@ struct QkvPlan {
     int bm, n_mtiles, n_ntiles, n_ktiles;
 };
 
-// Cache-phase row counts (R <= 128) take the weight-streaming kernel.  Row
+// Cache-phase row counts (R <= 128) take the weight-streaming kernel
+// (d_model a multiple of 128: four waves split the 32-wide K chunks).  Row
 // counts that give at least two 256 x 256 tiles per compute unit take the
 // large-tile kernel (head_dim 128, whole heads per wave); the rest take the
-// 128 x 128 LDS-tiled kernel.  None splits K, so no workspace is needed.
+// 128 x 128 LDS-tiled kernel.  None splits K across workgroups, so no
+// workspace is needed.
 // DLLM_QKV_KERNEL=tiled|gemm overrides the choice where the shape allows it.
 QkvPlan plan_bf16(int R, int d_model, int n_out, int head_dim) {
     QkvPlan p{};
@@ -672,6 +699,31 @@ int check_shape(dllm_dtype dt, int n_rows, int d_model, int n_heads, int head_di
         DLLM_CHECK_SUP(d_model % kBK == 0);
     }
     return DLLM_OK;
+}
+
+template <int MT, int NT>
+void launch_stream_t(dim3 grid, hipStream_t stream, const QkvArgs& a, int n_pairs) {
+    hipLaunchKernelGGL((qkv_stream_kernel<MT, NT>), grid, dim3(256), 0, stream, a, n_pairs);
+}
+
+template <int NT>
+void launch_stream_nt(int mt, dim3 grid, hipStream_t stream, const QkvArgs& a, int n_pairs) {
+    switch (mt) {
+        case 1: launch_stream_t<1, NT>(grid, stream, a, n_pairs); break;
+        case 2: launch_stream_t<2, NT>(grid, stream, a, n_pairs); break;
+        case 3: launch_stream_t<3, NT>(grid, stream, a, n_pairs); break;
+        case 4: launch_stream_t<4, NT>(grid, stream, a, n_pairs); break;
+        case 5: launch_stream_t<5, NT>(grid, stream, a, n_pairs); break;
+        case 6: launch_stream_t<6, NT>(grid, stream, a, n_pairs); break;
+        case 7: launch_stream_t<7, NT>(grid, stream, a, n_pairs); break;
+        default: launch_stream_t<8, NT>(grid, stream, a, n_pairs); break;
+    }
+}
+
+void launch_stream(int mt, int nt, dim3 grid, hipStream_t stream, const QkvArgs& a, int n_pairs) {
+    if (nt == 3) launch_stream_nt<3>(mt, grid, stream, a, n_pairs);
+    else if (nt == 2) launch_stream_nt<2>(mt, grid, stream, a, n_pairs);
+    else launch_stream_nt<1>(mt, grid, stream, a, n_pairs);
 }
 
 }  // namespace
@@ -731,17 +783,11 @@ extern "C" int dllm_qkv_rope_cachewrite(dllm_dtype dt, int n_rows, int d_model, 
         hipLaunchKernelGGL(qkv_gemm_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, a,
                            p.n_mtiles, p.n_ntiles);
     } else if (p.kind == kSkinny) {
-        dim3 grid(3 * n_out / 64);
-        switch ((n_rows + 15) / 16) {
-            case 1: hipLaunchKernelGGL((qkv_skinny_kernel<1, 8>), grid, dim3(256), 0, stream, a); break;
-            case 2: hipLaunchKernelGGL((qkv_skinny_kernel<2, 8>), grid, dim3(256), 0, stream, a); break;
-            case 3: hipLaunchKernelGGL((qkv_skinny_kernel<3, 6>), grid, dim3(256), 0, stream, a); break;
-            case 4: hipLaunchKernelGGL((qkv_skinny_kernel<4, 6>), grid, dim3(256), 0, stream, a); break;
-            case 5: hipLaunchKernelGGL((qkv_skinny_kernel<5, 6>), grid, dim3(256), 0, stream, a); break;
-            case 6: hipLaunchKernelGGL((qkv_skinny_kernel<6, 5>), grid, dim3(256), 0, stream, a); break;
-            case 7: hipLaunchKernelGGL((qkv_skinny_kernel<7, 5>), grid, dim3(256), 0, stream, a); break;
-            default: hipLaunchKernelGGL((qkv_skinny_kernel<8, 4>), grid, dim3(256), 0, stream, a); break;
-        }
+        // pairs per workgroup: the most (up to 24) that still leaves >= 256 workgroups
+        const int n_pairs = 3 * n_out / 2;
+        const int nt = n_pairs >= 3 * 8 * kNumCu ? 3 : n_pairs >= 2 * 8 * kNumCu ? 2 : 1;
+        const dim3 grid((n_pairs + 8 * nt - 1) / (8 * nt));
+        launch_stream((n_rows + 15) / 16, nt, grid, stream, a, n_pairs);
     } else {
         dim3 grid(p.n_ntiles, p.n_mtiles, 1);
         if (p.bm == 64)
