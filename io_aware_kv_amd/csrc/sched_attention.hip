@@ -39,7 +39,6 @@ using namespace dllm;
 constexpr int kQT = 128;             // query rows per item
 constexpr int kKT = 64;              // keys per tile
 constexpr int kHD = 128;             // head dim of the bf16 kernel
-constexpr int kThreads = 512;        // 8 waves x 16 rows
 constexpr int kLDK = kHD + 8;        // K tile row stride, halfwords (272 B)
 constexpr int kLDV = kKT + 8;        // V^T tile row stride, halfwords (144 B)
 constexpr int kMaxSeq = 1024;
@@ -128,21 +127,89 @@ __device__ __forceinline__ s16x4 ds_read_tr(const uint16_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
 }
 
-constexpr int kRing = 4;            // register ring of K/V tiles (3 in flight)
+// K/V (and the query tile, and mask words) reach LDS through direct-to-LDS
+// copies, kNS key tiles deep.  A copy writes lane i's bytes at base + size*i,
+// so K and V rows (256 B: one key, one head) are stored with their 16-byte
+// slots permuted by an XOR swizzle applied on the source side.  swz_k keeps
+// the 16 keys a K-fragment read touches in 16 distinct bank groups; swz_v
+// keeps the 8 keys x 32 bytes of a 32-lane V transpose read in 16 distinct
+// bank groups.
+//
+// The copies are issued from inline assembly.  A copy the compiler can see
+// makes it wait for every copy in flight before any LDS read it cannot prove
+// disjoint, and it cannot for the transpose read; the ring's ordering is
+// instead explicit: each step waits for its own stage with s_waitcnt and
+// publishes it with a barrier, and the assembly's memory clobber keeps LDS
+// reads from moving across a copy.
+constexpr int kNS = 2;                  // ring stages (two workgroups share a compute unit)
+constexpr int kTileH = kKT * kHD;       // halfwords of one K (or V) tile: 16 KiB
+constexpr int kDmaPerWave = 8;          // 1 KiB copies per wave per stage (16 for K, 16 for V)
+constexpr int kAttnThreads = 256;       // 4 waves
+constexpr int kMaskStageBytes = 2048;   // up to 256 rows x 2 mask words per stage
+constexpr int kStageBytes = 2 * kTileH * 2 + kMaskStageBytes;
+constexpr int kRingBytes = kNS * kStageBytes;
 
-__global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sK[2][kKT * kLDK];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[2][kKT * kLDK];
-    __shared__ int s_pref[kMaxSeq + 1];
-    __shared__ int s_pages[kMaxPages];
-    __shared__ float s_col[8][kKT];
-    __shared__ uint8_t s_tile_full[kMaxPages / 4];   // tile fully in range with valid pages
-    __shared__ int s_total;
+__device__ __forceinline__ int swz_k(int key) { return (key + 4 * (key >> 4)) & 15; }
+__device__ __forceinline__ int swz_v(int key) { return 2 * ((key & 3) + 4 * ((key >> 3) & 1)); }
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// s_waitcnt immediate: vector-memory count vm, LDS/scalar count lgkm, no wait
+// on the export counter
+__device__ __forceinline__ constexpr int waitcnt_imm(int vm, int lgkm) {
+    return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// 16 bytes per lane from gptr to LDS byte address base + 16 * lane (base wave-uniform)
+__device__ __forceinline__ void copy16_to_lds(const void* gptr, uint32_t base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(gptr), "s"(base) : "memory", "m0");
+}
+// 4 bytes per lane from gptr to LDS byte address base + 4 * lane
+__device__ __forceinline__ void copy4_to_lds(const void* gptr, uint32_t base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :: "v"(gptr), "s"(base) : "memory", "m0");
+}
+
+// Workgroup barrier that orders LDS only: the fences wait for this wave's
+// LDS operations, not for its global loads in flight (a plain __syncthreads
+// would drain those too).
+__device__ __forceinline__ void lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// One workgroup per (sequence, head, QT-row query tile, key split); wave w
+// owns query rows 16 RT w .. 16 RT w + 16 RT - 1 (RT row tiles of 16), so the
+// K and V fragments a wave reads from LDS serve RT row tiles.
+template <int RT, bool HAS_MASK>
+__global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) {
+    constexpr int QT = 64 * RT;
+    constexpr int kMaskPerWave = HAS_MASK ? QT * 2 / 64 / 4 : 0;      // 4-byte copies per wave per stage
+    constexpr int kPerStage = kDmaPerWave + kMaskPerWave;              // copies per wave per stage
+    constexpr int kQSlots = RT / 2;                                     // ring stages the query tile borrows
+    constexpr int kQPerWave = QT / 4 / 4;                               // query-tile copies per wave
+    static_assert(QT * 8 <= kMaskStageBytes && kQPerWave * 4 * 4 * 256 <= kQSlots * kStageBytes, "layout");
+    static_assert((kNS - 1) * kPerStage + kQPerWave < 64, "wait counts");
+    static_assert(kRingBytes >= (kMaxSeq + 1) * 4, "the schedule scan borrows the ring");
+    // one LDS allocation: the ring (which the schedule scan borrows first), then the page tables
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kRingBytes + (kMaxPages + 4 * kKT + 1) * 4 + kMaxPages / 4];
+    int* s_pref = reinterpret_cast<int*>(lds);                                    // [kMaxSeq + 1], scheduling only
+    int* s_pages = reinterpret_cast<int*>(lds + kRingBytes);                      // [kMaxPages]
+    float (*s_col)[kKT] = reinterpret_cast<float (*)[kKT]>(s_pages + kMaxPages);   // [4][kKT]
+    int* s_total = reinterpret_cast<int*>(&s_col[4][0]);
+    uint8_t* s_tile_full = reinterpret_cast<uint8_t*>(s_total + 1);               // [kMaxPages / 4]
+    auto k_tile = [&](int sl) { return reinterpret_cast<uint16_t*>(lds + sl * kStageBytes); };
+    auto v_tile = [&](int sl) { return reinterpret_cast<uint16_t*>(lds + sl * kStageBytes) + kTileH; };
+    auto m_words = [&](int sl) { return reinterpret_cast<uint32_t*>(lds + sl * kStageBytes + 4 * kTileH); };
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, ln = lane & 15;
 
-    // ---- schedule: per-sequence item counts (query tiles x heads), prefix-summed by wave 0 ----
+    // ---- schedule: per-sequence item counts (query tiles x heads x splits), prefix-summed by wave 0 ----
     if (wave == 0) {
         int base = 0;
         for (int c = 0; c < a.n_seq; c += 64) {
@@ -150,7 +217,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnArgs a) {
             int items = 0;
             if (b < a.n_seq) {
                 SeqInfo s = seq_info(a, b);
-                items = s.nqt * a.H * a.splits;
+                items = (s.rows + QT - 1) / QT * a.H * a.splits;
             }
             int scan = items;
 #pragma unroll
@@ -163,13 +230,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnArgs a) {
         }
         if (lane == 0) {
             s_pref[0] = 0;
-            s_total = base;
+            *s_total = base;
         }
     }
     __syncthreads();
     // a malformed cu_q (not non-decreasing) can claim more items than were
     // launched: then nothing runs (outputs unspecified, nothing out of bounds)
-    const int total = s_total;
+    const int total = *s_total;
     if (total > (int)gridDim.x || (int)blockIdx.x >= total) return;
     const int item = xcd_remap(blockIdx.x, total);
     int lo = 0, hi = a.n_seq - 1;                       // last b with s_pref[b] <= item
@@ -179,336 +246,426 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnArgs a) {
     }
     const int b = lo;
     const SeqInfo si = seq_info(a, b);
+    const int nqt = (si.rows + QT - 1) / QT;
     const int local = item - s_pref[b];
-    const int qt = local % si.nqt;                      // consecutive items: next query tile, same head
-    const int hs = local / si.nqt;
+    const int qt = local % nqt;                         // consecutive items: next query tile, same head
+    const int hs = local / nqt;
     const int sp = hs % a.splits;                       // key split
     const int h = hs / a.splits;
     const int seq_r0 = max(0, min(a.cu_q[b], a.n_rows));
-    const int r0 = seq_r0 + qt * kQT;
-    const int nr = min(kQT, si.rows - qt * kQT);
+    const int r0 = seq_r0 + qt * QT;
+    const int nr = min(QT, si.rows - qt * QT);
     const int ntiles = (si.kv + kKT - 1) / kKT;
     const int tiles_per = (ntiles + a.splits - 1) / a.splits;
     const int t_begin = min(sp * tiles_per, ntiles);    // this item's key tiles
     const int t_end = min(t_begin + tiles_per, ntiles);
     const int npages = (si.kv + 15) / 16;
-    for (int j = tid; j < npages; j += kThreads) {
+    for (int j = tid; j < npages; j += kAttnThreads) {
         int p = a.page_table[(int64_t)b * a.max_pages + j];
         s_pages[j] = (p >= 0 && p < a.pool_pages) ? p : -1;
     }
     __syncthreads();
-    for (int t = tid; t < kMaxPages / 4; t += kThreads) {     // every slot: padded tiles read theirs
+    for (int t = tid; t < kMaxPages / 4; t += kAttnThreads) {
         bool full = t < ntiles && (t + 1) * kKT <= si.kv;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) full = full && s_pages[min(t * 4 + q, npages - 1)] >= 0;
+        for (int q = 0; q < 4; ++q) full = full && s_pages[min(t * 4 + q, max(npages - 1, 0))] >= 0;
         s_tile_full[t] = full ? 1 : 0;
     }
     __syncthreads();
 
-    // ---- query fragments (B operand of S^T = K Q^T) ----
-    // Every global load below is unconditional (indices clamped to valid
-    // memory, the value selected afterwards): a load under a divergent branch
-    // makes the compiler wait for all outstanding loads, which would drain the
-    // prefetch ring.
-    const int wrow = wave * 16;
-    const bool active = wrow < nr;
-    const int my_row = wrow + ln;
-    const bool row_ok = my_row < nr;
-    const int q_row = r0 + min(my_row, nr - 1);
-    bf16x8 qf[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        u32x4 v = *(const u32x4*)(a.q + (int64_t)q_row * a.n_out + h * kHD + ks * 32 + g * 8);
-        u32x4 z = {0u, 0u, 0u, 0u};
-        qf[ks] = __builtin_bit_cast(bf16x8, row_ok ? v : z);
-    }
-    const bool has_mask = a.mask != nullptr;
-    const int64_t mwords = (si.kv + 31) / 32;
-    const int64_t mrow_base = has_mask ? a.mask_off[b] + (int64_t)(qt * kQT + min(my_row, nr - 1)) * mwords : 0;
     const int last_page = max(npages - 1, 0);
-
-    // ---- K/V tile pipeline: 64 keys x 128 d, 16 B per thread per pass ----
-    // A prefetched value is never touched before its consumer (a select right
-    // after a load would make the compiler wait for it).  Keys past kv_len, or
-    // on a bad page, read the sequence's key 0 instead (a row the step reads
-    // anyway); the visibility bits give them probability exactly 0.
+    // keys past kv_len, on a bad page, or of a padded step read the sequence's
+    // key 0 (a row the step reads anyway); the visibility bits zero them
     const int key0_page = npages > 0 ? s_pages[0] : -1;
     const int64_t safe_row = key0_page >= 0 ? (int64_t)key0_page * 16 : 0;
-    u32x4 rk[kRing][2], rv[kRing][2];
-    uint32_t rmw[kRing][2];              // this lane's mask words for the tile (raw)
-    auto gload = [&](auto S, int t, bool with_v) __attribute__((always_inline)) {
-        constexpr int sl = decltype(S)::value;
-        {   // unconditional: tiles past the end load the safe row and are fully masked
+    const int64_t mwords = (si.kv + 31) / 32;
+    const int64_t mask_row0 = HAS_MASK ? a.mask_off[b] + (int64_t)(qt * QT) * mwords : 0;
+
+    // ---- copies: K groups (waves 0, 1) or V groups (waves 2, 3) of 4 keys; mask words; query tile ----
+    const bool is_v = wave >= 2;
+    const uint16_t* kv_src = (is_v ? a.v : a.k) + h * kHD;
+    int lslot[kDmaPerWave];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                int c = tid + i * kThreads;
-                int key = c >> 4, dc = c & 15;
-                int kg = t * kKT + key;
-                int page = s_pages[min(kg >> 4, last_page)];
-                bool ok = (t < t_end) & (kg < si.kv) & (page >= 0);
-                int64_t row = ok ? (int64_t)page * 16 + (kg & 15) : safe_row;
-                int64_t off = row * a.n_out + h * kHD + dc * 8;
-                rk[sl][i] = *(const u32x4*)(a.k + off);
-                if (with_v) rv[sl][i] = *(const u32x4*)(a.v + off);
-            }
-            if (has_mask) {
-                int64_t i0 = mrow_base + t * (kKT / 32);
-                rmw[sl][0] = a.mask[min(max(i0, (int64_t)0), a.mask_words - 1)];
-                rmw[sl][1] = a.mask[min(max(i0 + 1, (int64_t)0), a.mask_words - 1)];
-            }
+    for (int i = 0; i < kDmaPerWave; ++i) {
+        const int kk = 4 * ((wave & 1) * kDmaPerWave + i) + (lane >> 4);
+        lslot[i] = (lane & 15) ^ (is_v ? swz_v(kk) : swz_k(kk));
+    }
+    auto issue = [&](int sl, int t) __attribute__((always_inline)) {
+        const uint32_t dst = lds_addr(is_v ? v_tile(sl) : k_tile(sl));
+#pragma unroll
+        for (int i = 0; i < kDmaPerWave; ++i) {
+            const int q = (wave & 1) * kDmaPerWave + i;            // 4-key group of the tile
+            const int kg = t * kKT + 4 * q + (lane >> 4);
+            const int page = s_pages[min(kg >> 4, last_page)];
+            const bool ok = (t < t_end) & (kg < si.kv) & (page >= 0);
+            const int64_t row = ok ? (int64_t)page * 16 + (kg & 15) : safe_row;
+            copy16_to_lds(kv_src + row * a.n_out + lslot[i] * 8, __builtin_amdgcn_readfirstlane(dst + q * 1024));
         }
-    };
-    // mask word validity of tile t for this lane (applied where the words are used)
-    auto mask_words_of = [&](auto S, int t, uint32_t& w0, uint32_t& w1) __attribute__((always_inline)) {
-        constexpr int sl = decltype(S)::value;
-        if (!has_mask) {
-            w0 = w1 = 0xffffffffu;
-            return;
-        }
-        int64_t i0 = mrow_base + t * (kKT / 32);
-        w0 = (row_ok && i0 >= 0 && i0 < a.mask_words) ? rmw[sl][0] : 0u;
-        w1 = (row_ok && i0 + 1 >= 0 && i0 + 1 < a.mask_words) ? rmw[sl][1] : 0u;
-    };
-    auto lstore = [&](auto S, int buf, bool with_v) __attribute__((always_inline)) {
-        constexpr int sl = decltype(S)::value;
+        if constexpr (HAS_MASK) {
+            // words 2t, 2t+1 of every query row of the tile: [row][2]
+            const uint32_t mdst = lds_addr(m_words(sl));
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            int c = tid + i * kThreads;
-            int key = c >> 4, dc = c & 15;
-            *(u32x4*)(&sK[buf][key * kLDK + dc * 8]) = rk[sl][i];
-            if (with_v) *(u32x4*)(&sV[buf][key * kLDK + dc * 8]) = rv[sl][i];
-        }
-    };
-    auto scores = [&](int buf, f32x4 (&st)[4]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const uint16_t* krow = &sK[buf][perm_key(t, ln) * kLDK + g * 8];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                bf16x8 kf = *(const bf16x8*)(krow + ks * 32);
-                st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], st[t], 0, 0, 0);
+            for (int i = 0; i < kMaskPerWave; ++i) {
+                const int m = wave * kMaskPerWave + i;
+                const int idx = m * 64 + lane;
+                const int row = min(idx >> 1, max(nr - 1, 0));
+                int64_t wi = mask_row0 + (int64_t)row * mwords + 2 * (int64_t)t + (idx & 1);
+                wi = min(max(wi, (int64_t)0), a.mask_words - 1);
+                copy4_to_lds(a.mask + wi, __builtin_amdgcn_readfirstlane(mdst + m * 256));
             }
         }
     };
-    // visibility of this lane's 16 scores in tile t (mask words come from the ring slot)
-    auto vis_bits = [&](int kbase, uint32_t w0, uint32_t w1) __attribute__((always_inline)) -> uint32_t {
+
+    // query tile: rows r0 .. r0 + QT - 1 (clamped) into the last kQSlots stages, 4 rows per copy
+    {
+        const uint32_t qdst = lds_addr(k_tile(kNS - kQSlots));
+#pragma unroll
+        for (int i = 0; i < kQPerWave; ++i) {
+            const int c = wave * kQPerWave + i;
+            const int row = 4 * c + (lane >> 4);
+            const int qrow = r0 + min(row, nr - 1);
+            const int sl16 = (lane & 15) ^ swz_k(row);
+            copy16_to_lds(a.q + (int64_t)qrow * a.n_out + h * kHD + sl16 * 8,
+                          __builtin_amdgcn_readfirstlane(qdst + c * 1024));
+        }
+    }
+    for (int s = 0; s < kNS - kQSlots; ++s) issue(s, t_begin + s);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm((kNS - kQSlots) * kPerStage, 15));   // the query tile
+    lds_sync();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- query fragments (B operand of S^T = K Q^T), rows of this wave ----
+    const int wrow = wave * 16 * RT;
+    bool rt_active[RT], row_ok[RT];
+    bf16x8 qf[RT][4];
+    {
+        const uint16_t* qt_lds = k_tile(kNS - kQSlots);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int row = wrow + rt * 16 + ln;
+            rt_active[rt] = wrow + rt * 16 < nr;
+            row_ok[rt] = row < nr;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                qf[rt][ks] = *(const bf16x8*)(qt_lds + row * kHD + (((ks * 4 + g) ^ swz_k(row)) * 8));
+        }
+    }
+    lds_sync();                                         // every wave holds its query rows: the slots are free
+    __builtin_amdgcn_sched_barrier(0);
+    for (int s = kNS - kQSlots; s < kNS - 1; ++s) issue(s, t_begin + s);
+
+    // ---- per-tile math ----
+    // visibility of this lane's 16 scores in tile t (row validity and mask applied)
+    auto vis_bits = [&](int t, bool rok, uint32_t w0, uint32_t w1) __attribute__((always_inline)) -> uint32_t {
         uint32_t bits = 0;
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                int kk = reg_key(t, g, e);
-                int kg = kbase + kk;
-                uint32_t w = (kk < 32) ? w0 : w1;
-                bool ok = (kg < si.kv) & (s_pages[min(kg >> 4, last_page)] >= 0) & (((w >> (kk & 31)) & 1u) != 0);
-                bits |= (ok ? 1u : 0u) << (t * 4 + e);
-            }
-        return bits;
-    };
-
-    float m_run = kNegBig, l_run = 0.f;
-    f32x4 acc[8];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    auto attend = [&](int buf, int t, uint32_t w0, uint32_t w1) __attribute__((always_inline)) {
         const int kbase = t * kKT;
-        f32x4 st[4];
-        scores(buf, st);
-        // raw scores; the scale is folded into the exponent (c > 0 keeps the order)
-        const bool full = !has_mask && s_tile_full[t];
-        if (!full) {
-            const uint32_t vis = vis_bits(kbase, w0, w1);
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    st[tt][e] = ((vis >> (tt * 4 + e)) & 1u) ? st[tt][e] : -INFINITY;
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) mx = fmaxf(mx, st[tt][e]);
-        mx = wave_max16(mx);
-        const float m_new = fmaxf(m_run, mx * a.scale_log2);
-        float rs = 0.f;
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
+        for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                float p = __builtin_amdgcn_exp2f(fmaf(st[tt][e], a.scale_log2, -m_new));
-                st[tt][e] = p;
-                rs += p;
+                const int kk = reg_key(t4, g, e);
+                const int kg = kbase + kk;
+                const uint32_t w = (kk < 32) ? w0 : w1;
+                const bool ok = (kg < si.kv) & (s_pages[min(kg >> 4, last_page)] >= 0) &
+                                (((w >> (kk & 31)) & 1u) != 0);
+                bits |= (ok ? 1u : 0u) << (t4 * 4 + e);
             }
-        rs = wave_sum16(rs);
-        if (m_new != m_run) {                  // a row maximum moved: rescale that row
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            l_run *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
-        }
-        l_run += rs;
-        m_run = m_new;
-        bf16x8 pf[2];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            u32x4 u;
-            u[0] = pack_bf16x2(st[2 * c][0], st[2 * c][1]);
-            u[1] = pack_bf16x2(st[2 * c][2], st[2 * c][3]);
-            u[2] = pack_bf16x2(st[2 * c + 1][0], st[2 * c + 1][1]);
-            u[3] = pack_bf16x2(st[2 * c + 1][2], st[2 * c + 1][3]);
-            pf[c] = __builtin_bit_cast(bf16x8, u);
-        }
-        // V^T fragments: source lane ln of group g points at key c*32 + 8g + 4*hf + (ln >> 2),
-        // column dt*16 + 4*(ln & 3)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const uint16_t* vbase = &sV[buf][(c * 32 + 8 * g + (ln >> 2)) * kLDK + 4 * (ln & 3)];
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                s16x4 lo4 = ds_read_tr(vbase + dt * 16);
-                s16x4 hi4 = ds_read_tr(vbase + 4 * kLDK + dt * 16);
-                typedef short s16x8 __attribute__((ext_vector_type(8)));
-                s16x8 v8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-                bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
-                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[c], acc[dt], 0, 0, 0);
-            }
+        return rok ? bits : 0u;
+    };
+    // mask words of query row `row` (tile-relative) for tile t, from the stage's copy
+    auto mask_pair = [&](int sl, int row, int t, uint32_t& w0, uint32_t& w1) __attribute__((always_inline)) {
+        if constexpr (!HAS_MASK) {
+            w0 = w1 = 0xffffffffu;
+        } else {
+            const uint32_t* mw = m_words(sl);
+            const int64_t i0 = mask_row0 + (int64_t)min(row, max(nr - 1, 0)) * mwords + 2 * (int64_t)t;
+            w0 = (i0 >= 0 && i0 < a.mask_words) ? mw[2 * row] : 0u;
+            w1 = (i0 + 1 >= 0 && i0 + 1 < a.mask_words) ? mw[2 * row + 1] : 0u;
         }
     };
 
-    // ---- main pass: this item's key tiles, 3 tiles in flight ----
-    gload(Ic<0>{}, t_begin, true);
-    __builtin_amdgcn_sched_barrier(0);
-    gload(Ic<1>{}, t_begin + 1, true);
-    __builtin_amdgcn_sched_barrier(0);
-    gload(Ic<2>{}, t_begin + 2, true);
-    __builtin_amdgcn_sched_barrier(0);
-    lstore(Ic<0>{}, 0, true);
-    __syncthreads();
-    // step i handles tile t_begin + i; ring slot and LDS buffer follow i
-    auto step_main = [&](auto S, int i) __attribute__((always_inline)) {
-        constexpr int sl = decltype(S)::value;            // i % kRing
-        const int t = t_begin + i;
-        uint32_t w0, w1;
-        mask_words_of(S, t, w0, w1);
-        gload(Ic<(sl + 3) % kRing>{}, t + 3, true);
-        __builtin_amdgcn_sched_barrier(0);      // keep the prefetch where it is issued
-        if (active && t < t_end) attend(i & 1, t, w0, w1);
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        lstore(Ic<(sl + 1) % kRing>{}, (i + 1) & 1, true);
-        __syncthreads();
-    };
-    // the trip count is padded to whole rings so that no load sits under a
-    // branch (the padded steps only load and stage)
-    const int n_main = (t_end - t_begin + kRing - 1) / kRing * kRing;
-    for (int i = 0; i < n_main; i += kRing) {
-        step_main(Ic<0>{}, i);
-        step_main(Ic<1>{}, i + 1);
-        step_main(Ic<2>{}, i + 2);
-        step_main(Ic<3>{}, i + 3);
+    float m_run[RT], l_run[RT];
+    f32x4 acc[RT][8];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        m_run[rt] = kNegBig;
+        l_run[rt] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) acc[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
+    // S^T for the active row tiles (K fragments shared across them)
+    auto scores = [&](const uint16_t* kt_lds, f32x4 (&st)[RT][4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+            const int key = perm_key(t4, ln);
+            bf16x8 kf[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                kf[ks] = *(const bf16x8*)(kt_lds + key * kHD + (((ks * 4 + g) ^ swz_k(key)) * 8));
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                st[rt][t4] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (!rt_active[rt]) continue;             // uniform per wave
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    st[rt][t4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[rt][ks], st[rt][t4], 0, 0, 0);
+            }
+        }
+    };
+
+    auto attend = [&](int sl, int t) __attribute__((always_inline)) {
+        f32x4 st[RT][4];
+        scores(k_tile(sl), st);
+        const bool full = !HAS_MASK && s_tile_full[t];
+        bf16x8 pf[RT][2];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            if (!rt_active[rt]) continue;
+            // raw scores; the scale is folded into the exponent (c > 0 keeps the order)
+            if (!full) {
+                uint32_t w0, w1;
+                mask_pair(sl, wrow + rt * 16 + ln, t, w0, w1);
+                const uint32_t vis = vis_bits(t, row_ok[rt], w0, w1);
+#pragma unroll
+                for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        st[rt][t4][e] = ((vis >> (t4 * 4 + e)) & 1u) ? st[rt][t4][e] : -INFINITY;
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mx = fmaxf(mx, st[rt][t4][e]);
+            mx = wave_max16(mx);
+            const float m_new = fmaxf(m_run[rt], mx * a.scale_log2);
+            float rs = 0.f;
+#pragma unroll
+            for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(st[rt][t4][e], a.scale_log2, -m_new));
+                    st[rt][t4][e] = p;
+                    rs += p;
+                }
+            rs = wave_sum16(rs);
+            if (m_new != m_run[rt]) {                     // a row maximum moved: rescale that row
+                const float alpha = __builtin_amdgcn_exp2f(m_run[rt] - m_new);
+                l_run[rt] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) acc[rt][dt] *= alpha;
+            }
+            l_run[rt] += rs;
+            m_run[rt] = m_new;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                u32x4 u;
+                u[0] = pack_bf16x2(st[rt][2 * c][0], st[rt][2 * c][1]);
+                u[1] = pack_bf16x2(st[rt][2 * c][2], st[rt][2 * c][3]);
+                u[2] = pack_bf16x2(st[rt][2 * c + 1][0], st[rt][2 * c + 1][1]);
+                u[3] = pack_bf16x2(st[rt][2 * c + 1][2], st[rt][2 * c + 1][3]);
+                pf[rt][c] = __builtin_bit_cast(bf16x8, u);
+            }
+        }
+        // O^T += V^T P^T.  V^T fragments: source lane ln of group g points at key
+        // c*32 + 8g + 4*hf + (ln >> 2), column dt*16 + 4*(ln & 3)
+        const uint16_t* vt_lds = v_tile(sl);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            bf16x8 vf[8];
+            {
+                // keys c*32 + 8g + (ln >> 2) (lo) and 4 further (hi); one 8-element
+                // initializer per fragment (element-wise insertion is mis-lowered)
+                const int key = c * 32 + 8 * g + (ln >> 2);
+                const uint16_t* vlo = vt_lds + key * kHD + 4 * (ln & 1);
+                const uint16_t* vhi = vlo + 4 * kHD;
+                const int sw = swz_v(key);               // equal for key and key + 4
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) {
+                    const int lsl = 2 * dt + ((ln & 3) >> 1);
+                    const s16x4 lo4 = ds_read_tr(vlo + ((lsl ^ sw) * 8));
+                    const s16x4 hi4 = ds_read_tr(vhi + ((lsl ^ sw) * 8));
+                    typedef short s16x8 __attribute__((ext_vector_type(8)));
+                    const s16x8 v8 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+                    vf[dt] = __builtin_bit_cast(bf16x8, v8);
+                }
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                if (!rt_active[rt]) continue;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt)
+                    acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf[rt][c], acc[rt][dt], 0, 0, 0);
+            }
+        }
+    };
+
+    // ---- main pass: this item's key tiles through the ring ----
+    // Every step issues one stage (past t_end: the safe row, fully masked), so
+    // "stage i has landed" is always the same wait count; an LDS-only barrier
+    // then publishes it (__syncthreads would also wait for the younger stages).
+    const int n_main = t_end - t_begin;
+    for (int i = 0; i < n_main; ++i) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm((kNS - 2) * kPerStage, 15));
+        lds_sync();
+        __builtin_amdgcn_sched_barrier(0);
+        issue((i + kNS - 1) % kNS, t_begin + i + kNS - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        attend(i % kNS, t_begin + i);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));      // drain the stages past the end
+    __syncthreads();
+
     if (a.splits > 1) {
-        // split mode: publish the unnormalised partial; attn_finish_kernel
+        // split mode (QT == kQT): publish the unnormalised partial; attn_finish_kernel
         // merges the splits and forms the column mass
-        if (active) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            if (!rt_active[rt]) continue;
+            const int my_row = wrow + rt * 16 + ln;
             float* po = a.part_o + (int64_t)item * kQT * kHD + my_row * kHD + g * 4;
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) *(f32x4*)(po + dt * 16) = acc[dt];
+            for (int dt = 0; dt < 8; ++dt) *(f32x4*)(po + dt * 16) = acc[rt][dt];
             if (g == 0) {
-                a.part_ml[((int64_t)item * kQT + my_row) * 2] = m_run;
-                a.part_ml[((int64_t)item * kQT + my_row) * 2 + 1] = l_run;
+                a.part_ml[((int64_t)item * kQT + my_row) * 2] = m_run[rt];
+                a.part_ml[((int64_t)item * kQT + my_row) * 2 + 1] = l_run[rt];
             }
         }
         return;
     }
 
     // ---- output ----
-    if (row_ok) {
-        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        if (!row_ok[rt]) continue;
+        const int my_row = wrow + rt * 16 + ln;
+        const float inv = l_run[rt] > 0.f ? 1.f / l_run[rt] : 0.f;
         uint16_t* orow = a.o + (int64_t)(r0 + my_row) * a.n_out + h * kHD + g * 4;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
             uint2 u;
-            u.x = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
-            u.y = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
+            u.x = pack_bf16x2(acc[rt][dt][0] * inv, acc[rt][dt][1] * inv);
+            u.y = pack_bf16x2(acc[rt][dt][2] * inv, acc[rt][dt][3] * inv);
             *(uint2*)(orow + dt * 16) = u;
         }
     }
 
     // ---- formula (2): this head's column mass from the masked-window rows ----
+    // The window rows' log-sum-exp is final only now, so their scores are
+    // recomputed in a second pass over the keys (K only, staged through
+    // registers with ordinary loads; nothing is in flight to LDS any more).
     if (qt != 0 || a.mass_accum == nullptr || a.mass_count == nullptr) return;
     int mb = a.mass_count[b];
     mb = max(0, min(mb, min(a.max_mass, min(si.rows, kQT))));
     if (mb == 0 || si.kv == 0) return;
-    const int mass_waves = (mb + 15) / 16;
-    const bool mwave = wave < mass_waves;
-    const bool mrow = my_row < mb;
-    const float inv_l = (mrow && l_run > 0.f) ? 1.f / l_run : 0.f;
     const float norm = 1.f / ((float)a.H * (float)mb);
     float* macc = a.mass_accum + ((int64_t)b * a.H + h) * a.n_cap;
-    gload(Ic<0>{}, 0, false);
-    __builtin_amdgcn_sched_barrier(0);
-    gload(Ic<1>{}, 1, false);
-    __builtin_amdgcn_sched_barrier(0);
-    gload(Ic<2>{}, 2, false);
-    __builtin_amdgcn_sched_barrier(0);
-    lstore(Ic<0>{}, 0, false);
-    __syncthreads();
-    // column sums of this head accumulate in LDS (the V tiles are free now);
-    // the running score is read, updated and written once at the end
-    float* s_mass = reinterpret_cast<float*>(&sV[0][0]);
-    const int kmax = min(si.kv, a.n_cap);
-    constexpr int kMassLds = (int)(sizeof(sV) / sizeof(float));
-    for (int i = tid; i < kMassLds; i += kThreads) s_mass[i] = 0.f;
-    __syncthreads();
-    auto step_mass = [&](auto S, int t) __attribute__((always_inline)) {
-        constexpr int sl = decltype(S)::value;
-        const int buf = t & 1;
-        const int kbase = t * kKT;
-        uint32_t w0, w1;
-        mask_words_of(S, t, w0, w1);
-        gload(Ic<(sl + 3) % kRing>{}, t + 3, false);
-        __builtin_amdgcn_sched_barrier(0);
-        if (mwave) {
-            f32x4 st[4];
-            scores(buf, st);
-            const bool full = !has_mask && s_tile_full[t];
-            const uint32_t vis = full ? 0xffffu : vis_bits(kbase, w0, w1);
+    bool mrt[RT];
+    float inv_l[RT];
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    bool ok = mrow && ((vis >> (tt * 4 + e)) & 1u);
-                    float p = __builtin_amdgcn_exp2f(fmaf(st[tt][e], a.scale_log2, -m_run)) * inv_l;
-                    p = row16_sum(ok ? p : 0.f);
-                    if (ln == 0) s_col[wave][reg_key(tt, g, e)] = p;
-                }
-        }
-        __syncthreads();
-        if (tid < kKT) {
-            float sum = 0.f;
-            for (int w = 0; w < mass_waves; ++w) sum += s_col[w][tid];
-            const int kg = kbase + tid;
-            if (kg < kMassLds) s_mass[kg] += sum;
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        lstore(Ic<(sl + 1) % kRing>{}, (t + 1) & 1, false);
-        __syncthreads();
-    };
-    const int ntiles_pad = (ntiles + kRing - 1) / kRing * kRing;
-    if (kmax <= kMassLds) {
-        for (int t = 0; t < ntiles_pad; t += kRing) {
-            step_mass(Ic<0>{}, t);
-            step_mass(Ic<1>{}, t + 1);
-            step_mass(Ic<2>{}, t + 2);
-            step_mass(Ic<3>{}, t + 3);
-        }
-        for (int i = tid; i < kmax; i += kThreads) macc[i] += s_mass[i] * norm;
+    for (int rt = 0; rt < RT; ++rt) {
+        mrt[rt] = wrow + rt * 16 < mb;
+        inv_l[rt] = (wrow + rt * 16 + ln < mb && l_run[rt] > 0.f) ? 1.f / l_run[rt] : 0.f;
     }
+    uint16_t* sKm = k_tile(0);                             // two staged K tiles (stage 0 area, 32 KiB)
+    float* s_mass = reinterpret_cast<float*>(lds + kStageBytes);
+    constexpr int kMassLds = (int)((kNS - 1) * kStageBytes / sizeof(float));
+    const int kmax = min(si.kv, a.n_cap);
+    if (kmax > kMassLds) return;                           // rejected by the host
+    for (int i = tid; i < kmax; i += kAttnThreads) s_mass[i] = 0.f;
+    // staging: thread c moves 16-byte slot c % 16 of key c / 16 (4 passes per tile)
+    constexpr int kMassRing = 3;
+    u32x4 rk[kMassRing][4];
+    auto mload = [&](auto S, int t) __attribute__((always_inline)) {
+        constexpr int sl = decltype(S)::value;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + i * kAttnThreads;
+            const int kg = t * kKT + (c >> 4);
+            const int page = s_pages[min(kg >> 4, last_page)];
+            const bool ok = (t < ntiles) & (kg < si.kv) & (page >= 0);
+            const int64_t row = ok ? (int64_t)page * 16 + (kg & 15) : safe_row;
+            rk[sl][i] = *(const u32x4*)(a.k + row * a.n_out + h * kHD + (c & 15) * 8);
+        }
+    };
+    auto mstore = [&](auto S, int buf) __attribute__((always_inline)) {
+        constexpr int sl = decltype(S)::value;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + i * kAttnThreads;
+            const int key = c >> 4;
+            *(u32x4*)(sKm + buf * kTileH + key * kHD + (((c & 15) ^ swz_k(key)) * 8)) = rk[sl][i];
+        }
+    };
+    auto mstep = [&](auto S, int t) __attribute__((always_inline)) {
+        constexpr int sl = decltype(S)::value;             // t % kMassRing
+        const int buf = t & 1;
+        mload(Ic<(sl + 2) % kMassRing>{}, t + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        if (t < ntiles) {
+            float cs[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) cs[j] = 0.f;
+            bool any = false;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) any = any || mrt[rt];
+            if (any) {
+                f32x4 st[RT][4];
+                scores(sKm + buf * kTileH, st);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    if (!mrt[rt]) continue;
+                    const int row = wrow + rt * 16 + ln;
+                    uint32_t w0 = 0xffffffffu, w1 = 0xffffffffu;
+                    if constexpr (HAS_MASK) {
+                        const int64_t i0 = mask_row0 + (int64_t)min(row, max(nr - 1, 0)) * mwords + 2 * (int64_t)t;
+                        w0 = (i0 >= 0 && i0 < a.mask_words) ? a.mask[i0] : 0u;
+                        w1 = (i0 + 1 >= 0 && i0 + 1 < a.mask_words) ? a.mask[i0 + 1] : 0u;
+                    }
+                    const uint32_t vis = vis_bits(t, row < mb, w0, w1);
+#pragma unroll
+                    for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float p = ((vis >> (t4 * 4 + e)) & 1u)
+                                ? __builtin_amdgcn_exp2f(fmaf(st[rt][t4][e], a.scale_log2, -m_run[rt])) * inv_l[rt]
+                                : 0.f;
+                            cs[t4 * 4 + e] += p;
+                        }
+                }
+            }
+            // column sums over this wave's window rows: the 16 lanes of a row
+            // group hold one key each per register; sum over the rows (lanes)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float v = row16_sum(cs[j]);
+                if (ln == 0) s_col[wave][reg_key(j >> 2, g, j & 3)] = v;
+            }
+        }
+        lds_sync();
+        if (t < ntiles && tid < kKT) {
+            const int kg = t * kKT + tid;
+            if (kg < kmax) s_mass[kg] += s_col[0][tid] + s_col[1][tid] + s_col[2][tid] + s_col[3][tid];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mstore(Ic<(sl + 1) % kMassRing>{}, (t + 1) & 1);
+        lds_sync();
+    };
+    mload(Ic<0>{}, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mload(Ic<1>{}, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_sync();                                       // s_mass zeroed
+    mstore(Ic<0>{}, 0);
+    lds_sync();
+    const int nm_pad = (ntiles + kMassRing - 1) / kMassRing * kMassRing;
+    for (int t = 0; t < nm_pad; t += kMassRing) {
+        mstep(Ic<0>{}, t);
+        mstep(Ic<1>{}, t + 1);
+        mstep(Ic<2>{}, t + 2);
+    }
+    for (int i = tid; i < kmax; i += kAttnThreads) macc[i] += s_mass[i] * norm;
 }
 
 // Split mode, second launch.  Items per sequence b: H * nqt merge items
@@ -627,16 +784,24 @@ __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
         s_lse[r] = l > 0.f ? m + __log2f(l) : INFINITY;      // a row that sees nothing adds 0
     }
     __syncthreads();
-    // wave w: keys kt*64 + 16w .. +15 (A operand, natural order) x window row tiles
-    const int kw = kt * kKT + wave * 16 + ln;               // this lane's key row for the A operand
-    const int pidx = min(kw, si.kv - 1) >> 4;
-    int page = a.page_table[(int64_t)b * a.max_pages + pidx];
-    const bool key_ok = kw < si.kv && page >= 0 && page < a.pool_pages;
+    // wave w: keys kt*64 + 16w .. +15 (A operand, natural order) x window row tiles.
+    // The wave's 16 keys share one page (16-key pages, 16-aligned), so one
+    // page-table entry gives every key's validity; they also share one 32-bit
+    // mask word per row.
+    const int kw0 = kt * kKT + wave * 16;
+    const int kw = kw0 + ln;                                 // this lane's key row for the A operand
+    const int page = a.page_table[(int64_t)b * a.max_pages + (min(kw0, si.kv - 1) >> 4)];
+    const bool page_ok = page >= 0 && page < a.pool_pages;
+    const bool key_ok = kw < si.kv && page_ok;
     const int64_t krow = key_ok ? (int64_t)page * 16 + (kw & 15) : 0;
     bf16x8 kf[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
         kf[ks] = *(const bf16x8*)(a.k + krow * a.n_out + h * kHD + ks * 32 + g * 8);
+    // C layout: register e of lane group g is key kw0 + 4g + e
+    uint32_t kvalid = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kvalid |= (page_ok && kw0 + 4 * g + e < si.kv ? 1u : 0u) << e;
     const int rtiles = (mb + 15) / 16;
     float csum[4] = {0.f, 0.f, 0.f, 0.f};                    // keys 16w + 4g + e
     const bool has_mask = a.mask != nullptr;
@@ -651,19 +816,15 @@ __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
             st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf, st, 0, 0, 0);
         }
         const float lse = row < mb ? s_lse[row] : INFINITY;
+        uint32_t vis = row < mb ? kvalid : 0u;
+        if (has_mask) {
+            const int64_t wi = a.mask_off[b] + (int64_t)min(row, mb - 1) * mwords + kw0 / 32;
+            const uint32_t word = (wi >= 0 && wi < a.mask_words) ? a.mask[wi] : 0u;
+            vis &= (word >> ((kw0 + 4 * g) & 31)) & 0xfu;
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int key = kt * kKT + wave * 16 + g * 4 + e;    // C layout: key 4g+e of the sub-tile
-            bool ok = row < mb && key < si.kv;
-            if (ok) {
-                int pg = a.page_table[(int64_t)b * a.max_pages + (key >> 4)];
-                ok = pg >= 0 && pg < a.pool_pages;
-            }
-            if (ok && has_mask) {
-                int64_t wi = a.mask_off[b] + (int64_t)row * mwords + key / 32;
-                ok = wi >= 0 && wi < a.mask_words && ((a.mask[wi] >> (key & 31)) & 1u);
-            }
-            float p = ok ? exp2f(fmaf(st[e], a.scale_log2, -lse)) : 0.f;
+            const float p = ((vis >> e) & 1u) ? exp2f(fmaf(st[e], a.scale_log2, -lse)) : 0.f;
             csum[e] += row16_sum(p);
         }
     }
@@ -890,9 +1051,19 @@ extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_
         a.part_ml = a.part_o + items * kQT * kHD;
     }
     if (dt == DLLM_BF16) {
-        const int64_t items = first_items(n_seq, n_rows, n_heads, splits);
+        // 256-row query tiles (64 rows per wave) when sequences are long enough
+        // to fill them; split keys only with 128-row tiles (the partials' layout)
+        const int rt = 2;
+        const int64_t items = (int64_t)n_heads * (n_rows / (64 * rt) + n_seq) * splits;
         DLLM_CHECK_SUP(items > 0 && items < (1ll << 30));
-        hipLaunchKernelGGL(attn_bf16_kernel, dim3((unsigned)items), dim3(kThreads), 0, stream, a);
+        const dim3 grid((unsigned)items), block(kAttnThreads);
+        if (rt == 4) {
+            if (mask_bits) hipLaunchKernelGGL((attn_bf16_kernel<4, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((attn_bf16_kernel<4, false>), grid, block, 0, stream, a);
+        } else {
+            if (mask_bits) hipLaunchKernelGGL((attn_bf16_kernel<2, true>), grid, block, 0, stream, a);
+            else hipLaunchKernelGGL((attn_bf16_kernel<2, false>), grid, block, 0, stream, a);
+        }
         if (splits > 1) {
             DLLM_CHECK_LAUNCH();
             int64_t fin = (int64_t)n_heads * (n_rows / kQT + n_seq);
