@@ -678,6 +678,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) 
 // touches: no atomics and no cross-workgroup synchronisation.
 constexpr int kFinThreads = 256;
 
+// MAXS: a power of two >= the split count.  Every loop over splits runs to
+// MAXS with clamped indices (loads in flight together; a loop to the runtime
+// count with a running maximum or sum would serialise them) and the values
+// past the split count are ignored.
+template <int MAXS>
 __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
     __shared__ int s_pref[kMaxSeq + 1];
     __shared__ int s_total;
@@ -738,21 +743,38 @@ __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
         const int nr = min(kQT, si.rows - qt * kQT);
         for (int idx = tid; idx < nr * (kHD / 8); idx += kFinThreads) {
             const int r = idx / (kHD / 8), c8 = idx % (kHD / 8);
-            float m = -INFINITY;
-            for (int spl = 0; spl < a.splits; ++spl)
-                m = fmaxf(m, a.part_ml[((int64_t)split_item(h, spl, qt) * kQT + r) * 2]);
-            float l = 0.f, o8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            for (int spl = 0; spl < a.splits; ++spl) {
-                const int64_t it = split_item(h, spl, qt);
-                const float ms = a.part_ml[(it * kQT + r) * 2];
-                const float f = exp2f(ms - m);
-                l += a.part_ml[(it * kQT + r) * 2 + 1] * f;
-                const float* po = a.part_o + (it * kQT + r) * kHD + c8 * 8;
-                f32x4 v0 = *(const f32x4*)po, v1 = *(const f32x4*)(po + 4);
+            float ms[MAXS], ls[MAXS];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    o8[e] += v0[e] * f;
-                    o8[4 + e] += v1[e] * f;
+            for (int spl = 0; spl < MAXS; ++spl) {
+                const int64_t it = split_item(h, min(spl, a.splits - 1), qt);
+                ms[spl] = a.part_ml[(it * kQT + r) * 2];
+                ls[spl] = a.part_ml[(it * kQT + r) * 2 + 1];
+            }
+            float m = -INFINITY;
+#pragma unroll
+            for (int spl = 0; spl < MAXS; ++spl)
+                if (spl < a.splits) m = fmaxf(m, ms[spl]);
+            float l = 0.f, o8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s0 = 0; s0 < MAXS; s0 += 4) {
+                f32x4 v[4][2];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int64_t it = split_item(h, min(s0 + j, a.splits - 1), qt);
+                    const float* po = a.part_o + (it * kQT + r) * kHD + c8 * 8;
+                    v[j][0] = *(const f32x4*)po;
+                    v[j][1] = *(const f32x4*)(po + 4);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (s0 + j >= a.splits) continue;
+                    const float f = exp2f(ms[s0 + j] - m);
+                    l += ls[s0 + j] * f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        o8[e] += v[j][0][e] * f;
+                        o8[4 + e] += v[j][1][e] * f;
+                    }
                 }
             }
             const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -773,14 +795,21 @@ __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
     if (mb == 0) return;
     // final log-sum-exp (base 2) of each window row, merged over the splits
     for (int r = tid; r < mb; r += kFinThreads) {
-        float m = -INFINITY;
-        for (int spl = 0; spl < a.splits; ++spl)
-            m = fmaxf(m, a.part_ml[((int64_t)split_item(h, spl, 0) * kQT + r) * 2]);
-        float l = 0.f;
-        for (int spl = 0; spl < a.splits; ++spl) {
-            const int64_t it = split_item(h, spl, 0);
-            l += a.part_ml[(it * kQT + r) * 2 + 1] * exp2f(a.part_ml[(it * kQT + r) * 2] - m);
+        float ms[MAXS], ls[MAXS];
+#pragma unroll
+        for (int spl = 0; spl < MAXS; ++spl) {
+            const int64_t it = split_item(h, min(spl, a.splits - 1), 0);
+            ms[spl] = a.part_ml[(it * kQT + r) * 2];
+            ls[spl] = a.part_ml[(it * kQT + r) * 2 + 1];
         }
+        float m = -INFINITY;
+#pragma unroll
+        for (int spl = 0; spl < MAXS; ++spl)
+            if (spl < a.splits) m = fmaxf(m, ms[spl]);
+        float l = 0.f;
+#pragma unroll
+        for (int spl = 0; spl < MAXS; ++spl)
+            if (spl < a.splits) l += ls[spl] * exp2f(ms[spl] - m);
         s_lse[r] = l > 0.f ? m + __log2f(l) : INFINITY;      // a row that sees nothing adds 0
     }
     __syncthreads();
@@ -806,22 +835,35 @@ __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
     float csum[4] = {0.f, 0.f, 0.f, 0.f};                    // keys 16w + 4g + e
     const bool has_mask = a.mask != nullptr;
     const int64_t mwords = (si.kv + 31) / 32;
-    for (int rt = 0; rt < rtiles; ++rt) {
+    // query fragments of every window row tile first (one round trip), then the scores
+    bf16x8 qfr[kQT / 16][4];
+#pragma unroll
+    for (int rt = 0; rt < kQT / 16; ++rt) {
+        const int qrow = seq_r0 + min(rt * 16 + ln, mb - 1);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            qfr[rt][ks] = *(const bf16x8*)(a.q + (int64_t)qrow * a.n_out + h * kHD + ks * 32 + g * 8);
+    }
+    uint32_t mword[kQT / 16];
+#pragma unroll
+    for (int rt = 0; rt < kQT / 16; ++rt) {
+        mword[rt] = 0xffffffffu;
+        if (has_mask) {
+            const int64_t wi = a.mask_off[b] + (int64_t)min(rt * 16 + ln, mb - 1) * mwords + kw0 / 32;
+            mword[rt] = (wi >= 0 && wi < a.mask_words) ? a.mask[wi] : 0u;
+        }
+    }
+#pragma unroll
+    for (int rt = 0; rt < kQT / 16; ++rt) {
+        if (rt >= rtiles) continue;
         const int row = rt * 16 + ln;                        // this lane's window row (B operand / C column)
-        const int qrow = seq_r0 + min(row, mb - 1);
         f32x4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            bf16x8 qf = *(const bf16x8*)(a.q + (int64_t)qrow * a.n_out + h * kHD + ks * 32 + g * 8);
-            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf, st, 0, 0, 0);
-        }
+        for (int ks = 0; ks < 4; ++ks)
+            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qfr[rt][ks], st, 0, 0, 0);
         const float lse = row < mb ? s_lse[row] : INFINITY;
         uint32_t vis = row < mb ? kvalid : 0u;
-        if (has_mask) {
-            const int64_t wi = a.mask_off[b] + (int64_t)min(row, mb - 1) * mwords + kw0 / 32;
-            const uint32_t word = (wi >= 0 && wi < a.mask_words) ? a.mask[wi] : 0u;
-            vis &= (word >> ((kw0 + 4 * g) & 31)) & 0xfu;
-        }
+        vis &= (mword[rt] >> ((kw0 + 4 * g) & 31)) & 0xfu;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float p = ((vis >> e) & 1u) ? exp2f(fmaf(st[e], a.scale_log2, -lse)) : 0.f;
@@ -1069,7 +1111,14 @@ extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_
             int64_t fin = (int64_t)n_heads * (n_rows / kQT + n_seq);
             if (want_mass) fin += (int64_t)n_heads * n_seq * ((max_kv + kKT - 1) / kKT);
             DLLM_CHECK_SUP(fin < (1ll << 30));
-            hipLaunchKernelGGL(attn_finish_kernel, dim3((unsigned)fin), dim3(kFinThreads), 0, stream, a);
+            if (splits <= 2)
+                hipLaunchKernelGGL(attn_finish_kernel<2>, dim3((unsigned)fin), dim3(kFinThreads), 0, stream, a);
+            else if (splits <= 4)
+                hipLaunchKernelGGL(attn_finish_kernel<4>, dim3((unsigned)fin), dim3(kFinThreads), 0, stream, a);
+            else if (splits <= 8)
+                hipLaunchKernelGGL(attn_finish_kernel<8>, dim3((unsigned)fin), dim3(kFinThreads), 0, stream, a);
+            else
+                hipLaunchKernelGGL(attn_finish_kernel<16>, dim3((unsigned)fin), dim3(kFinThreads), 0, stream, a);
         }
     } else {
         hipLaunchKernelGGL(attn_f32_kernel, dim3(n_seq * n_heads), dim3(kF32Threads), 0, stream,
