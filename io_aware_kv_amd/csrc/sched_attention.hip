@@ -68,7 +68,7 @@ struct AttnArgs {
 };
 
 struct SeqInfo {
-    int rows, kv, nqt;
+    int r0, rows, kv, nqt;
 };
 
 __device__ __forceinline__ SeqInfo seq_info(const AttnArgs& a, int b) {
@@ -76,6 +76,7 @@ __device__ __forceinline__ SeqInfo seq_info(const AttnArgs& a, int b) {
     int r0 = a.cu_q[b], r1 = a.cu_q[b + 1];
     r0 = max(0, min(r0, a.n_rows));
     r1 = max(r0, min(r1, a.n_rows));
+    s.r0 = r0;
     s.rows = r1 - r0;
     int kv = a.kv_len[b];
     kv = max(0, min(kv, min(a.max_kv, a.max_pages * 16)));
@@ -193,10 +194,11 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) 
     constexpr int kQPerWave = QT / 4 / 4;                               // query-tile copies per wave
     static_assert(QT * 8 <= kMaskStageBytes && kQPerWave * 4 * 4 * 256 <= kQSlots * kStageBytes, "layout");
     static_assert((kNS - 1) * kPerStage + kQPerWave < 64, "wait counts");
-    static_assert(kRingBytes >= (kMaxSeq + 1) * 4, "the schedule scan borrows the ring");
+    static_assert(kRingBytes >= (4 * kMaxSeq + 1) * 4, "the schedule scan borrows the ring");
     // one LDS allocation: the ring (which the schedule scan borrows first), then the page tables
     __shared__ __attribute__((aligned(16))) uint8_t lds[kRingBytes + (kMaxPages + 4 * kKT + 1) * 4 + kMaxPages / 4];
     int* s_pref = reinterpret_cast<int*>(lds);                                    // [kMaxSeq + 1], scheduling only
+    int* s_seq = s_pref + (kMaxSeq + 1);                                          // [kMaxSeq][3], scheduling only
     int* s_pages = reinterpret_cast<int*>(lds + kRingBytes);                      // [kMaxPages]
     float (*s_col)[kKT] = reinterpret_cast<float (*)[kKT]>(s_pages + kMaxPages);   // [4][kKT]
     int* s_total = reinterpret_cast<int*>(&s_col[4][0]);
@@ -218,6 +220,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) 
             if (b < a.n_seq) {
                 SeqInfo s = seq_info(a, b);
                 items = (s.rows + QT - 1) / QT * a.H * a.splits;
+                s_seq[3 * b] = s.r0;
+                s_seq[3 * b + 1] = s.rows;
+                s_seq[3 * b + 2] = s.kv;
             }
             int scan = items;
 #pragma unroll
@@ -245,14 +250,18 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) 
         if (s_pref[mid] <= item) lo = mid; else hi = mid - 1;
     }
     const int b = lo;
-    const SeqInfo si = seq_info(a, b);
+    SeqInfo si;                                          // from the scan: no second round trip
+    si.r0 = s_seq[3 * b];
+    si.rows = s_seq[3 * b + 1];
+    si.kv = s_seq[3 * b + 2];
+    si.nqt = (si.rows + kQT - 1) / kQT;
     const int nqt = (si.rows + QT - 1) / QT;
     const int local = item - s_pref[b];
     const int qt = local % nqt;                         // consecutive items: next query tile, same head
     const int hs = local / nqt;
     const int sp = hs % a.splits;                       // key split
     const int h = hs / a.splits;
-    const int seq_r0 = max(0, min(a.cu_q[b], a.n_rows));
+    const int seq_r0 = si.r0;
     const int r0 = seq_r0 + qt * QT;
     const int nr = min(QT, si.rows - qt * QT);
     const int ntiles = (si.kv + kKT - 1) / kKT;
@@ -688,29 +697,43 @@ __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
     __shared__ int s_total;
     __shared__ float s_lse[kQT];
     __shared__ float s_csum[4][kKT];
+    __shared__ int s_seq[kMaxSeq * 3];          // (r0, rows, kv) per sequence, from the scan
+    __shared__ int s_first[kMaxSeq + 1];        // first-launch items before each sequence
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, ln = lane & 15;
     const bool want_mass = a.mass_accum != nullptr && a.mass_count != nullptr;
     if (wave == 0) {
-        int base = 0;
+        int base = 0, base1 = 0;
         for (int c = 0; c < a.n_seq; c += 64) {
             int b = c + lane;
-            int items = 0;
+            int items = 0, first = 0;
             if (b < a.n_seq) {
                 SeqInfo s = seq_info(a, b);
                 items = a.H * (s.nqt + (want_mass ? (s.kv + kKT - 1) / kKT : 0));
+                first = s.nqt * a.H * a.splits;
+                s_seq[3 * b] = s.r0;
+                s_seq[3 * b + 1] = s.rows;
+                s_seq[3 * b + 2] = s.kv;
             }
-            int scan = items;
+            int scan = items, scan1 = first;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
-                int t = __shfl_up(scan, off);
-                if (lane >= off) scan += t;
+                int t = __shfl_up(scan, off), t1 = __shfl_up(scan1, off);
+                if (lane >= off) {
+                    scan += t;
+                    scan1 += t1;
+                }
             }
-            if (b < a.n_seq) s_pref[b + 1] = base + scan;
+            if (b < a.n_seq) {
+                s_pref[b + 1] = base + scan;
+                s_first[b + 1] = base1 + scan1;
+            }
             base += __shfl(scan, 63);
+            base1 += __shfl(scan1, 63);
         }
         if (lane == 0) {
             s_pref[0] = 0;
+            s_first[0] = 0;
             s_total = base;
         }
     }
@@ -724,16 +747,15 @@ __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
         if (s_pref[mid] <= item) lo = mid; else hi = mid - 1;
     }
     const int b = lo;
-    const SeqInfo si = seq_info(a, b);
+    SeqInfo si;                                          // from the scan: no second round trip
+    si.r0 = s_seq[3 * b];
+    si.rows = s_seq[3 * b + 1];
+    si.kv = s_seq[3 * b + 2];
+    si.nqt = (si.rows + kQT - 1) / kQT;
     const int local = item - s_pref[b];
-    const int seq_r0 = max(0, min(a.cu_q[b], a.n_rows));
+    const int seq_r0 = si.r0;
     // split-mode item index of (b, h, split, qt) in the first launch
-    int first_items = 0;
-    {
-        // items of sequences before b in the first launch: recount (cheap, n_seq <= 1024)
-        for (int bb = lane; bb < b; bb += 64) first_items += seq_info(a, bb).nqt * a.H * a.splits;
-        for (int off = 32; off > 0; off >>= 1) first_items += __shfl_xor(first_items, off);
-    }
+    const int first_items = s_first[b];
     auto split_item = [&](int h, int spl, int qt) { return first_items + (h * a.splits + spl) * si.nqt + qt; };
 
     if (local < a.H * si.nqt) {

@@ -81,21 +81,22 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(int n_heads, int n_cap, 
         cand[e] = false;
         key[e] = 0xffffffffu;
     }
-    // heads in groups of 8: the group's loads are independent and in flight
-    // together (a plain running sum would serialise every load), then added
-    // in ascending head order
+    // heads in groups of kGroup: the group's loads are independent and in
+    // flight together (a plain running sum would serialise every load), then
+    // added in ascending head order
+    constexpr int kGroup = 32 / kPer;
     const int nvalid = max(0, min(per, n_cap - i0));
-    for (int h0 = 0; h0 < n_heads; h0 += 8) {
-        float v[8][kPer];
+    for (int h0 = 0; h0 < n_heads; h0 += kGroup) {
+        float v[kGroup][kPer];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < kGroup; ++j) {
             const int hh = min(h0 + j, n_heads - 1);
             const float* mh = mseq + (int64_t)hh * n_cap + min(i0, n_cap - 1);
 #pragma unroll
             for (int e = 0; e < kPer; ++e) v[j][e] = mh[min(e, max(nvalid - 1, 0))];
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < kGroup; ++j)
 #pragma unroll
             for (int e = 0; e < kPer; ++e)
                 if (h0 + j < n_heads && e < nvalid) sc[e] += v[j][e];
