@@ -12,21 +12,25 @@
 // averaged over heads and window rows.
 //
 // bf16 kernel (gfx950).  One launch covers every (sequence, head, 128-row
-// query tile) item.  Items are decoded on the device from cu_q and kv_len:
-// each workgroup scans the per-sequence item counts (no host round-trip), and
-// consecutive items (same head, next query tile) are placed on the same XCD so
-// they share its L2 copy of the head's keys.  Eight waves own 16 query rows
-// each and walk all keys of the sequence in 64-key tiles gathered through the
-// block table, three tiles in flight in registers ahead of a double-buffered
-// LDS tile.  S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_16x16x32_bf16;
-// the K rows fed to the first product are permuted so that the P^T fragment a
-// lane holds covers 8 consecutive keys, and the matching V^T fragment is read
-// from the row-major V tile with the gfx950 LDS transpose read.  Softmax is
-// online in fp32 (base 2).  The workgroup of a sequence's first query tile
-// then re-reads the keys for the masked-window rows (their log-sum-exp is
-// final only then) and adds this head's column mass to mass_accum[b][h][:],
-// which only it writes: no atomics, no cross-workgroup synchronisation, and
-// the reduction order is fixed.
+// query tile[, key split]) item.  Items are decoded on the device from cu_q
+// and kv_len: each workgroup scans the per-sequence item counts (no host
+// round trip), and consecutive items (same head, next query tile) are placed
+// on the same XCD so they share its L2 copy of the head's keys.  Four waves
+// own 32 query rows each (two 16-row MFMA tiles, which share every K and V
+// fragment read) and walk the item's keys in 64-key tiles gathered through the
+// block table by direct-to-LDS copies, a two-stage ring so that two
+// workgroups share a compute unit.  S^T = K Q^T and O^T = V^T P^T run on
+// v_mfma_f32_16x16x32_bf16; the K rows fed to the first product are permuted
+// so that the P^T fragment a lane holds covers 8 consecutive keys, and the
+// matching V^T fragment is read from the row-major V tile with the gfx950 LDS
+// transpose read.  Softmax is online in fp32 (base 2).
+//
+// Formula (2) needs the masked-window rows' final log-sum-exp, so their
+// scores are recomputed after the main pass: by the workgroup of the
+// sequence's first query tile when keys are not split, else by the merge
+// launch.  Either way each (sequence, head, key) term is added to
+// mass_accum[b][h][key] by exactly one workgroup, in a fixed order: no
+// atomics, no cross-workgroup synchronisation, deterministic results.
 #include <math.h>
 #include <stdlib.h>
 
@@ -142,13 +146,14 @@ __device__ __forceinline__ s16x4 ds_read_tr(const uint16_t* p) {
 // instead explicit: each step waits for its own stage with s_waitcnt and
 // publishes it with a barrier, and the assembly's memory clobber keeps LDS
 // reads from moving across a copy.
-constexpr int kNS = 2;                  // ring stages (two workgroups share a compute unit)
 constexpr int kTileH = kKT * kHD;       // halfwords of one K (or V) tile: 16 KiB
 constexpr int kDmaPerWave = 8;          // 1 KiB copies per wave per stage (16 for K, 16 for V)
 constexpr int kAttnThreads = 256;       // 4 waves
 constexpr int kMaskStageBytes = 2048;   // up to 256 rows x 2 mask words per stage
 constexpr int kStageBytes = 2 * kTileH * 2 + kMaskStageBytes;
-constexpr int kRingBytes = kNS * kStageBytes;
+constexpr int kMaxSplits = 16;          // key splits per (sequence, head, query tile)
+constexpr int kMassQOffset = 1024;      // after the main pass: window-row queries at this LDS offset
+static_assert(kQT * 4 <= kMassQOffset && kMassQOffset + kQT * kHD * 2 <= 2 * kStageBytes, "tail LDS layout");
 
 __device__ __forceinline__ int swz_k(int key) { return (key + 4 * (key >> 4)) & 15; }
 __device__ __forceinline__ int swz_v(int key) { return 2 * ((key & 3) + 4 * ((key >> 3) & 1)); }
@@ -185,23 +190,25 @@ __device__ __forceinline__ void lds_sync() {
 // One workgroup per (sequence, head, QT-row query tile, key split); wave w
 // owns query rows 16 RT w .. 16 RT w + 16 RT - 1 (RT row tiles of 16), so the
 // K and V fragments a wave reads from LDS serve RT row tiles.
-template <int RT, bool HAS_MASK>
-__global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) {
+// NS: ring stages.  Two are launched (two workgroups per compute unit); four
+// stages with one workgroup per unit measured slower even on small grids.
+template <int RT, int NS, bool HAS_MASK>
+__global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kernel(AttnArgs a) {
+    constexpr int kRing = NS * kStageBytes;
     constexpr int QT = 64 * RT;
     constexpr int kMaskPerWave = HAS_MASK ? QT * 2 / 64 / 4 : 0;      // 4-byte copies per wave per stage
     constexpr int kPerStage = kDmaPerWave + kMaskPerWave;              // copies per wave per stage
     constexpr int kQSlots = RT / 2;                                     // ring stages the query tile borrows
     constexpr int kQPerWave = QT / 4 / 4;                               // query-tile copies per wave
     static_assert(QT * 8 <= kMaskStageBytes && kQPerWave * 4 * 4 * 256 <= kQSlots * kStageBytes, "layout");
-    static_assert((kNS - 1) * kPerStage + kQPerWave < 64, "wait counts");
-    static_assert(kRingBytes >= (4 * kMaxSeq + 1) * 4, "the schedule scan borrows the ring");
+    static_assert((NS - 1) * kPerStage + kQPerWave < 64, "wait counts");
+    static_assert(kRing >= (4 * kMaxSeq + 1) * 4, "the schedule scan borrows the ring");
     // one LDS allocation: the ring (which the schedule scan borrows first), then the page tables
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kRingBytes + (kMaxPages + 4 * kKT + 1) * 4 + kMaxPages / 4];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kRing + (kMaxPages + 1) * 4 + kMaxPages / 4];
     int* s_pref = reinterpret_cast<int*>(lds);                                    // [kMaxSeq + 1], scheduling only
     int* s_seq = s_pref + (kMaxSeq + 1);                                          // [kMaxSeq][3], scheduling only
-    int* s_pages = reinterpret_cast<int*>(lds + kRingBytes);                      // [kMaxPages]
-    float (*s_col)[kKT] = reinterpret_cast<float (*)[kKT]>(s_pages + kMaxPages);   // [4][kKT]
-    int* s_total = reinterpret_cast<int*>(&s_col[4][0]);
+    int* s_pages = reinterpret_cast<int*>(lds + kRing);                      // [kMaxPages]
+    int* s_total = s_pages + kMaxPages;
     uint8_t* s_tile_full = reinterpret_cast<uint8_t*>(s_total + 1);               // [kMaxPages / 4]
     auto k_tile = [&](int sl) { return reinterpret_cast<uint16_t*>(lds + sl * kStageBytes); };
     auto v_tile = [&](int sl) { return reinterpret_cast<uint16_t*>(lds + sl * kStageBytes) + kTileH; };
@@ -257,6 +264,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) 
     si.nqt = (si.rows + kQT - 1) / kQT;
     const int nqt = (si.rows + QT - 1) / QT;
     const int local = item - s_pref[b];
+    const int seq_first = s_pref[b];                    // the ring overwrites s_pref below
     const int qt = local % nqt;                         // consecutive items: next query tile, same head
     const int hs = local / nqt;
     const int sp = hs % a.splits;                       // key split
@@ -289,6 +297,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) 
     const int64_t safe_row = key0_page >= 0 ? (int64_t)key0_page * 16 : 0;
     const int64_t mwords = (si.kv + 31) / 32;
     const int64_t mask_row0 = HAS_MASK ? a.mask_off[b] + (int64_t)(qt * QT) * mwords : 0;
+    // window rows of formula (2) (query tile 0 only); loaded before any copy is issued
+    const bool want_mass = qt == 0 && a.mass_accum != nullptr && a.mass_count != nullptr;
+    const int mb_in = want_mass ? a.mass_count[b] : 0;
 
     // ---- copies: K groups (waves 0, 1) or V groups (waves 2, 3) of 4 keys; mask words; query tile ----
     const bool is_v = wave >= 2;
@@ -327,7 +338,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) 
 
     // query tile: rows r0 .. r0 + QT - 1 (clamped) into the last kQSlots stages, 4 rows per copy
     {
-        const uint32_t qdst = lds_addr(k_tile(kNS - kQSlots));
+        const uint32_t qdst = lds_addr(k_tile(NS - kQSlots));
 #pragma unroll
         for (int i = 0; i < kQPerWave; ++i) {
             const int c = wave * kQPerWave + i;
@@ -338,8 +349,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) 
                           __builtin_amdgcn_readfirstlane(qdst + c * 1024));
         }
     }
-    for (int s = 0; s < kNS - kQSlots; ++s) issue(s, t_begin + s);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm((kNS - kQSlots) * kPerStage, 15));   // the query tile
+    for (int s = 0; s < NS - kQSlots; ++s) issue(s, t_begin + s);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - kQSlots) * kPerStage, 15));   // the query tile
     lds_sync();
     __builtin_amdgcn_sched_barrier(0);
 
@@ -348,7 +359,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) 
     bool rt_active[RT], row_ok[RT];
     bf16x8 qf[RT][4];
     {
-        const uint16_t* qt_lds = k_tile(kNS - kQSlots);
+        const uint16_t* qt_lds = k_tile(NS - kQSlots);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const int row = wrow + rt * 16 + ln;
@@ -361,7 +372,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) 
     }
     lds_sync();                                         // every wave holds its query rows: the slots are free
     __builtin_amdgcn_sched_barrier(0);
-    for (int s = kNS - kQSlots; s < kNS - 1; ++s) issue(s, t_begin + s);
+    for (int s = NS - kQSlots; s < NS - 1; ++s) issue(s, t_begin + s);
 
     // ---- per-tile math ----
     // visibility of this lane's 16 scores in tile t (row validity and mask applied)
@@ -516,19 +527,24 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) 
     // then publishes it (__syncthreads would also wait for the younger stages).
     const int n_main = t_end - t_begin;
     for (int i = 0; i < n_main; ++i) {
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm((kNS - 2) * kPerStage, 15));
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * kPerStage, 15));
         lds_sync();
         __builtin_amdgcn_sched_barrier(0);
-        issue((i + kNS - 1) % kNS, t_begin + i + kNS - 1);
+        issue((i + NS - 1) % NS, t_begin + i + NS - 1);
         __builtin_amdgcn_sched_barrier(0);
-        attend(i % kNS, t_begin + i);
+        attend(i % NS, t_begin + i);
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));      // drain the stages past the end
     __syncthreads();
 
+    // LDS after the main pass (the ring is free): final log-sum-exp (base 2) of
+    // the tile's rows, the window rows' queries
+    float* s_lse = reinterpret_cast<float*>(lds);                        // [kQT]
+    uint16_t* s_qm = reinterpret_cast<uint16_t*>(lds + kMassQOffset);    // [kQT][kHD], row-swizzled
+
     if (a.splits > 1) {
-        // split mode (QT == kQT): publish the unnormalised partial; attn_finish_kernel
-        // merges the splits and forms the column mass
+        // ---- split mode (QT == kQT): publish the unnormalised partial; attn_finish_kernel
+        // merges the splits and forms the column mass ----
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             if (!rt_active[rt]) continue;
@@ -542,150 +558,163 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_bf16_kernel(AttnArgs a) 
             }
         }
         return;
-    }
-
-    // ---- output ----
+    } else {
+        // ---- output ----
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        if (!row_ok[rt]) continue;
-        const int my_row = wrow + rt * 16 + ln;
-        const float inv = l_run[rt] > 0.f ? 1.f / l_run[rt] : 0.f;
-        uint16_t* orow = a.o + (int64_t)(r0 + my_row) * a.n_out + h * kHD + g * 4;
+        for (int rt = 0; rt < RT; ++rt) {
+            if (!row_ok[rt]) continue;
+            const int my_row = wrow + rt * 16 + ln;
+            const float inv = l_run[rt] > 0.f ? 1.f / l_run[rt] : 0.f;
+            uint16_t* orow = a.o + (int64_t)(r0 + my_row) * a.n_out + h * kHD + g * 4;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            uint2 u;
-            u.x = pack_bf16x2(acc[rt][dt][0] * inv, acc[rt][dt][1] * inv);
-            u.y = pack_bf16x2(acc[rt][dt][2] * inv, acc[rt][dt][3] * inv);
-            *(uint2*)(orow + dt * 16) = u;
+            for (int dt = 0; dt < 8; ++dt) {
+                uint2 u;
+                u.x = pack_bf16x2(acc[rt][dt][0] * inv, acc[rt][dt][1] * inv);
+                u.y = pack_bf16x2(acc[rt][dt][2] * inv, acc[rt][dt][3] * inv);
+                *(uint2*)(orow + dt * 16) = u;
+            }
+            if (g == 0 && my_row < kQT)
+                s_lse[my_row] = l_run[rt] > 0.f ? m_run[rt] + __log2f(l_run[rt]) : INFINITY;
         }
     }
 
-    // ---- formula (2): this head's column mass from the masked-window rows ----
+    // ---- formula (2): this head's column mass over every key of the sequence ----
     // The window rows' log-sum-exp is final only now, so their scores are
-    // recomputed in a second pass over the keys (K only, staged through
-    // registers with ordinary loads; nothing is in flight to LDS any more).
-    if (qt != 0 || a.mass_accum == nullptr || a.mass_count == nullptr) return;
-    int mb = a.mass_count[b];
-    mb = max(0, min(mb, min(a.max_mass, min(si.rows, kQT))));
+    // recomputed.  Their queries are staged in LDS; wave w takes the 16-key
+    // groups w, w + 4, ...: the group's key fragments come straight from the
+    // cache rows into registers (A operand, keys as rows; the 16 keys share one
+    // page), up to four groups ahead, with the mask words and the running score they
+    // add to.  S^T = K Q^T gives a lane four keys of one window row; a row
+    // tile's column sums are DPP sums over its 16 lanes.  No LDS traffic for
+    // keys and no barrier in the loop; each key's sum is formed in a fixed
+    // order and added to mass_accum once, by this workgroup only.
+    if (!want_mass) return;
+    const int mb = max(0, min(mb_in, min(a.max_mass, min(si.rows, kQT))));
     if (mb == 0 || si.kv == 0) return;
+    {
+        u32x4 qv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = min(tid + i * kAttnThreads, mb * 16 - 1);
+            qv[i] = *(const u32x4*)(a.q + (int64_t)(seq_r0 + (c >> 4)) * a.n_out + h * kHD + (c & 15) * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = tid + i * kAttnThreads;
+            const int row = c >> 4;
+            if (c < mb * 16) *(u32x4*)(s_qm + row * kHD + (((c & 15) ^ swz_k(row)) * 8)) = qv[i];
+        }
+    }
+    lds_sync();                                              // s_qm, and s_lse of every window row
     const float norm = 1.f / ((float)a.H * (float)mb);
     float* macc = a.mass_accum + ((int64_t)b * a.H + h) * a.n_cap;
-    bool mrt[RT];
-    float inv_l[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        mrt[rt] = wrow + rt * 16 < mb;
-        inv_l[rt] = (wrow + rt * 16 + ln < mb && l_run[rt] > 0.f) ? 1.f / l_run[rt] : 0.f;
-    }
-    uint16_t* sKm = k_tile(0);                             // two staged K tiles (stage 0 area, 32 KiB)
-    float* s_mass = reinterpret_cast<float*>(lds + kStageBytes);
-    constexpr int kMassLds = (int)((kNS - 1) * kStageBytes / sizeof(float));
     const int kmax = min(si.kv, a.n_cap);
-    if (kmax > kMassLds) return;                           // rejected by the host
-    for (int i = tid; i < kmax; i += kAttnThreads) s_mass[i] = 0.f;
-    // staging: thread c moves 16-byte slot c % 16 of key c / 16 (4 passes per tile)
-    constexpr int kMassRing = 3;
-    u32x4 rk[kMassRing][4];
-    auto mload = [&](auto S, int t) __attribute__((always_inline)) {
-        constexpr int sl = decltype(S)::value;
+    const int rtiles = (mb + 15) / 16;
+    float lse_l[kQT / 16];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + i * kAttnThreads;
-            const int kg = t * kKT + (c >> 4);
-            const int page = s_pages[min(kg >> 4, last_page)];
-            const bool ok = (t < ntiles) & (kg < si.kv) & (page >= 0);
-            const int64_t row = ok ? (int64_t)page * 16 + (kg & 15) : safe_row;
-            rk[sl][i] = *(const u32x4*)(a.k + row * a.n_out + h * kHD + (c & 15) * 8);
+    for (int rt = 0; rt < kQT / 16; ++rt) {
+        const int row = rt * 16 + ln;
+        lse_l[rt] = row < mb ? s_lse[row] : INFINITY;
+    }
+    const int ngroups = (kmax + 15) / 16;
+    const int my_groups = ngroups > wave ? (ngroups - 1 - wave) / 4 + 1 : 0;
+    constexpr int kMR = HAS_MASK ? 2 : 4;                       // key groups in flight (registers)
+    bf16x8 kr[kMR][4];
+    uint32_t mw[kMR][kQT / 16];
+    float mold[kMR][4];
+    auto gload = [&](auto S, int i) __attribute__((always_inline)) {
+        constexpr int sl = decltype(S)::value;
+        const int kw0 = 16 * (wave + 4 * min(i, max(my_groups - 1, 0)));
+        const int page = s_pages[min(kw0 >> 4, last_page)];
+        const int key = kw0 + ln;
+        const int64_t row = (page >= 0 && key < si.kv) ? (int64_t)page * 16 + (key & 15) : safe_row;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            kr[sl][ks] = *(const bf16x8*)(a.k + row * a.n_out + h * kHD + ks * 32 + g * 8);
+        if constexpr (HAS_MASK) {
+#pragma unroll
+            for (int rt = 0; rt < kQT / 16; ++rt) {
+                const int64_t wi = mask_row0 + (int64_t)min(rt * 16 + ln, mb - 1) * mwords + kw0 / 32;
+                mw[sl][rt] = (rt < rtiles && wi >= 0 && wi < a.mask_words) ? a.mask[wi] : 0u;
+            }
+        }
+        // running scores of keys kw0 + 4g + e (the lanes with ln == 0 update them)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int kk = kw0 + 4 * g + e;
+            mold[sl][e] = (ln == 0 && kk < kmax) ? macc[kk] : 0.f;
         }
     };
-    auto mstore = [&](auto S, int buf) __attribute__((always_inline)) {
-        constexpr int sl = decltype(S)::value;
+    auto gstep = [&](auto S, int i) __attribute__((always_inline)) {
+        constexpr int sl = decltype(S)::value;                 // i % kMR
+        gload(Ic<(sl + kMR - 1) % kMR>{}, i + kMR - 1);
+        if (i < my_groups) {
+            const int kw0 = 16 * (wave + 4 * i);
+            const int page = s_pages[min(kw0 >> 4, last_page)];
+            uint32_t kvalid = 0;                               // C layout: register e of lane group g is key kw0 + 4g + e
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + i * kAttnThreads;
-            const int key = c >> 4;
-            *(u32x4*)(sKm + buf * kTileH + key * kHD + (((c & 15) ^ swz_k(key)) * 8)) = rk[sl][i];
-        }
-    };
-    auto mstep = [&](auto S, int t) __attribute__((always_inline)) {
-        constexpr int sl = decltype(S)::value;             // t % kMassRing
-        const int buf = t & 1;
-        mload(Ic<(sl + 2) % kMassRing>{}, t + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        if (t < ntiles) {
-            float cs[16];
+            for (int e = 0; e < 4; ++e) kvalid |= (page >= 0 && kw0 + 4 * g + e < si.kv ? 1u : 0u) << e;
+            float csum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < 16; ++j) cs[j] = 0.f;
-            bool any = false;
+            for (int rt = 0; rt < kQT / 16; ++rt) {
+                if (rt >= rtiles) continue;
+                const int row = rt * 16 + ln;                  // this lane's window row (B operand / C column)
+                bf16x8 qb[4];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) any = any || mrt[rt];
-            if (any) {
-                f32x4 st[RT][4];
-                scores(sKm + buf * kTileH, st);
+                for (int ks = 0; ks < 4; ++ks)
+                    qb[ks] = *(const bf16x8*)(s_qm + row * kHD + (((ks * 4 + g) ^ swz_k(row)) * 8));
+                f32x4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    if (!mrt[rt]) continue;
-                    const int row = wrow + rt * 16 + ln;
-                    uint32_t w0 = 0xffffffffu, w1 = 0xffffffffu;
-                    if constexpr (HAS_MASK) {
-                        const int64_t i0 = mask_row0 + (int64_t)min(row, max(nr - 1, 0)) * mwords + 2 * (int64_t)t;
-                        w0 = (i0 >= 0 && i0 < a.mask_words) ? a.mask[i0] : 0u;
-                        w1 = (i0 + 1 >= 0 && i0 + 1 < a.mask_words) ? a.mask[i0 + 1] : 0u;
-                    }
-                    const uint32_t vis = vis_bits(t, row < mb, w0, w1);
+                for (int ks = 0; ks < 4; ++ks)
+                    st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[sl][ks], qb[ks], st, 0, 0, 0);
+                uint32_t vis = row < mb ? kvalid : 0u;
+                if constexpr (HAS_MASK) vis &= (mw[sl][rt] >> ((kw0 + 4 * g) & 31)) & 0xfu;
 #pragma unroll
-                    for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float p = ((vis >> (t4 * 4 + e)) & 1u)
-                                ? __builtin_amdgcn_exp2f(fmaf(st[rt][t4][e], a.scale_log2, -m_run[rt])) * inv_l[rt]
-                                : 0.f;
-                            cs[t4 * 4 + e] += p;
-                        }
+                for (int e = 0; e < 4; ++e) {
+                    const float p = ((vis >> e) & 1u) ? exp2f(fmaf(st[e], a.scale_log2, -lse_l[rt])) : 0.f;
+                    csum[e] += row16_sum(p);
                 }
             }
-            // column sums over this wave's window rows: the 16 lanes of a row
-            // group hold one key each per register; sum over the rows (lanes)
+            if (ln == 0) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const float v = row16_sum(cs[j]);
-                if (ln == 0) s_col[wave][reg_key(j >> 2, g, j & 3)] = v;
+                for (int e = 0; e < 4; ++e) {
+                    const int kk = kw0 + 4 * g + e;
+                    if (kk < kmax) macc[kk] = mold[sl][e] + csum[e] * norm;
+                }
             }
         }
-        lds_sync();
-        if (t < ntiles && tid < kKT) {
-            const int kg = t * kKT + tid;
-            if (kg < kmax) s_mass[kg] += s_col[0][tid] + s_col[1][tid] + s_col[2][tid] + s_col[3][tid];
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        mstore(Ic<(sl + 1) % kMassRing>{}, (t + 1) & 1);
-        lds_sync();
     };
-    mload(Ic<0>{}, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mload(Ic<1>{}, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    lds_sync();                                       // s_mass zeroed
-    mstore(Ic<0>{}, 0);
-    lds_sync();
-    const int nm_pad = (ntiles + kMassRing - 1) / kMassRing * kMassRing;
-    for (int t = 0; t < nm_pad; t += kMassRing) {
-        mstep(Ic<0>{}, t);
-        mstep(Ic<1>{}, t + 1);
-        mstep(Ic<2>{}, t + 2);
+    gload(Ic<0>{}, 0);
+    if constexpr (kMR == 4) {
+        gload(Ic<1>{}, 1);
+        gload(Ic<2>{}, 2);
+        for (int i = 0; i < my_groups; i += 4) {
+            gstep(Ic<0>{}, i);
+            gstep(Ic<1>{}, i + 1);
+            gstep(Ic<2>{}, i + 2);
+            gstep(Ic<3>{}, i + 3);
+        }
+    } else {
+        for (int i = 0; i < my_groups; i += 2) {
+            gstep(Ic<0>{}, i);
+            gstep(Ic<1>{}, i + 1);
+        }
     }
-    for (int i = tid; i < kmax; i += kAttnThreads) macc[i] += s_mass[i] * norm;
 }
 
-// Split mode, second launch.  Items per sequence b: H * nqt merge items
-// (b, h, query tile) and, when formula (2) is requested, H * ntiles mass items
-// (b, h, key tile).  A merge item combines the key splits of its tile in split
-// order (fixed, so the result is deterministic) and writes o.  A mass item
-// rebuilds the masked-window rows' final log-sum-exp from the split partials,
-// recomputes those rows' scores against its 64 keys (S^T = K Q^T on MFMA) and
-// adds the column sums to mass_accum[b][h][its keys], which no other item
-// touches: no atomics and no cross-workgroup synchronisation.
+// Split mode, second launch.  Items per sequence b: H * ceil(rows_b / 16)
+// merge items (b, h, 16-row chunk) and, when formula (2) is requested,
+// H * ntiles mass items (b, h, key tile).  A merge item combines the key
+// splits of its rows in split order (fixed, so the result is deterministic)
+// and writes o: one thread per (row, 8 columns), every split's partials in
+// flight together.  A mass item rebuilds the masked-window rows' final
+// log-sum-exp from the split partials, recomputes those rows' scores against
+// its 64 keys (S^T = K Q^T on MFMA) and adds the column sums to
+// mass_accum[b][h][its keys], which no other item touches: no atomics and no
+// cross-workgroup synchronisation.  Every load that does not depend on
+// another is issued before the first wait.
 constexpr int kFinThreads = 256;
+constexpr int kMergeRows = kFinThreads / (kHD / 8);      // 16 rows per merge item
 
 // MAXS: a power of two >= the split count.  Every loop over splits runs to
 // MAXS with clamped indices (loads in flight together; a loop to the runtime
@@ -709,7 +738,7 @@ __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
             int items = 0, first = 0;
             if (b < a.n_seq) {
                 SeqInfo s = seq_info(a, b);
-                items = a.H * (s.nqt + (want_mass ? (s.kv + kKT - 1) / kKT : 0));
+                items = a.H * ((s.rows + kMergeRows - 1) / kMergeRows + (want_mass ? (s.kv + kKT - 1) / kKT : 0));
                 first = s.nqt * a.H * a.splits;
                 s_seq[3 * b] = s.r0;
                 s_seq[3 * b + 1] = s.rows;
@@ -754,76 +783,111 @@ __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
     si.nqt = (si.rows + kQT - 1) / kQT;
     const int local = item - s_pref[b];
     const int seq_r0 = si.r0;
+    const int nch = (si.rows + kMergeRows - 1) / kMergeRows;
     // split-mode item index of (b, h, split, qt) in the first launch
     const int first_items = s_first[b];
     auto split_item = [&](int h, int spl, int qt) { return first_items + (h * a.splits + spl) * si.nqt + qt; };
 
-    if (local < a.H * si.nqt) {
-        // ---- merge item ----
-        const int qt = local % si.nqt, h = local / si.nqt;
-        const int r0 = seq_r0 + qt * kQT;
-        const int nr = min(kQT, si.rows - qt * kQT);
-        for (int idx = tid; idx < nr * (kHD / 8); idx += kFinThreads) {
-            const int r = idx / (kHD / 8), c8 = idx % (kHD / 8);
-            float ms[MAXS], ls[MAXS];
+    if (local < a.H * nch) {
+        // ---- merge item: rows ch*16 .. ch*16+15 of head h, thread = (row, 8 columns) ----
+        const int ch = local % nch, h = local / nch;
+        const int row = ch * kMergeRows + (tid >> 4), c8 = tid & 15;
+        if (row >= si.rows) return;
+        const int qt = row / kQT, r = row % kQT;
+        float ms[MAXS], ls[MAXS];
+        f32x4 v[MAXS][2];
 #pragma unroll
-            for (int spl = 0; spl < MAXS; ++spl) {
-                const int64_t it = split_item(h, min(spl, a.splits - 1), qt);
-                ms[spl] = a.part_ml[(it * kQT + r) * 2];
-                ls[spl] = a.part_ml[(it * kQT + r) * 2 + 1];
-            }
-            float m = -INFINITY;
-#pragma unroll
-            for (int spl = 0; spl < MAXS; ++spl)
-                if (spl < a.splits) m = fmaxf(m, ms[spl]);
-            float l = 0.f, o8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s0 = 0; s0 < MAXS; s0 += 4) {
-                f32x4 v[4][2];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int64_t it = split_item(h, min(s0 + j, a.splits - 1), qt);
-                    const float* po = a.part_o + (it * kQT + r) * kHD + c8 * 8;
-                    v[j][0] = *(const f32x4*)po;
-                    v[j][1] = *(const f32x4*)(po + 4);
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (s0 + j >= a.splits) continue;
-                    const float f = exp2f(ms[s0 + j] - m);
-                    l += ls[s0 + j] * f;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        o8[e] += v[j][0][e] * f;
-                        o8[4 + e] += v[j][1][e] * f;
-                    }
-                }
-            }
-            const float inv = l > 0.f ? 1.f / l : 0.f;
-            u32x4 u;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(o8[2 * e] * inv, o8[2 * e + 1] * inv);
-            *(u32x4*)(a.o + (int64_t)(r0 + r) * a.n_out + h * kHD + c8 * 8) = u;
+        for (int spl = 0; spl < MAXS; ++spl) {
+            const int64_t it = split_item(h, min(spl, a.splits - 1), qt);
+            ms[spl] = a.part_ml[(it * kQT + r) * 2];
+            ls[spl] = a.part_ml[(it * kQT + r) * 2 + 1];
+            const float* po = a.part_o + (it * kQT + r) * kHD + c8 * 8;
+            v[spl][0] = *(const f32x4*)po;
+            v[spl][1] = *(const f32x4*)(po + 4);
         }
+        float m = -INFINITY;
+#pragma unroll
+        for (int spl = 0; spl < MAXS; ++spl)
+            if (spl < a.splits) m = fmaxf(m, ms[spl]);
+        float l = 0.f, o8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int spl = 0; spl < MAXS; ++spl) {
+            if (spl >= a.splits) continue;
+            const float f = exp2f(ms[spl] - m);
+            l += ls[spl] * f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                o8[e] += v[spl][0][e] * f;
+                o8[4 + e] += v[spl][1][e] * f;
+            }
+        }
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        u32x4 u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(o8[2 * e] * inv, o8[2 * e + 1] * inv);
+        *(u32x4*)(a.o + (int64_t)(seq_r0 + row) * a.n_out + h * kHD + c8 * 8) = u;
         return;
     }
 
     // ---- mass item: (h, key tile kt) of sequence b ----
-    const int ml = local - a.H * si.nqt;
+    const int ml = local - a.H * nch;
     const int ntiles = (si.kv + kKT - 1) / kKT;
     const int kt = ml % ntiles, h = ml / ntiles;
+    // wave w: keys kt*64 + 16w .. +15 (A operand, natural order) x window row tiles.
+    // The wave's 16 keys share one page (16-key pages, 16-aligned), so one
+    // page-table entry gives every key's validity; they also share one 32-bit
+    // mask word per row.
+    const int kw0 = kt * kKT + wave * 16;
+    const int page = a.page_table[(int64_t)b * a.max_pages + (min(kw0, si.kv - 1) >> 4)];
     int mb = a.mass_count[b];
-    mb = max(0, min(mb, min(a.max_mass, min(si.rows, kQT))));
-    if (mb == 0) return;
-    // final log-sum-exp (base 2) of each window row, merged over the splits
-    for (int r = tid; r < mb; r += kFinThreads) {
-        float ms[MAXS], ls[MAXS];
+    // window rows' split statistics, queries and mask words, and the running
+    // scores of this item's keys: all independent of the page entry above
+    const int r_ml = min(tid, kQT - 1);
+    float ms[MAXS], ls[MAXS];
 #pragma unroll
-        for (int spl = 0; spl < MAXS; ++spl) {
-            const int64_t it = split_item(h, min(spl, a.splits - 1), 0);
-            ms[spl] = a.part_ml[(it * kQT + r) * 2];
-            ls[spl] = a.part_ml[(it * kQT + r) * 2 + 1];
+    for (int spl = 0; spl < MAXS; ++spl) {
+        const int64_t it = split_item(h, min(spl, a.splits - 1), 0);
+        ms[spl] = a.part_ml[(it * kQT + r_ml) * 2];
+        ls[spl] = a.part_ml[(it * kQT + r_ml) * 2 + 1];
+    }
+    const int mb_rows = max(1, min(si.rows, min(a.max_mass, kQT)));   // mb <= this (clamped below)
+    bf16x8 qfr[kQT / 16][4];
+#pragma unroll
+    for (int rt = 0; rt < kQT / 16; ++rt) {
+        if (rt * 16 >= mb_rows) continue;                    // uniform: only the window's row tiles
+        const int qrow = seq_r0 + min(rt * 16 + ln, mb_rows - 1);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            qfr[rt][ks] = *(const bf16x8*)(a.q + (int64_t)qrow * a.n_out + h * kHD + ks * 32 + g * 8);
+    }
+    const bool has_mask = a.mask != nullptr;
+    const int64_t mwords = (si.kv + 31) / 32;
+    uint32_t mword[kQT / 16];
+#pragma unroll
+    for (int rt = 0; rt < kQT / 16; ++rt) {
+        mword[rt] = 0xffffffffu;
+        if (has_mask && rt * 16 < mb_rows) {
+            const int64_t wi = a.mask_off[b] + (int64_t)min(rt * 16 + ln, mb_rows - 1) * mwords + kw0 / 32;
+            mword[rt] = (wi >= 0 && wi < a.mask_words) ? a.mask[wi] : 0u;
         }
+    }
+    float* macc = a.mass_accum + ((int64_t)b * a.H + h) * a.n_cap;
+    const int key_t = kt * kKT + tid;
+    const float mold = (tid < kKT && key_t < si.kv && key_t < a.n_cap) ? macc[key_t] : 0.f;
+    // keys: need the page entry
+    const bool page_ok = page >= 0 && page < a.pool_pages;
+    const int kw = kw0 + ln;                                 // this lane's key row for the A operand
+    const bool key_ok = kw < si.kv && page_ok;
+    const int64_t krow = key_ok ? (int64_t)page * 16 + (kw & 15) : 0;
+    bf16x8 kf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        kf[ks] = *(const bf16x8*)(a.k + krow * a.n_out + h * kHD + ks * 32 + g * 8);
+
+    mb = max(0, min(mb, min(a.max_mass, min(si.rows, kQT))));
+    if (mb == 0) return;                                     // uniform: nothing to add
+    // final log-sum-exp (base 2) of each window row, merged over the splits
+    if (tid < mb) {
         float m = -INFINITY;
 #pragma unroll
         for (int spl = 0; spl < MAXS; ++spl)
@@ -832,49 +896,15 @@ __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
 #pragma unroll
         for (int spl = 0; spl < MAXS; ++spl)
             if (spl < a.splits) l += ls[spl] * exp2f(ms[spl] - m);
-        s_lse[r] = l > 0.f ? m + __log2f(l) : INFINITY;      // a row that sees nothing adds 0
+        s_lse[tid] = l > 0.f ? m + __log2f(l) : INFINITY;      // a row that sees nothing adds 0
     }
     __syncthreads();
-    // wave w: keys kt*64 + 16w .. +15 (A operand, natural order) x window row tiles.
-    // The wave's 16 keys share one page (16-key pages, 16-aligned), so one
-    // page-table entry gives every key's validity; they also share one 32-bit
-    // mask word per row.
-    const int kw0 = kt * kKT + wave * 16;
-    const int kw = kw0 + ln;                                 // this lane's key row for the A operand
-    const int page = a.page_table[(int64_t)b * a.max_pages + (min(kw0, si.kv - 1) >> 4)];
-    const bool page_ok = page >= 0 && page < a.pool_pages;
-    const bool key_ok = kw < si.kv && page_ok;
-    const int64_t krow = key_ok ? (int64_t)page * 16 + (kw & 15) : 0;
-    bf16x8 kf[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-        kf[ks] = *(const bf16x8*)(a.k + krow * a.n_out + h * kHD + ks * 32 + g * 8);
     // C layout: register e of lane group g is key kw0 + 4g + e
     uint32_t kvalid = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) kvalid |= (page_ok && kw0 + 4 * g + e < si.kv ? 1u : 0u) << e;
     const int rtiles = (mb + 15) / 16;
     float csum[4] = {0.f, 0.f, 0.f, 0.f};                    // keys 16w + 4g + e
-    const bool has_mask = a.mask != nullptr;
-    const int64_t mwords = (si.kv + 31) / 32;
-    // query fragments of every window row tile first (one round trip), then the scores
-    bf16x8 qfr[kQT / 16][4];
-#pragma unroll
-    for (int rt = 0; rt < kQT / 16; ++rt) {
-        const int qrow = seq_r0 + min(rt * 16 + ln, mb - 1);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            qfr[rt][ks] = *(const bf16x8*)(a.q + (int64_t)qrow * a.n_out + h * kHD + ks * 32 + g * 8);
-    }
-    uint32_t mword[kQT / 16];
-#pragma unroll
-    for (int rt = 0; rt < kQT / 16; ++rt) {
-        mword[rt] = 0xffffffffu;
-        if (has_mask) {
-            const int64_t wi = a.mask_off[b] + (int64_t)min(rt * 16 + ln, mb - 1) * mwords + kw0 / 32;
-            mword[rt] = (wi >= 0 && wi < a.mask_words) ? a.mask[wi] : 0u;
-        }
-    }
 #pragma unroll
     for (int rt = 0; rt < kQT / 16; ++rt) {
         if (rt >= rtiles) continue;
@@ -897,13 +927,9 @@ __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
         for (int e = 0; e < 4; ++e) s_csum[wave][g * 4 + e] = csum[e];
     }
     __syncthreads();
-    if (tid < kKT) {
-        const int key = kt * kKT + tid;
-        if (key < si.kv && key < a.n_cap) {
-            const float norm = 1.f / ((float)a.H * (float)mb);
-            float* macc = a.mass_accum + ((int64_t)b * a.H + h) * a.n_cap;
-            macc[key] += s_csum[tid >> 4][tid & 15] * norm;
-        }
+    if (tid < kKT && key_t < si.kv && key_t < a.n_cap) {
+        const float norm = 1.f / ((float)a.H * (float)mb);
+        macc[key_t] = mold + s_csum[tid >> 4][tid & 15] * norm;
     }
 }
 
@@ -1016,7 +1042,7 @@ int choose_splits(dllm_dtype dt, int n_seq, int n_rows, int n_heads, int max_kv)
     }
     const char* env = getenv("DLLM_ATTN_SPLITS");
     if (env && atoi(env) > 0) s = atoi(env);
-    if (s > 16) s = 16;
+    if (s > kMaxSplits) s = kMaxSplits;
     if (s > ktiles) s = ktiles > 0 ? ktiles : 1;
     return s < 1 ? 1 : s;
 }
@@ -1115,22 +1141,15 @@ extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_
         a.part_ml = a.part_o + items * kQT * kHD;
     }
     if (dt == DLLM_BF16) {
-        // 256-row query tiles (64 rows per wave) when sequences are long enough
-        // to fill them; split keys only with 128-row tiles (the partials' layout)
-        const int rt = 2;
-        const int64_t items = (int64_t)n_heads * (n_rows / (64 * rt) + n_seq) * splits;
+        // 128-row query tiles: four waves of 32 rows (two 16-row MFMA tiles each)
+        const int64_t items = (int64_t)n_heads * (n_rows / kQT + n_seq) * splits;
         DLLM_CHECK_SUP(items > 0 && items < (1ll << 30));
         const dim3 grid((unsigned)items), block(kAttnThreads);
-        if (rt == 4) {
-            if (mask_bits) hipLaunchKernelGGL((attn_bf16_kernel<4, true>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((attn_bf16_kernel<4, false>), grid, block, 0, stream, a);
-        } else {
-            if (mask_bits) hipLaunchKernelGGL((attn_bf16_kernel<2, true>), grid, block, 0, stream, a);
-            else hipLaunchKernelGGL((attn_bf16_kernel<2, false>), grid, block, 0, stream, a);
-        }
+        if (mask_bits) hipLaunchKernelGGL((attn_bf16_kernel<2, 2, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((attn_bf16_kernel<2, 2, false>), grid, block, 0, stream, a);
         if (splits > 1) {
             DLLM_CHECK_LAUNCH();
-            int64_t fin = (int64_t)n_heads * (n_rows / kQT + n_seq);
+            int64_t fin = (int64_t)n_heads * (n_rows / kMergeRows + n_seq);
             if (want_mass) fin += (int64_t)n_heads * n_seq * ((max_kv + kKT - 1) / kKT);
             DLLM_CHECK_SUP(fin < (1ll << 30));
             if (splits <= 2)
