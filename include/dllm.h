@@ -137,6 +137,32 @@ int dllm_qkv_rope_cachewrite(dllm_dtype dt, int n_rows, int d_model, int n_heads
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * a0-a3 in one call: dllm_qkv_rope_cachewrite where each row's cache slot is
+ * formed on the device from its logical position and the block table, with
+ * dllm_map_slots's rule (slot = page_table[b][l/page_size]*page_size +
+ * l%page_size for row r of sequence b, l = q_logical[r]; -1, and no write,
+ * for a negative or out-of-table position, a -1 entry or a page >=
+ * cache_rows/page_size).  [FD] 核心方法: K/V go straight into the paged cache
+ * from the projection kernel.  In the cache phase (bf16, n_rows <= 128) the
+ * mapping runs inside the projection kernel (no separate launch); otherwise
+ * it is a launch of its own ahead of the projection.
+ *
+ *   n_seq (1..1024), cu_q int32[n_seq+1], q_logical int32[n_rows],
+ *   page_table int32[n_seq*max_pages] (device), page_size > 0
+ *   slot     int32[n_rows]          out: the slot each row was written to (-1: none)
+ *   other arguments as dllm_qkv_rope_cachewrite
+ * Errors: as dllm_qkv_rope_cachewrite; INVALID_ARG for n_seq < 1, max_pages
+ * < 1, page_size < 1 or a null pointer; UNSUPPORTED for n_seq > 1024.
+ */
+int dllm_qkv_rope_cachewrite_paged(dllm_dtype dt, int n_seq, int n_rows, int d_model, int n_heads,
+                                   int head_dim, float rope_base, const void* x, const void* w_qkv,
+                                   const int32_t* pos, const int32_t* cu_q, const int32_t* q_logical,
+                                   const int32_t* page_table, int max_pages, int page_size,
+                                   int32_t* slot, void* q_out, void* k_cache, void* v_cache,
+                                   int64_t cache_rows, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+/*
  * a4-a5: block-table scheduled bidirectional attention over the paged cache,
  * every sequence's query rows in one launch with no padding, plus one layer's
  * term of the tracked-set score.  [FD] 核心方法 / 技术新颖性: variable-length

@@ -55,6 +55,54 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
     return x * per + (x < extra ? x : extra) + j;
 }
 
+
+// s_waitcnt immediate: vector-memory count vm, LDS/scalar count lgkm, no wait
+// on the export counter
+__device__ __forceinline__ constexpr int waitcnt_imm(int vm, int lgkm) {
+    return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Direct-to-LDS copies issued from inline assembly: lane i's bytes land at
+// LDS byte address base + size * i (base wave-uniform).  The compiler does
+// not see these loads, so it adds no waits for them: the caller orders them
+// with explicit s_waitcnt and barriers; the memory clobber keeps LDS reads
+// from moving across a copy.
+__device__ __forceinline__ void copy16_to_lds(const void* gptr, uint32_t base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(gptr), "s"(base) : "memory", "m0");
+}
+__device__ __forceinline__ void copy4_to_lds(const void* gptr, uint32_t base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :: "v"(gptr), "s"(base) : "memory", "m0");
+}
+
+// A 4-byte load the compiler does not track (so it adds no wait for it, and
+// counts none of it in the waits it adds): the caller waits with an explicit
+// s_waitcnt and then passes the value through fence_value() before using it.
+__device__ __forceinline__ int load_untracked(const int32_t* p) {
+    int v;
+    asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+    return v;
+}
+// Keeps later uses of v from being scheduled above the preceding wait.
+__device__ __forceinline__ int fence_value(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// Workgroup barrier that orders LDS only: the fences wait for this wave's
+// LDS operations, not for its global loads in flight (a plain __syncthreads
+// would drain those too).
+__device__ __forceinline__ void lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace dllm
 
 #define DLLM_CHECK_ARG(cond) \

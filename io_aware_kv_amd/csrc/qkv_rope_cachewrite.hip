@@ -14,15 +14,14 @@
 // the epilogue without leaving the workgroup: the fp32 tile is staged in LDS,
 // rotated with an fp64-reduced angle, rounded once to bf16 and written as
 // 16-byte row segments of q_out or of the slot's cache row.
-//   * R <= 128 (cache phase): qkv_stream_kernel streams W once, deep rings of
-//     direct-to-LDS copies keeping enough bytes in flight for HBM rate.
+//   * R <= 128 (cache phase): qkv_stream2_kernel streams W once through one
+//     ring of direct-to-LDS copies shared by the workgroup's four waves.
 //   * large R (full refresh): qkv_gemm_kernel, 256 x 256 tiles fed by
 //     direct-to-LDS copies.
 //   * in between: qkv_bf16_kernel, LDS-tiled 128 x 128 tiles.
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
-
 
 #include "common.h"
 
@@ -47,6 +46,13 @@ struct QkvArgs {
     uint16_t* k_cache;
     uint16_t* v_cache;
     int64_t cache_rows;
+    // paged mode (cache-phase kernel only): slots formed on the device from the
+    // block table; slot above is then unused
+    const int32_t* cu_q;
+    const int32_t* logical;
+    const int32_t* page_table;
+    int32_t* slot_out;
+    int n_seq, max_pages, page_size, pool_pages;
 };
 
 template <int BM>
@@ -232,12 +238,6 @@ constexpr int kGroupM = 4;
 // of bank conflicts.
 __device__ __forceinline__ int gemm_swz(int row) { return ((row >> 2) ^ (row >> 1)) & 3; }
 
-// s_waitcnt immediate: vector-memory count vm, LDS/scalar count lgkm, no wait
-// on the export counter
-__device__ __forceinline__ constexpr int waitcnt_imm(int vm, int lgkm) {
-    return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
-}
-
 __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(QkvArgs a, int n_mtiles, int n_ntiles) {
     constexpr int BK = kGBK, NS = kGNS;
     constexpr int kSlots = BK / 8;                      // 16-byte slots per staged row
@@ -412,85 +412,87 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(QkvArgs a, int n_mtile
 }
 
 // Cache-phase projection (R <= 128 rows).  Streaming W from HBM is the whole
-// cost (W is read exactly once), so what matters is the number of bytes in
-// flight: at ~2 us of memory latency the GPU needs ~11 MB outstanding to run
-// at HBM rate.  Each of 256-odd workgroups owns PP = 8 NT rotation pairs
-// (columns c and c + D/2 of one head, over the flattened Q/K/V pair list),
-// i.e. 2 PP rows of W.  Each of its 4 waves streams every fourth 32-wide K
-// chunk of both x (R_pad rows, from L2) and its W rows through a private
-// ring of NSW direct-to-LDS stages: no barriers in the main loop, and a ring
-// as deep as LDS allows.  The waves' partial sums meet once, in LDS, for the
-// rotation (one pow per pair, hardware sin/cos per element) and the 16-byte
-// stores.
-constexpr int kStreamLds = 144 * 1024;     // ring (and, after the loop, the partial sums)
+// HBM cost (W is read exactly once); every workgroup also re-reads all of x
+// from L2.  Each of 256-odd workgroups owns PP = 8 NT rotation pairs (columns
+// c and c + D/2 of one head, over the flattened Q/K/V pair list), i.e. 2 PP
+// rows of W, and all R rows of x (padded to 16 MT).  Measured on MI355X: a
+// compute unit keeps a bounded amount of memory traffic in flight, and the
+// L2-hit x copies share it with the HBM-miss W copies, so neither a deeper
+// ring nor larger copies moves the kernel; staggering the workgroups' K order
+// (so the compute units of one L2 do not read the same x lines at once) does
+// a little.
 constexpr int kStreamMaxRows = 128;
+constexpr int kMaxSeqPaged = 1024;        // paged mode: cu_q entries staged (n_seq + 1 <= this + 1)
 
-// KC: K elements per staged chunk (32 or 64).  A 64-wide chunk stages 128-byte
-// row pieces, one whole L2 line per row, so a copy instruction touches 8 lines
-// instead of 16 half lines: measured 20% faster at 72 rows.  It needs twice
-// the LDS per stage, so the widest shapes keep 32.
-template <int MT, int NT, int KC>
-struct StreamCfg {
-    static constexpr int kRows = MT * 16 + NT * 16;          // staged rows: x (padded), then W lo, W hi
-    static constexpr int kRowB = KC * 2;                      // bytes of a staged row
-    static constexpr int kRowsPerInst = 1024 / kRowB;         // rows one 1 KiB copy covers
-    static constexpr int kInst = kRows / kRowsPerInst;        // copies per stage
-    static constexpr int kStage = kRows * KC;                 // halfwords per stage
-    static constexpr int kNsw0 = kStreamLds / (4 * kRows * kRowB);
-    static constexpr int kNsw = kNsw0 < 8 ? kNsw0 : 8;
-    static constexpr int kPP = NT * 8;                        // pairs per workgroup
-    static constexpr int kLdc = 2 * kPP + 4;                  // partial-sum row stride (floats)
-    static constexpr int kRing = 4 * kNsw * kStage;           // halfwords
-    static constexpr int kCs = 4 * MT * 16 * kLdc * 2 + kPP * 4;   // partial sums + pair frequencies, halfwords
-    static constexpr int kSmem = kRing > kCs ? kRing : kCs;
+// Cache-phase projection with a shared ring: the four waves fill one ring of
+// 128-wide K stages together (256-byte row pieces, two whole L2 lines per row
+// per copy; each wave issues a quarter of a stage's copies) and each wave
+// takes one 32-wide k-step of every stage for all rows and pairs.  One
+// LDS-only barrier per stage publishes it (every wave's copies have landed)
+// and frees the oldest slot (every wave has read it).  With all 160 KiB of LDS
+// in one ring, five 32 KiB stages at 72 rows: four in flight per compute unit.
+constexpr int kStream2Lds = 160 * 1024;
+
+template <int MT, int NT>
+struct Stream2Cfg {
+    static constexpr int kKC = 128;                               // K elements per stage
+    static constexpr int kRows = 16 * (MT + NT);                  // x (padded), then W lo, W hi
+    static constexpr int kStageBytes = kRows * kKC * 2;
+    static constexpr int kInst = kStageBytes / 1024 / 4;          // 1 KiB copies per wave per stage
+    static constexpr int kNS0 = kStream2Lds / kStageBytes;
+    static constexpr int kNS = kNS0 < 6 ? kNS0 : 6;
+    static constexpr int kPP = NT * 8;                            // pairs per workgroup
+    static constexpr int kLdc = 2 * kPP + 4;                      // partial-sum row stride (floats)
+    static constexpr int kCsBytes = 4 * MT * 16 * kLdc * 4 + kPP * 8;
+    static constexpr int kSmem = kNS * kStageBytes > kCsBytes ? kNS * kStageBytes : kCsBytes;
 };
 
-// ring depth of a (row tiles, pair tiles, chunk width) configuration
-constexpr int stream_nsw(int mt, int nt, int kc) { return kStreamLds / (4 * 16 * (mt + nt) * kc * 2); }
-
-// physical 16-byte slot of logical slot kc in staged row r (conflict-free
-// fragment reads for 64-byte and 128-byte rows)
-template <int KC>
-__device__ __forceinline__ int stream_slot(int r, int kc) {
-    if constexpr (KC == 32) return (kc ^ gemm_swz(r)) & 3;
-    else return (kc ^ r ^ (r >> 3)) & 7;
-}
-
-template <int MT, int NT, int KC>
-__global__ __launch_bounds__(256, 1) void qkv_stream_kernel(QkvArgs a, int n_pairs) {
-    using C = StreamCfg<MT, NT, KC>;
-    static_assert(C::kNsw >= 2 && C::kNsw * C::kInst < 64, "ring depth / wait count");
-    static_assert(C::kSmem * 2 <= kStreamLds, "LDS budget");
-    constexpr int kPP = C::kPP, kInst = C::kInst, kNsw = C::kNsw, kStage = C::kStage;
+template <int MT, int NT, bool PAGED>
+__global__ __launch_bounds__(256, 1) void qkv_stream2_kernel(QkvArgs a, int n_pairs) {
+    using C = Stream2Cfg<MT, NT>;
+    constexpr int KC = C::kKC, NS = C::kNS, kInst = C::kInst, kPP = C::kPP;
+    constexpr int kStageBytes = C::kStageBytes;
+    static_assert(NS >= 2 && (NS - 1) * kInst < 64, "ring depth / wait count");
+    static_assert(C::kSmem <= kStream2Lds, "LDS budget");
+    static_assert(kStageBytes >= (kMaxSeqPaged + 1) * 4, "cu_q fits a ring slot");
     constexpr int kPieces = kPP / 8;                       // 8-pair output pieces per row
     constexpr int kItems = (kStreamMaxRows * kPieces + 255) / 256;   // epilogue items per thread
-    __shared__ __attribute__((aligned(16))) uint16_t smem[C::kSmem];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[C::kSmem];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, ln = lane & 15;
     const int D = a.head_dim, half = D >> 1, H = a.n_out / D;
     const int p0 = blockIdx.x * kPP;
-    const int n_chunks = a.d_model / KC;
-    const int n_local = n_chunks / 4;                      // chunks of this wave: c = 4 j + wave
+    const int n_st = a.d_model / KC;
 
-    // Epilogue items (row, 8-pair piece) of this thread: idx = tid + 256 k.
-    // Their positions and slots are fetched now, older than every copy below.
-    int it_pos[kItems], it_slot[kItems];
+    // epilogue items (row, 8-pair piece) of this thread: idx = tid + 256 k;
+    // their positions and slots are first used after the ring has drained.
+    // Paged mode: the rows' logical positions and cu_q are loaded here, ahead
+    // of every copy; the slot lookups follow once the ring is running.
+    int it_pos[kItems], it_slot[kItems], it_log[kItems];
+    int cuq[kMaxSeqPaged / 256 + 1];
 #pragma unroll
     for (int k = 0; k < kItems; ++k) {
         const int idx = tid + 256 * k;
         const int r = min(idx / kPieces, a.R - 1);
         it_pos[k] = a.pos[r];
-        it_slot[k] = a.slot[r];
+        if constexpr (PAGED) it_log[k] = load_untracked(a.logical + r);
+        else it_slot[k] = a.slot[r];
+    }
+    if constexpr (PAGED) {
+#pragma unroll
+        for (int i = 0; i <= kMaxSeqPaged / 256; ++i) cuq[i] = load_untracked(a.cu_q + min(tid + 256 * i, a.n_seq));
     }
 
-    // copy sources: instruction i covers staged rows kRowsPerInst i .., lane -> row + lane / (KC / 8)
-    constexpr int kSlots = KC / 8;
+    // copy sources: copy i of this wave covers staged rows 4 (wave kInst + i) ..
+    // +3, lane -> row + lane / 16 and the 16-byte slot lane % 16 of its place;
+    // the logical slot stored there is XOR-swizzled by the row, so the 16 rows
+    // a fragment read touches sit in 16 distinct bank groups
     const uint16_t* src[kInst];
 #pragma unroll
     for (int i = 0; i < kInst; ++i) {
-        const int r = i * C::kRowsPerInst + lane / kSlots;
-        const int kc = stream_slot<KC>(r, lane % kSlots);      // the logical slot stored at this lane's place
+        const int r = 4 * (wave * kInst + i) + (lane >> 4);
+        const int ls = (lane & 15) ^ (r & 15);
         const uint16_t* row_ptr;
         if (r < MT * 16) {
             row_ptr = a.x + (int64_t)min(r, a.R - 1) * a.d_model;          // padding rows repeat a real row
@@ -502,22 +504,51 @@ __global__ __launch_bounds__(256, 1) void qkv_stream_kernel(QkvArgs a, int n_pai
             const int64_t wrow = (int64_t)part * a.n_out + head * D + i_pair + (wr >= kPP ? half : 0);
             row_ptr = a.w + wrow * a.d_model;
         }
-        src[i] = row_ptr + kc * 8;
+        src[i] = row_ptr + ls * 8;
     }
-    uint16_t* ring = smem + wave * (kNsw * kStage);
+    const uint32_t ring0 = lds_addr(smem);
+    // workgroups start at different K stages (and wrap), so the compute units
+    // sharing an L2 do not all read the same x lines at the same moment
+    const int k_off = (int)((blockIdx.x * 7u) % (unsigned)n_st);
     auto issue = [&](int slot, int j) __attribute__((always_inline)) {
-        const int c = 4 * min(j, n_local - 1) + wave;     // past the end: re-read the last chunk
+        int c = min(j, n_st - 1) + k_off;                  // past the end: re-read the last stage
+        c -= c >= n_st ? n_st : 0;
+        const uint32_t base = __builtin_amdgcn_readfirstlane(ring0 + slot * kStageBytes + wave * kInst * 1024);
 #pragma unroll
-        for (int i = 0; i < kInst; ++i)
-            __builtin_amdgcn_global_load_lds((const void*)(src[i] + c * KC),
-                                             (__attribute__((address_space(3))) void*)(ring + slot * kStage + i * 512),
-                                             16, 0, 0);
+        for (int i = 0; i < kInst; ++i) copy16_to_lds(src[i] + c * KC, base + i * 1024);
     };
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s = 0; s < kNsw; ++s) issue(s, s);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(kNsw * kInst, 15));   // the item metadata only
-    __builtin_amdgcn_sched_barrier(0);
+    for (int s = 0; s < NS - 1; ++s) issue(s, s);
+
+    if constexpr (PAGED) {
+        // sequence of each item row from cu_q (staged in the ring's last slot,
+        // which the first copy into it follows a barrier), then its page entry
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 1) * kInst, 15));   // the metadata, not the copies
+#pragma unroll
+        for (int i = 0; i <= kMaxSeqPaged / 256; ++i) cuq[i] = fence_value(cuq[i]);
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) it_log[k] = fence_value(it_log[k]);
+        int* s_cuq = reinterpret_cast<int*>(smem + (NS - 1) * kStageBytes);
+#pragma unroll
+        for (int i = 0; i <= kMaxSeqPaged / 256; ++i)
+            if (tid + 256 * i <= a.n_seq) s_cuq[tid + 256 * i] = cuq[i];
+        lds_sync();
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) {
+            const int r = min((tid + 256 * k) / kPieces, a.R - 1);
+            int lo = 0, hi = a.n_seq - 1;                  // last b with cu_q[b] <= r
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_cuq[mid] <= r) lo = mid; else hi = mid - 1;
+            }
+            const int l = it_log[k];
+            const bool in_seq = r >= s_cuq[lo] && r < s_cuq[lo + 1];
+            const int j = l >= 0 ? l / a.page_size : -1;
+            const bool ok = in_seq && j >= 0 && j < a.max_pages;
+            // the page entry (-1: no slot), resolved after the ring drains
+            it_slot[k] = ok ? a.page_table[(int64_t)lo * a.max_pages + j] : -1;
+        }
+    }
 
     f32x4 acc[MT][NT];
 #pragma unroll
@@ -525,39 +556,42 @@ __global__ __launch_bounds__(256, 1) void qkv_stream_kernel(QkvArgs a, int n_pai
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int j = 0; j < n_local; ++j) {
-        const int slot = j % kNsw;
-        // stage j landed (kNsw - 1 younger stages may stay in flight: one is issued per trip)
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm((kNsw - 1) * kInst, 15));
-        const uint16_t* st = ring + slot * kStage;
+    const int ls = 4 * wave + g;                           // this lane's logical slot: k-step = wave
+    for (int j = 0; j < n_st; ++j) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * kInst, 15));   // this wave's copies of stage j
+        lds_sync();                                        // everyone's copies; everyone is done with j - 1
+        issue((j + NS - 1) % NS, j + NS - 1);
+        const uint16_t* st = reinterpret_cast<const uint16_t*>(smem + (j % NS) * kStageBytes);
+        bf16x8 xf[MT], wf[NT];
 #pragma unroll
-        for (int ks = 0; ks < KC / 32; ++ks) {
-            const int kc = ks * 4 + g;
-            bf16x8 xf[MT], wf[NT];
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const int r = m * 16 + ln;
-                xf[m] = *(const bf16x8*)(st + r * KC + stream_slot<KC>(r, kc) * 8);
-            }
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const int r = MT * 16 + t * 16 + ln;
-                wf[t] = *(const bf16x8*)(st + r * KC + stream_slot<KC>(r, kc) * 8);
-            }
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-#pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[m], wf[t], acc[m][t], 0, 0, 0);
+        for (int m = 0; m < MT; ++m) {
+            const int r = m * 16 + ln;
+            xf[m] = *(const bf16x8*)(st + r * KC + ((ls ^ (r & 15)) * 8));
         }
-        // the slot's fragment reads have returned before its next copy lands
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
-        __builtin_amdgcn_sched_barrier(0);
-        issue(slot, j + kNsw);
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int r = MT * 16 + t * 16 + ln;
+            wf[t] = *(const bf16x8*)(st + r * KC + ((ls ^ (r & 15)) * 8));
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[m], wf[t], acc[m][t], 0, 0, 0);
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));        // drain the re-read stages
     __syncthreads();
+    if constexpr (PAGED) {
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) {
+            const int idx = tid + 256 * k;
+            const int r = idx / kPieces;
+            const int page = it_slot[k];
+            const int l = it_log[k];
+            it_slot[k] = (page >= 0 && page < a.pool_pages) ? page * a.page_size + l % a.page_size : -1;
+            if (blockIdx.x == 0 && a.slot_out && idx % kPieces == 0 && r < a.R) a.slot_out[r] = it_slot[k];
+        }
+    }
 
     // ---- epilogue: per-wave fp32 partials [row][2 PP] in LDS, summed, rotated, stored ----
     float* Cs = reinterpret_cast<float*>(smem);
@@ -724,34 +758,25 @@ int check_shape(dllm_dtype dt, int n_rows, int d_model, int n_heads, int head_di
     return DLLM_OK;
 }
 
-template <int MT, int NT>
-void launch_stream_t(dim3 grid, hipStream_t stream, const QkvArgs& a, int n_pairs) {
-    // 64-wide chunks where a 2-deep ring fits and d_model splits into 4 x 64
-    constexpr int kWide = stream_nsw(MT, NT, 64) >= 2 ? 64 : 32;
-    if (kWide == 64 && a.d_model % 256 == 0)
-        hipLaunchKernelGGL((qkv_stream_kernel<MT, NT, kWide>), grid, dim3(256), 0, stream, a, n_pairs);
-    else
-        hipLaunchKernelGGL((qkv_stream_kernel<MT, NT, 32>), grid, dim3(256), 0, stream, a, n_pairs);
-}
-
-template <int NT>
-void launch_stream_nt(int mt, dim3 grid, hipStream_t stream, const QkvArgs& a, int n_pairs) {
+template <int NT, bool PAGED>
+void launch_stream2_nt(int mt, dim3 grid, hipStream_t stream, const QkvArgs& a, int n_pairs) {
     switch (mt) {
-        case 1: launch_stream_t<1, NT>(grid, stream, a, n_pairs); break;
-        case 2: launch_stream_t<2, NT>(grid, stream, a, n_pairs); break;
-        case 3: launch_stream_t<3, NT>(grid, stream, a, n_pairs); break;
-        case 4: launch_stream_t<4, NT>(grid, stream, a, n_pairs); break;
-        case 5: launch_stream_t<5, NT>(grid, stream, a, n_pairs); break;
-        case 6: launch_stream_t<6, NT>(grid, stream, a, n_pairs); break;
-        case 7: launch_stream_t<7, NT>(grid, stream, a, n_pairs); break;
-        default: launch_stream_t<8, NT>(grid, stream, a, n_pairs); break;
+        case 1: hipLaunchKernelGGL((qkv_stream2_kernel<1, NT, PAGED>), grid, dim3(256), 0, stream, a, n_pairs); break;
+        case 2: hipLaunchKernelGGL((qkv_stream2_kernel<2, NT, PAGED>), grid, dim3(256), 0, stream, a, n_pairs); break;
+        case 3: hipLaunchKernelGGL((qkv_stream2_kernel<3, NT, PAGED>), grid, dim3(256), 0, stream, a, n_pairs); break;
+        case 4: hipLaunchKernelGGL((qkv_stream2_kernel<4, NT, PAGED>), grid, dim3(256), 0, stream, a, n_pairs); break;
+        case 5: hipLaunchKernelGGL((qkv_stream2_kernel<5, NT, PAGED>), grid, dim3(256), 0, stream, a, n_pairs); break;
+        case 6: hipLaunchKernelGGL((qkv_stream2_kernel<6, NT, PAGED>), grid, dim3(256), 0, stream, a, n_pairs); break;
+        case 7: hipLaunchKernelGGL((qkv_stream2_kernel<7, NT, PAGED>), grid, dim3(256), 0, stream, a, n_pairs); break;
+        default: hipLaunchKernelGGL((qkv_stream2_kernel<8, NT, PAGED>), grid, dim3(256), 0, stream, a, n_pairs); break;
     }
 }
 
+template <bool PAGED>
 void launch_stream(int mt, int nt, dim3 grid, hipStream_t stream, const QkvArgs& a, int n_pairs) {
-    if (nt == 3) launch_stream_nt<3>(mt, grid, stream, a, n_pairs);
-    else if (nt == 2) launch_stream_nt<2>(mt, grid, stream, a, n_pairs);
-    else launch_stream_nt<1>(mt, grid, stream, a, n_pairs);
+    if (nt == 3) launch_stream2_nt<3, PAGED>(mt, grid, stream, a, n_pairs);
+    else if (nt == 2) launch_stream2_nt<2, PAGED>(mt, grid, stream, a, n_pairs);
+    else launch_stream2_nt<1, PAGED>(mt, grid, stream, a, n_pairs);
 }
 
 }  // namespace
@@ -762,18 +787,33 @@ extern "C" size_t dllm_qkv_rope_cachewrite_workspace(dllm_dtype dt, int n_rows, 
     return 0;      // no kernel of this entry point needs scratch memory
 }
 
-extern "C" int dllm_qkv_rope_cachewrite(dllm_dtype dt, int n_rows, int d_model, int n_heads,
-                                        int head_dim, float rope_base, const void* x,
-                                        const void* w_qkv, const int32_t* pos, const int32_t* slot,
-                                        void* q_out, void* k_cache, void* v_cache,
-                                        int64_t cache_rows, void* workspace,
-                                        size_t workspace_bytes, hipStream_t stream) {
-    int st = check_shape(dt, n_rows, d_model, n_heads, head_dim);
-    if (st != DLLM_OK) return st;
-    DLLM_CHECK_ARG(rope_base > 0.f && cache_rows >= 0);
-    if (n_rows == 0) return DLLM_OK;
-    DLLM_CHECK_ARG(x && w_qkv && pos && slot && q_out && k_cache && v_cache);
+namespace {
+
+// paged: the slot mapping's arguments (nullptr page_table: slots given)
+struct PagedArgs {
+    int n_seq, max_pages, page_size;
+    const int32_t* cu_q;
+    const int32_t* logical;
+    const int32_t* page_table;
+    int32_t* slot_out;
+};
+
+int qkv_launch(dllm_dtype dt, int n_rows, int d_model, int n_heads, int head_dim, float rope_base,
+               const void* x, const void* w_qkv, const int32_t* pos, const int32_t* slot, void* q_out,
+               void* k_cache, void* v_cache, int64_t cache_rows, const PagedArgs* pg,
+               hipStream_t stream) {
     const int n_out = n_heads * head_dim;
+    const int pool_pages = pg ? (int)(cache_rows / pg->page_size < (1ll << 30) ? cache_rows / pg->page_size
+                                                                               : (1ll << 30))
+                              : 0;
+    const bool skinny = dt == DLLM_BF16 && plan_bf16(n_rows, d_model, n_out, head_dim).kind == kSkinny;
+    if (pg && !skinny) {
+        // slots first (the same rule, its own launch), then the slot-taking kernels
+        int st = dllm_map_slots(pg->n_seq, n_rows, pg->page_size, pg->max_pages, pool_pages, pg->cu_q,
+                                pg->logical, pg->page_table, pg->slot_out, stream);
+        if (st != DLLM_OK) return st;
+        slot = pg->slot_out;
+    }
     if (dt == DLLM_F32) {
         int64_t total = (int64_t)n_rows * 3 * n_heads * (head_dim / 2);
         int threads = 256;
@@ -787,10 +827,8 @@ extern "C" int dllm_qkv_rope_cachewrite(dllm_dtype dt, int n_rows, int d_model, 
         return DLLM_OK;
     }
     QkvPlan p = plan_bf16(n_rows, d_model, n_out, head_dim);
-    (void)workspace;
-    (void)workspace_bytes;
     DLLM_CHECK_SUP(p.n_mtiles < 65536);
-    QkvArgs a;
+    QkvArgs a{};
     a.R = n_rows;
     a.d_model = d_model;
     a.head_dim = head_dim;
@@ -815,7 +853,19 @@ extern "C" int dllm_qkv_rope_cachewrite(dllm_dtype dt, int n_rows, int d_model, 
         const int n_pairs = 3 * n_out / 2;
         const int nt = n_pairs >= 3 * 8 * kNumCu ? 3 : n_pairs >= 2 * 8 * kNumCu ? 2 : 1;
         const dim3 grid((n_pairs + 8 * nt - 1) / (8 * nt));
-        launch_stream((n_rows + 15) / 16, nt, grid, stream, a, n_pairs);
+        if (pg) {
+            a.cu_q = pg->cu_q;
+            a.logical = pg->logical;
+            a.page_table = pg->page_table;
+            a.slot_out = pg->slot_out;
+            a.n_seq = pg->n_seq;
+            a.max_pages = pg->max_pages;
+            a.page_size = pg->page_size;
+            a.pool_pages = pool_pages;
+            launch_stream<true>((n_rows + 15) / 16, nt, grid, stream, a, n_pairs);
+        } else {
+            launch_stream<false>((n_rows + 15) / 16, nt, grid, stream, a, n_pairs);
+        }
     } else {
         dim3 grid(p.n_ntiles, p.n_mtiles, 1);
         if (p.bm == 64)
@@ -825,4 +875,47 @@ extern "C" int dllm_qkv_rope_cachewrite(dllm_dtype dt, int n_rows, int d_model, 
     }
     DLLM_CHECK_LAUNCH();
     return DLLM_OK;
+}
+
+}  // namespace
+
+extern "C" int dllm_qkv_rope_cachewrite(dllm_dtype dt, int n_rows, int d_model, int n_heads,
+                                        int head_dim, float rope_base, const void* x,
+                                        const void* w_qkv, const int32_t* pos, const int32_t* slot,
+                                        void* q_out, void* k_cache, void* v_cache,
+                                        int64_t cache_rows, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+    int st = check_shape(dt, n_rows, d_model, n_heads, head_dim);
+    if (st != DLLM_OK) return st;
+    DLLM_CHECK_ARG(rope_base > 0.f && cache_rows >= 0);
+    if (n_rows == 0) return DLLM_OK;
+    DLLM_CHECK_ARG(x && w_qkv && pos && slot && q_out && k_cache && v_cache);
+    (void)workspace;
+    (void)workspace_bytes;
+    return qkv_launch(dt, n_rows, d_model, n_heads, head_dim, rope_base, x, w_qkv, pos, slot, q_out,
+                      k_cache, v_cache, cache_rows, nullptr, stream);
+}
+
+extern "C" int dllm_qkv_rope_cachewrite_paged(dllm_dtype dt, int n_seq, int n_rows, int d_model,
+                                              int n_heads, int head_dim, float rope_base,
+                                              const void* x, const void* w_qkv, const int32_t* pos,
+                                              const int32_t* cu_q, const int32_t* q_logical,
+                                              const int32_t* page_table, int max_pages,
+                                              int page_size, int32_t* slot, void* q_out,
+                                              void* k_cache, void* v_cache, int64_t cache_rows,
+                                              void* workspace, size_t workspace_bytes,
+                                              hipStream_t stream) {
+    int st = check_shape(dt, n_rows, d_model, n_heads, head_dim);
+    if (st != DLLM_OK) return st;
+    DLLM_CHECK_ARG(rope_base > 0.f && cache_rows >= 0);
+    DLLM_CHECK_ARG(n_seq > 0 && max_pages > 0 && page_size > 0);
+    DLLM_CHECK_SUP(n_seq <= kMaxSeqPaged);
+    if (n_rows == 0) return DLLM_OK;
+    DLLM_CHECK_ARG(x && w_qkv && pos && cu_q && q_logical && page_table && slot && q_out && k_cache &&
+                   v_cache);
+    (void)workspace;
+    (void)workspace_bytes;
+    const PagedArgs pg{n_seq, max_pages, page_size, cu_q, q_logical, page_table, slot};
+    return qkv_launch(dt, n_rows, d_model, n_heads, head_dim, rope_base, x, w_qkv, pos, nullptr, q_out,
+                      k_cache, v_cache, cache_rows, &pg, stream);
 }

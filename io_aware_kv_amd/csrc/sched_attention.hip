@@ -133,7 +133,7 @@ __device__ __forceinline__ s16x4 ds_read_tr(const uint16_t* p) {
 }
 
 // K/V (and the query tile, and mask words) reach LDS through direct-to-LDS
-// copies, kNS key tiles deep.  A copy writes lane i's bytes at base + size*i,
+// copies, NS key tiles deep.  A copy writes lane i's bytes at base + size*i,
 // so K and V rows (256 B: one key, one head) are stored with their 16-byte
 // slots permuted by an XOR swizzle applied on the source side.  swz_k keeps
 // the 16 keys a K-fragment read touches in 16 distinct bank groups; swz_v
@@ -157,35 +157,6 @@ static_assert(kQT * 4 <= kMassQOffset && kMassQOffset + kQT * kHD * 2 <= 2 * kSt
 
 __device__ __forceinline__ int swz_k(int key) { return (key + 4 * (key >> 4)) & 15; }
 __device__ __forceinline__ int swz_v(int key) { return 2 * ((key & 3) + 4 * ((key >> 3) & 1)); }
-
-// s_waitcnt immediate: vector-memory count vm, LDS/scalar count lgkm, no wait
-// on the export counter
-__device__ __forceinline__ constexpr int waitcnt_imm(int vm, int lgkm) {
-    return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-// 16 bytes per lane from gptr to LDS byte address base + 16 * lane (base wave-uniform)
-__device__ __forceinline__ void copy16_to_lds(const void* gptr, uint32_t base) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(gptr), "s"(base) : "memory", "m0");
-}
-// 4 bytes per lane from gptr to LDS byte address base + 4 * lane
-__device__ __forceinline__ void copy4_to_lds(const void* gptr, uint32_t base) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-                 :: "v"(gptr), "s"(base) : "memory", "m0");
-}
-
-// Workgroup barrier that orders LDS only: the fences wait for this wave's
-// LDS operations, not for its global loads in flight (a plain __syncthreads
-// would drain those too).
-__device__ __forceinline__ void lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // One workgroup per (sequence, head, QT-row query tile, key split); wave w
 // owns query rows 16 RT w .. 16 RT w + 16 RT - 1 (RT row tiles of 16), so the

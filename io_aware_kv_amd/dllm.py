@@ -20,7 +20,7 @@ PAGE = 16
 # names in include/dllm.h, in declaration order
 EXPORTS = (
     "dllm_status_string", "dllm_version", "dllm_build_block_table", "dllm_map_slots",
-    "dllm_qkv_rope_cachewrite_workspace", "dllm_qkv_rope_cachewrite",
+    "dllm_qkv_rope_cachewrite_workspace", "dllm_qkv_rope_cachewrite", "dllm_qkv_rope_cachewrite_paged",
     "dllm_sched_attention_workspace", "dllm_sched_attention", "dllm_topk_tracked",
 )
 
@@ -53,6 +53,9 @@ def load() -> ctypes.CDLL:
     lib.dllm_qkv_rope_cachewrite_workspace.restype = _sz
     lib.dllm_qkv_rope_cachewrite.argtypes = [_i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp,
                                              _vp, _vp, _vp, _i64, _vp, _sz, _vp]
+    lib.dllm_qkv_rope_cachewrite_paged.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp,
+                                                   _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _i64,
+                                                   _vp, _sz, _vp]
     lib.dllm_sched_attention_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32]
     lib.dllm_sched_attention_workspace.restype = _sz
     lib.dllm_sched_attention.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
@@ -60,7 +63,7 @@ def load() -> ctypes.CDLL:
                                          _vp, _vp, _sz, _vp]
     lib.dllm_topk_tracked.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp]
     for name in ("dllm_build_block_table", "dllm_map_slots", "dllm_qkv_rope_cachewrite",
-                 "dllm_sched_attention", "dllm_topk_tracked"):
+                 "dllm_qkv_rope_cachewrite_paged", "dllm_sched_attention", "dllm_topk_tracked"):
         getattr(lib, name).restype = _i32
     _lib = lib
     return lib
@@ -138,6 +141,20 @@ def qkv_rope_cachewrite(x, w_qkv, pos, slot, q_out, k_cache, v_cache, n_heads: i
         dt, x.shape[0], x.shape[1], n_heads, head_dim, float(rope_base), _ptr(x), _ptr(w_qkv),
         _ptr(pos), _ptr(slot), _ptr(q_out), _ptr(k_cache), _ptr(v_cache), k_cache.shape[0],
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def qkv_rope_cachewrite_paged(x, w_qkv, pos, cu_q, q_logical, page_table, max_pages: int, slot, q_out,
+                              k_cache, v_cache, n_heads: int, head_dim: int, rope_base: float,
+                              workspace=None, page_size: int = PAGE, stream=None) -> None:
+    """qkv_rope_cachewrite with each row's cache slot formed from its logical
+    position and the block table (written to slot as well)."""
+    dt = dtype_code(x)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dllm_qkv_rope_cachewrite_paged", load().dllm_qkv_rope_cachewrite_paged(
+        dt, cu_q.shape[0] - 1, x.shape[0], x.shape[1], n_heads, head_dim, float(rope_base), _ptr(x),
+        _ptr(w_qkv), _ptr(pos), _ptr(cu_q), _ptr(q_logical), _ptr(page_table), max_pages, page_size,
+        _ptr(slot), _ptr(q_out), _ptr(k_cache), _ptr(v_cache), k_cache.shape[0], _ptr(workspace),
+        ws_bytes, _stream(stream)))
 
 
 def sched_attention_workspace(dt: int, n_seq: int, n_rows: int, n_heads: int, head_dim: int,

@@ -112,6 +112,12 @@ class FlashCacheRunner:
         dllm.qkv_rope_cachewrite(x, w, st.pos, st.slot, st.q, self.k_cache[layer], self.v_cache[layer],
                                  self.H, self.D, self.wl.shape.rope_base, st.ws_qkv)
 
+    def cache_update_paged(self, st: StepDevice, x: torch.Tensor, w: torch.Tensor, layer: int = 0) -> None:
+        """a0-a3 in one call: slots from the block table inside the projection."""
+        dllm.qkv_rope_cachewrite_paged(x, w, st.pos, st.cu_q, st.logical, self.page_table, self.wl.max_pages,
+                                       st.slot, st.q, self.k_cache[layer], self.v_cache[layer], self.H, self.D,
+                                       self.wl.shape.rope_base, st.ws_qkv)
+
     def attention(self, st: StepDevice, layer: int = 0, with_mass: bool = True) -> None:
         dllm.sched_attention(st.q, st.cu_q, self.k_cache[layer], self.v_cache[layer], self.page_table,
                              self.wl.max_pages, st.kv_len, st.o, st.ws_attn, self.H, self.D, st.max_kv,
@@ -124,8 +130,13 @@ class FlashCacheRunner:
         dllm.topk_tracked(self.mass, self.eligible, self.wl.shape.top_k, self.top_idx, self.top_val,
                           self.top_cnt, clear_mass=clear_mass)
 
-    def layer_step(self, st: StepDevice, x: torch.Tensor, w: torch.Tensor, layer: int = 0) -> None:
-        """a0..a5 of one layer: slots, fused cache update, attention + mass."""
-        self.map_slots(st)
-        self.cache_update(st, x, w, layer)
+    def layer_step(self, st: StepDevice, x: torch.Tensor, w: torch.Tensor, layer: int = 0,
+                   fused_slots: bool = True) -> None:
+        """a0..a5 of one layer: slots and the fused cache update (one call, or
+        the slot mapping as a call of its own), then attention + mass."""
+        if fused_slots:
+            self.cache_update_paged(st, x, w, layer)
+        else:
+            self.map_slots(st)
+            self.cache_update(st, x, w, layer)
         self.attention(st, layer)

@@ -82,6 +82,18 @@ def test_kernel_entry_points_reject_bad_shapes(lib):
              None) == -1                                     # null x
     assert f(*args(1, 0, 4096, 32, 128, 5e5)) == 0           # empty: nothing to do
 
+    fp = lib.dllm_qkv_rope_cachewrite_paged
+    def paged(dt=1, n_seq=1, R=8, d=4096, H=32, D=128, base=5e5, max_pages=32, page=16, table=fake):
+        return fp(dt, n_seq, R, d, H, D, base, fake, fake, fake, fake, fake, table, max_pages, page, fake,
+                  fake, fake, fake, 1024, fake, 1 << 30, None)
+    assert paged(D=96) == -2                                 # same shape rules as the slot-taking call
+    assert paged(n_seq=0) == -1
+    assert paged(n_seq=1025) == -2                           # more sequences than the kernel stages
+    assert paged(max_pages=0) == -1
+    assert paged(page=0) == -1
+    assert paged(table=None) == -1                           # null block table
+    assert paged(R=0) == 0                                   # empty: nothing to do
+
     a = lib.dllm_sched_attention
     def att(dt=1, n_seq=1, R=8, H=32, D=128, page=16, max_kv=512, mask=None, off=None, words=0,
             mass=None, max_mass=0, macc=None, n_cap=512, ws=1 << 30, max_pages=32):

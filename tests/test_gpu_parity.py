@@ -35,7 +35,7 @@ def head_sum(m):
     return out
 
 
-def run_gpu_step(c: Case, step: int, gpu):
+def run_gpu_step(c: Case, step: int, gpu, fused_slots: bool = True):
     import torch
     from io_aware_kv_amd.runner import FlashCacheRunner
     wl = c.wl
@@ -53,7 +53,7 @@ def run_gpu_step(c: Case, step: int, gpu):
     st = run.upload_step(rows)
     x = run.to_device_array(x_raw)
     w = run.to_device_array(c.w_raw)
-    run.layer_step(st, x, w, 0)
+    run.layer_step(st, x, w, 0, fused_slots=fused_slots)
     mass = head_sum(run.mass.cpu().numpy())
     run.topk(clear_mass=True)
     torch.cuda.synchronize()
@@ -135,3 +135,15 @@ def test_projection_kernel_paths(name, kernel, gpu, monkeypatch):
     c = case(name)
     g = run_gpu_step(c, 0, gpu)
     compare_step(c, g, 0)
+
+
+@pytest.mark.parametrize("name,step", [("tiny_bf16", 1), ("llada_b1", 1), ("verify_b4", 1), ("mixed_b8", 0)])
+def test_separate_slot_mapping_path(name, step, gpu):
+    """dllm_map_slots followed by dllm_qkv_rope_cachewrite (slots as an
+    input) gives the same parity as the one-call paged entry point the other
+    tests use (which maps the slots inside the cache-phase projection kernel,
+    and as a launch of its own for larger row counts)."""
+    log(f"[gpu] separate slot mapping {name} step {step}")
+    c = case(name)
+    g = run_gpu_step(c, step, gpu, fused_slots=False)
+    compare_step(c, g, step)
