@@ -88,8 +88,17 @@ __device__ __forceinline__ int load_untracked(const int32_t* p) {
     asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p) : "memory");
     return v;
 }
+__device__ __forceinline__ u32x4 load_untracked_x4(const void* p) {
+    u32x4 v;
+    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+    return v;
+}
 // Keeps later uses of v from being scheduled above the preceding wait.
 __device__ __forceinline__ int fence_value(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+__device__ __forceinline__ u32x4 fence_value(u32x4 v) {
     asm volatile("" : "+v"(v));
     return v;
 }

@@ -717,10 +717,10 @@ struct QkvPlan {
 };
 
 // Cache-phase row counts (R <= 128) take the weight-streaming kernel
-// (d_model a multiple of 128: four waves split the 32-wide K chunks).  Row
-// counts that give at least two 256 x 256 tiles per compute unit take the
-// large-tile kernel (head_dim 128, whole heads per wave); the rest take the
-// 128 x 128 LDS-tiled kernel.  None splits K across workgroups, so no
+// (d_model a multiple of 128).  Row counts that give at least one 256 x 256
+// tile per compute unit take the large-tile kernel (head_dim 128, whole
+// heads per wave; measured ahead of the 128 x 128 kernel from ~1800 rows);
+// the rest take the 128 x 128 LDS-tiled kernel.  None splits K across workgroups, so no
 // workspace is needed.
 // DLLM_QKV_KERNEL=tiled|gemm overrides the choice where the shape allows it.
 QkvPlan plan_bf16(int R, int d_model, int n_out, int head_dim) {
@@ -728,7 +728,7 @@ QkvPlan plan_bf16(int R, int d_model, int n_out, int head_dim) {
     const bool gemm_ok = head_dim == 128 && n_out % kGBN == 0 && d_model % kGBK == 0;
     const int64_t tiles256 = (int64_t)((R + kGBM - 1) / kGBM) * (3 * n_out / kGBN);
     if (R <= 128 && d_model % 128 == 0) p.kind = kSkinny;
-    else if (gemm_ok && tiles256 >= 2 * kNumCu) p.kind = kGemm256;
+    else if (gemm_ok && tiles256 >= kNumCu) p.kind = kGemm256;
     else p.kind = kTiled128;
     if (const char* e = getenv("DLLM_QKV_KERNEL")) {
         if (!strcmp(e, "tiled")) p.kind = kTiled128;

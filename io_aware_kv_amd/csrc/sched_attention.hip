@@ -71,6 +71,13 @@ struct AttnArgs {
     float* part_ml;         // split mode: [item][kQT][2] running max (base 2) and sum
 };
 
+// split partial outputs, fragment-major: float offset of lane `lane`'s four
+// values of (item, wave, row tile rt, 16-column tile dt).  Row wave*32 +
+// rt*16 + lane%16, columns dt*16 + (lane/16)*4 .. +3.
+__host__ __device__ __forceinline__ int64_t part_frag(int64_t item, int wave, int rt, int dt, int lane) {
+    return ((((item * 4 + wave) * 2 + rt) * 8 + dt) * 64 + lane) * 4;
+}
+
 struct SeqInfo {
     int r0, rows, kv, nqt;
 };
@@ -89,23 +96,21 @@ __device__ __forceinline__ SeqInfo seq_info(const AttnArgs& a, int b) {
     return s;
 }
 
+// Reductions over the four 16-lane groups (lanes l, l^16, l^32, l^48) with the
+// gfx950 lane swaps: a swap of a value with itself leaves each lane holding its
+// own value in one result and its partner's in the other, so combining the
+// two results reduces without selecting (and without an LDS round trip).
 __device__ __forceinline__ float wave_max16(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
+    auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+    t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
 }
 __device__ __forceinline__ float wave_sum16(float v) {
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
-}
-// sum over the 16 lanes that share lane >> 4
-__device__ __forceinline__ float group_sum16(float v) {
-    v += __shfl_xor(v, 1);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 4);
-    v += __shfl_xor(v, 8);
-    return v;
+    auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+    t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
 // Key (within a 64-key tile) that A-row m of sub-tile t feeds to S^T.
@@ -161,6 +166,18 @@ __device__ __forceinline__ int swz_v(int key) { return 2 * ((key & 3) + 4 * ((ke
 // One workgroup per (sequence, head, QT-row query tile, key split); wave w
 // owns query rows 16 RT w .. 16 RT w + 16 RT - 1 (RT row tiles of 16), so the
 // K and V fragments a wave reads from LDS serve RT row tiles.
+// s_waitcnt until at most `younger` ring stages (of PER copies each) are in
+// flight: the count is only known at run time, the immediate must be a constant
+template <int NS, int PER>
+__device__ __forceinline__ void wait_stages(int younger) {
+    static_assert(NS <= 4, "wait_stages cases");
+    if (younger <= 0) __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+    else if (younger == 1) __builtin_amdgcn_s_waitcnt(waitcnt_imm(PER, 15));
+    else if (younger == 2) __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * PER, 15));
+    else if (younger == 3) __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * PER, 15));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_imm(4 * PER, 15));
+}
+
 // NS: ring stages.  Two are launched (two workgroups per compute unit); four
 // stages with one workgroup per unit measured slower even on small grids.
 template <int RT, int NS, bool HAS_MASK>
@@ -169,10 +186,8 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     constexpr int QT = 64 * RT;
     constexpr int kMaskPerWave = HAS_MASK ? QT * 2 / 64 / 4 : 0;      // 4-byte copies per wave per stage
     constexpr int kPerStage = kDmaPerWave + kMaskPerWave;              // copies per wave per stage
-    constexpr int kQSlots = RT / 2;                                     // ring stages the query tile borrows
-    constexpr int kQPerWave = QT / 4 / 4;                               // query-tile copies per wave
-    static_assert(QT * 8 <= kMaskStageBytes && kQPerWave * 4 * 4 * 256 <= kQSlots * kStageBytes, "layout");
-    static_assert((NS - 1) * kPerStage + kQPerWave < 64, "wait counts");
+    static_assert(QT * 8 <= kMaskStageBytes, "layout");
+    static_assert(NS * kPerStage + 4 * RT < 64, "wait counts");
     static_assert(kRing >= (4 * kMaxSeq + 1) * 4, "the schedule scan borrows the ring");
     // one LDS allocation: the ring (which the schedule scan borrows first), then the page tables
     __shared__ __attribute__((aligned(16))) uint8_t lds[kRing + (kMaxPages + 1) * 4 + kMaxPages / 4];
@@ -262,8 +277,8 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     __syncthreads();
 
     const int last_page = max(npages - 1, 0);
-    // keys past kv_len, on a bad page, or of a padded step read the sequence's
-    // key 0 (a row the step reads anyway); the visibility bits zero them
+    // keys past kv_len or on a bad page read the sequence's key 0 (a row the
+    // item reads anyway); the visibility bits zero them
     const int key0_page = npages > 0 ? s_pages[0] : -1;
     const int64_t safe_row = key0_page >= 0 ? (int64_t)key0_page * 16 : 0;
     const int64_t mwords = (si.kv + 31) / 32;
@@ -307,43 +322,33 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
         }
     };
 
-    // query tile: rows r0 .. r0 + QT - 1 (clamped) into the last kQSlots stages, 4 rows per copy
-    {
-        const uint32_t qdst = lds_addr(k_tile(NS - kQSlots));
-#pragma unroll
-        for (int i = 0; i < kQPerWave; ++i) {
-            const int c = wave * kQPerWave + i;
-            const int row = 4 * c + (lane >> 4);
-            const int qrow = r0 + min(row, nr - 1);
-            const int sl16 = (lane & 15) ^ swz_k(row);
-            copy16_to_lds(a.q + (int64_t)qrow * a.n_out + h * kHD + sl16 * 8,
-                          __builtin_amdgcn_readfirstlane(qdst + c * 1024));
-        }
-    }
-    for (int s = 0; s < NS - kQSlots; ++s) issue(s, t_begin + s);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - kQSlots) * kPerStage, 15));   // the query tile
-    lds_sync();
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- query fragments (B operand of S^T = K Q^T), rows of this wave ----
+    // ---- query fragments (B operand of S^T = K Q^T), rows of this wave, straight
+    // into registers; then every ring stage is issued at once (the fragments
+    // are older than every copy, so one explicit wait covers them) ----
     const int wrow = wave * 16 * RT;
     bool rt_active[RT], row_ok[RT];
-    bf16x8 qf[RT][4];
-    {
-        const uint16_t* qt_lds = k_tile(NS - kQSlots);
+    u32x4 qraw[RT][4];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const int row = wrow + rt * 16 + ln;
-            rt_active[rt] = wrow + rt * 16 < nr;
-            row_ok[rt] = row < nr;
+    for (int rt = 0; rt < RT; ++rt) {
+        const int row = wrow + rt * 16 + ln;
+        rt_active[rt] = wrow + rt * 16 < nr;
+        row_ok[rt] = row < nr;
+        const int qrow = r0 + min(row, max(nr - 1, 0));
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                qf[rt][ks] = *(const bf16x8*)(qt_lds + row * kHD + (((ks * 4 + g) ^ swz_k(row)) * 8));
-        }
+        for (int ks = 0; ks < 4; ++ks)
+            qraw[rt][ks] = load_untracked_x4(a.q + (int64_t)qrow * a.n_out + h * kHD + ks * 32 + g * 8);
     }
-    lds_sync();                                         // every wave holds its query rows: the slots are free
+    const int n_main = t_end - t_begin;
+    const int n_pro = min(NS, n_main);                   // the ring's first fill: real tiles only
+    for (int s = 0; s < NS; ++s)
+        if (s < n_pro) issue(s, t_begin + s);
+    wait_stages<NS, kPerStage>(n_pro);                   // the query fragments (older than every copy)
+    bf16x8 qf[RT][4];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qf[rt][ks] = __builtin_bit_cast(bf16x8, fence_value(qraw[rt][ks]));
     __builtin_amdgcn_sched_barrier(0);
-    for (int s = NS - kQSlots; s < NS - 1; ++s) issue(s, t_begin + s);
 
     // ---- per-tile math ----
     // visibility of this lane's 16 scores in tile t (row validity and mask applied)
@@ -493,20 +498,21 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     };
 
     // ---- main pass: this item's key tiles through the ring ----
-    // Every step issues one stage (past t_end: the safe row, fully masked), so
-    // "stage i has landed" is always the same wait count; an LDS-only barrier
-    // then publishes it (__syncthreads would also wait for the younger stages).
-    const int n_main = t_end - t_begin;
+    // The prologue filled the ring; from the second step on, each step refills
+    // the slot the previous step read, and nothing past t_end is ever fetched.
+    // A step waits until its own tile has landed (the stages issued after it
+    // may stay in flight), then an LDS-only barrier publishes it
+    // (__syncthreads would also wait for the younger stages).
     for (int i = 0; i < n_main; ++i) {
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * kPerStage, 15));
+        const int issued = min(n_main, NS + max(i - 1, 0));   // tiles issued before this step
+        wait_stages<NS, kPerStage>(issued - 1 - i);            // ... younger than tile i
         lds_sync();
         __builtin_amdgcn_sched_barrier(0);
-        issue((i + NS - 1) % NS, t_begin + i + NS - 1);
+        if (i > 0 && i - 1 + NS < n_main) issue((i - 1) % NS, t_begin + i - 1 + NS);
         __builtin_amdgcn_sched_barrier(0);
         attend(i % NS, t_begin + i);
     }
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));      // drain the stages past the end
-    __syncthreads();
+    __syncthreads();                                    // every copy has been waited for above
 
     // LDS after the main pass (the ring is free): final log-sum-exp (base 2) of
     // the tile's rows, the window rows' queries
@@ -516,13 +522,16 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     if (a.splits > 1) {
         // ---- split mode (QT == kQT): publish the unnormalised partial; attn_finish_kernel
         // merges the splits and forms the column mass ----
+        // fragment-major: [item][wave][rt][dt][lane][4], so every store
+        // instruction writes 1 KiB of whole lines (row-major stores would
+        // scatter 64-byte half lines over 16 rows)
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             if (!rt_active[rt]) continue;
             const int my_row = wrow + rt * 16 + ln;
-            float* po = a.part_o + (int64_t)item * kQT * kHD + my_row * kHD + g * 4;
+            float* po = a.part_o + part_frag(item, wave, rt, 0, lane);
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) *(f32x4*)(po + dt * 16) = acc[rt][dt];
+            for (int dt = 0; dt < 8; ++dt) *(f32x4*)(po + dt * 256) = acc[rt][dt];
             if (g == 0) {
                 a.part_ml[((int64_t)item * kQT + my_row) * 2] = m_run[rt];
                 a.part_ml[((int64_t)item * kQT + my_row) * 2 + 1] = l_run[rt];
@@ -772,9 +781,10 @@ __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
             const int64_t it = split_item(h, min(spl, a.splits - 1), qt);
             ms[spl] = a.part_ml[(it * kQT + r) * 2];
             ls[spl] = a.part_ml[(it * kQT + r) * 2 + 1];
-            const float* po = a.part_o + (it * kQT + r) * kHD + c8 * 8;
-            v[spl][0] = *(const f32x4*)po;
-            v[spl][1] = *(const f32x4*)(po + 4);
+            // columns c8*8 .. +7: tile dt = c8/2, lane groups 2 (c8 % 2) and +1
+            const int w = r >> 5, rt = (r >> 4) & 1, lr = r & 15, g0 = 2 * (c8 & 1);
+            v[spl][0] = *(const f32x4*)(a.part_o + part_frag(it, w, rt, c8 >> 1, g0 * 16 + lr));
+            v[spl][1] = *(const f32x4*)(a.part_o + part_frag(it, w, rt, c8 >> 1, (g0 + 1) * 16 + lr));
         }
         float m = -INFINITY;
 #pragma unroll
