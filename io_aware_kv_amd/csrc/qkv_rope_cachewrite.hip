@@ -343,7 +343,12 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(QkvArgs a, int n_mtile
             for (int t = 0; t < 8; ++t)
                 acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cw[t], cx[i], acc[i][t], 0, 0, 0);
             if (more) issue_one(kt % NS, kt + NS, i);
-            nw[i] = read_w(kt + 1, i);
+            // the next step's W fragments early (its first group needs all
+            // eight), x fragment i once this group has used its register
+            if (i < 4) {
+                nw[2 * i] = read_w(kt + 1, 2 * i);
+                nw[2 * i + 1] = read_w(kt + 1, 2 * i + 1);
+            }
             nx[i] = read_x(kt + 1, i);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -410,6 +415,7 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(QkvArgs a, int n_mtile
         *(u32x4*)(dst + cpart + pc * 8) = v;
     }
 }
+
 
 // Cache-phase projection (R <= 128 rows).  Streaming W from HBM is the whole
 // HBM cost (W is read exactly once); every workgroup also re-reads all of x
