@@ -111,6 +111,22 @@ def main():
                              mass_accum=run.mass, n_cap=run.n_cap)
         run.topk(clear_mass=True)
 
+    # the unfused comparison arm of the same step: slot mapping, projection to
+    # memory, rotary, cache write as launches of their own, then attention, top-k
+    qkv_raw = torch.empty(R, 3 * n_out, dtype=st.q.dtype, device=dev)
+
+    def step_unfused(i):
+        c = i % copies
+        run.map_slots(st)
+        dllm.qkv_project(Xs[c], Ws[c], qkv_raw, sh.n_heads, sh.head_dim, st.ws_qkv)
+        dllm.rope_apply(qkv_raw, st.pos, st.q, sh.n_heads, sh.head_dim, sh.rope_base)
+        dllm.cache_write(qkv_raw, st.slot, Ks[c], Vs[c], sh.n_heads, sh.head_dim)
+        dllm.sched_attention(st.q, st.cu_q, Ks[c], Vs[c], run.page_table, wl.max_pages, st.kv_len, st.o,
+                             st.ws_attn, sh.n_heads, sh.head_dim, st.max_kv, mask_bits=st.mask_bits,
+                             mask_off=st.mask_off, mass_count=st.mass_count, max_mass_rows=st.max_mass,
+                             mass_accum=run.mass, n_cap=run.n_cap)
+        run.topk(clear_mass=True)
+
     stream = torch.cuda.current_stream()
     for i in range(args.warmup):
         step(i)
@@ -194,6 +210,29 @@ def main():
         q1.record(stream)
         torch.cuda.synchronize()
         qkv_graph_us = q0.elapsed_time(q1) / (reps * copies) * 1e3
+
+    # ---- the unfused arm, same replay scheme ----
+    unfused_ms = None
+    if not args.no_graph and sh.dtype == "bf16":
+        ugraphs = []
+        with torch.cuda.stream(cs):
+            for c in range(copies):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cs):
+                    step_unfused(c)
+                ugraphs.append(g)
+        stream.wait_stream(cs)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            ugraphs[i % copies].replay()
+        torch.cuda.synchronize()
+        u0, u1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        u0.record(stream)
+        for i in range(K):
+            ugraphs[i % copies].replay()
+        u1.record(stream)
+        torch.cuda.synchronize()
+        unfused_ms = u0.elapsed_time(u1) / K
 
     step_ms = graph_ms if graph_ms is not None else plain_ms
     value = R / (step_ms * 1e-3)
@@ -279,6 +318,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "qkv_rope_cachewrite", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic},
+        "unfused_arm": None if unfused_ms is None else {
+            "ms_per_step": unfused_ms, "fused_speedup": unfused_ms / step_ms,
+            "note": "slot mapping, projection to memory, rotary, cache write as separate launches; same attention and top-k"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -163,6 +163,33 @@ int dllm_qkv_rope_cachewrite_paged(dllm_dtype dt, int n_seq, int n_rows, int d_m
                                    hipStream_t stream);
 
 /*
+ * The unfused comparison arm of a1-a3 (three launches, intermediates in
+ * memory), kept to measure what the fused call saves.  [FD] 研究动机: the
+ * four-kernel chain (projection, rotary, cache write, attention) moves every
+ * intermediate through global memory; 核心方法: the fused kernel removes that.
+ * bf16 only (UNSUPPORTED otherwise).
+ *
+ * dllm_qkv_project: qkv_out [R, 3*H*D] = x w_qkv^T, unrotated, row r holding
+ *   q | k | v (shapes and errors as dllm_qkv_rope_cachewrite).
+ * dllm_rope_apply: rotate-half rotary embedding (as dllm_qkv_rope_cachewrite)
+ *   of qkv's q part into q_out [R, H*D] and of its k part in place; pos
+ *   int32[R].  Errors: INVALID_ARG (negative sizes, rope_base <= 0, null
+ *   pointers), UNSUPPORTED (head_dim other than 64 or 128).
+ * dllm_cache_write: qkv's k and v parts of row r to row slot[r] of k_cache and
+ *   v_cache ([cache_rows, H*D]); rows whose slot is negative or >= cache_rows
+ *   are skipped.  Errors: INVALID_ARG, UNSUPPORTED (H*D not a multiple of 8).
+ * All three are asynchronous on `stream`.
+ */
+int dllm_qkv_project(dllm_dtype dt, int n_rows, int d_model, int n_heads, int head_dim,
+                     const void* x, const void* w_qkv, void* qkv_out, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+int dllm_rope_apply(dllm_dtype dt, int n_rows, int n_heads, int head_dim, float rope_base,
+                    const int32_t* pos, void* qkv, void* q_out, hipStream_t stream);
+int dllm_cache_write(dllm_dtype dt, int n_rows, int n_heads, int head_dim, const void* qkv,
+                     const int32_t* slot, void* k_cache, void* v_cache, int64_t cache_rows,
+                     hipStream_t stream);
+
+/*
  * a4-a5: block-table scheduled bidirectional attention over the paged cache,
  * every sequence's query rows in one launch with no padding, plus one layer's
  * term of the tracked-set score.  [FD] 核心方法 / 技术新颖性: variable-length

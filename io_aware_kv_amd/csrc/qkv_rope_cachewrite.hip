@@ -53,6 +53,9 @@ struct QkvArgs {
     const int32_t* page_table;
     int32_t* slot_out;
     int n_seq, max_pages, page_size, pool_pages;
+    // unfused comparison arm: unrotated q|k|v rows to raw_out [R, 3 n_out]; no
+    // rotation and no cache write (nullptr otherwise)
+    uint16_t* raw_out;
 };
 
 template <int BM>
@@ -175,14 +178,16 @@ __global__ __launch_bounds__(kThreads) void qkv_bf16_kernel(QkvArgs a) {
             hi[e] = Cs[r * kLDC + c_hi + e];
         }
         uint16_t* dst;
-        if (part == 0) {
+        if (a.raw_out) {
+            dst = a.raw_out + (int64_t)grow * 3 * a.n_out + part * a.n_out + cpart;
+        } else if (part == 0) {
             dst = a.q_out + (int64_t)grow * a.n_out + cpart;
         } else {
             int s = a.slot[grow];
             if (s < 0 || (int64_t)s >= a.cache_rows) continue;
             dst = (part == 1 ? a.k_cache : a.v_cache) + (int64_t)s * a.n_out + cpart;
         }
-        if (part < 2) {
+        if (part < 2 && !a.raw_out) {
             const double p = (double)a.pos[grow];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -262,7 +267,7 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(QkvArgs a, int n_mtile
     const int mt = first_m + local % gm_sz, nt = local / gm_sz;
     const int row0 = mt * kGBM, col0 = nt * kGBN;
     if (tid < a.head_dim / 2) s_theta[tid] = pow((double)a.rope_base, -2.0 * tid / a.head_dim);
-    {
+    if (!a.raw_out) {
         const int grow = min(row0 + tid, a.R - 1);      // blockDim.x == kGBM
         s_pos[tid] = a.pos[grow];
         s_slot[tid] = a.slot[grow];
@@ -362,7 +367,7 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(QkvArgs a, int n_mtile
     // ---- epilogue: rotate in registers (pairs are n-tiles t and t+4), bf16, via LDS to rows ----
     const int part = col0 / a.n_out;                    // 0 = Q, 1 = K, 2 = V (tiles never straddle parts)
     const int cpart = col0 % a.n_out + wn * 128;        // first column of this wave's head within the part
-    if (part < 2) {
+    if (part < 2 && !a.raw_out) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -405,7 +410,9 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(QkvArgs a, int n_mtile
         if (grow >= a.R) break;
         const u32x4 v = *(const u32x4*)(&tile[r * 128 + ((pc ^ (r & 15)) << 3)]);
         uint16_t* dst;
-        if (part == 0) {
+        if (a.raw_out) {
+            dst = a.raw_out + (int64_t)grow * 3 * a.n_out + part * a.n_out;
+        } else if (part == 0) {
             dst = a.q_out + (int64_t)grow * a.n_out;
         } else {
             const int sl = s_slot[wm * 128 + r];
@@ -481,9 +488,16 @@ __global__ __launch_bounds__(256, 1) void qkv_stream2_kernel(QkvArgs a, int n_pa
     for (int k = 0; k < kItems; ++k) {
         const int idx = tid + 256 * k;
         const int r = min(idx / kPieces, a.R - 1);
-        it_pos[k] = a.pos[r];
-        if constexpr (PAGED) it_log[k] = load_untracked(a.logical + r);
-        else it_slot[k] = a.slot[r];
+        if constexpr (PAGED) {
+            it_pos[k] = a.pos[r];
+            it_log[k] = load_untracked(a.logical + r);
+        } else if (!a.raw_out) {
+            it_pos[k] = a.pos[r];
+            it_slot[k] = a.slot[r];
+        } else {
+            it_pos[k] = 0;
+            it_slot[k] = -1;
+        }
     }
     if constexpr (PAGED) {
 #pragma unroll
@@ -637,14 +651,16 @@ __global__ __launch_bounds__(256, 1) void qkv_stream2_kernel(QkvArgs a, int n_pa
         const int hp = p / half, i0 = p % half;            // a piece never straddles a head (half % 8 == 0)
         const int part = hp / H, head = hp % H;
         uint16_t* dst;
-        if (part == 0) {
+        if (!PAGED && a.raw_out) {
+            dst = a.raw_out + (int64_t)r * 3 * a.n_out + part * a.n_out;
+        } else if (part == 0) {
             dst = a.q_out + (int64_t)r * a.n_out;
         } else {
             const int sl = it_slot[k];
             if (sl < 0 || (int64_t)sl >= a.cache_rows) continue;
             dst = (part == 1 ? a.k_cache : a.v_cache) + (int64_t)sl * a.n_out;
         }
-        if (part < 2) {
+        if (part < 2 && (PAGED || !a.raw_out)) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 double ang = (double)it_pos[k] * s_theta[q * 8 + e];
@@ -807,7 +823,7 @@ struct PagedArgs {
 int qkv_launch(dllm_dtype dt, int n_rows, int d_model, int n_heads, int head_dim, float rope_base,
                const void* x, const void* w_qkv, const int32_t* pos, const int32_t* slot, void* q_out,
                void* k_cache, void* v_cache, int64_t cache_rows, const PagedArgs* pg,
-               hipStream_t stream) {
+               hipStream_t stream, void* raw_out = nullptr) {
     const int n_out = n_heads * head_dim;
     const int pool_pages = pg ? (int)(cache_rows / pg->page_size < (1ll << 30) ? cache_rows / pg->page_size
                                                                                : (1ll << 30))
@@ -849,6 +865,7 @@ int qkv_launch(dllm_dtype dt, int n_rows, int d_model, int n_heads, int head_dim
     a.k_cache = (uint16_t*)k_cache;
     a.v_cache = (uint16_t*)v_cache;
     a.cache_rows = cache_rows;
+    a.raw_out = (uint16_t*)raw_out;
     if (p.kind == kGemm256) {
         const int64_t tiles = (int64_t)p.n_mtiles * p.n_ntiles;
         DLLM_CHECK_SUP(tiles < (1ll << 31));
@@ -924,4 +941,18 @@ extern "C" int dllm_qkv_rope_cachewrite_paged(dllm_dtype dt, int n_seq, int n_ro
     const PagedArgs pg{n_seq, max_pages, page_size, cu_q, q_logical, page_table, slot};
     return qkv_launch(dt, n_rows, d_model, n_heads, head_dim, rope_base, x, w_qkv, pos, nullptr, q_out,
                       k_cache, v_cache, cache_rows, &pg, stream);
+}
+
+extern "C" int dllm_qkv_project(dllm_dtype dt, int n_rows, int d_model, int n_heads, int head_dim,
+                                const void* x, const void* w_qkv, void* qkv_out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+    int st = check_shape(dt, n_rows, d_model, n_heads, head_dim);
+    if (st != DLLM_OK) return st;
+    DLLM_CHECK_SUP(dt == DLLM_BF16);
+    if (n_rows == 0) return DLLM_OK;
+    DLLM_CHECK_ARG(x && w_qkv && qkv_out);
+    (void)workspace;
+    (void)workspace_bytes;
+    return qkv_launch(dt, n_rows, d_model, n_heads, head_dim, 1.f, x, w_qkv, nullptr, nullptr, nullptr,
+                      nullptr, nullptr, 0, nullptr, stream, qkv_out);
 }

@@ -21,6 +21,7 @@ PAGE = 16
 EXPORTS = (
     "dllm_status_string", "dllm_version", "dllm_build_block_table", "dllm_map_slots",
     "dllm_qkv_rope_cachewrite_workspace", "dllm_qkv_rope_cachewrite", "dllm_qkv_rope_cachewrite_paged",
+    "dllm_qkv_project", "dllm_rope_apply", "dllm_cache_write",
     "dllm_sched_attention_workspace", "dllm_sched_attention", "dllm_topk_tracked",
 )
 
@@ -56,6 +57,9 @@ def load() -> ctypes.CDLL:
     lib.dllm_qkv_rope_cachewrite_paged.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp,
                                                    _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _i64,
                                                    _vp, _sz, _vp]
+    lib.dllm_qkv_project.argtypes = [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+    lib.dllm_rope_apply.argtypes = [_i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp]
+    lib.dllm_cache_write.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp]
     lib.dllm_sched_attention_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32]
     lib.dllm_sched_attention_workspace.restype = _sz
     lib.dllm_sched_attention.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
@@ -63,7 +67,8 @@ def load() -> ctypes.CDLL:
                                          _vp, _vp, _sz, _vp]
     lib.dllm_topk_tracked.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp]
     for name in ("dllm_build_block_table", "dllm_map_slots", "dllm_qkv_rope_cachewrite",
-                 "dllm_qkv_rope_cachewrite_paged", "dllm_sched_attention", "dllm_topk_tracked"):
+                 "dllm_qkv_rope_cachewrite_paged", "dllm_qkv_project", "dllm_rope_apply", "dllm_cache_write",
+                 "dllm_sched_attention", "dllm_topk_tracked"):
         getattr(lib, name).restype = _i32
     _lib = lib
     return lib
@@ -155,6 +160,29 @@ def qkv_rope_cachewrite_paged(x, w_qkv, pos, cu_q, q_logical, page_table, max_pa
         _ptr(w_qkv), _ptr(pos), _ptr(cu_q), _ptr(q_logical), _ptr(page_table), max_pages, page_size,
         _ptr(slot), _ptr(q_out), _ptr(k_cache), _ptr(v_cache), k_cache.shape[0], _ptr(workspace),
         ws_bytes, _stream(stream)))
+
+
+def qkv_project(x, w_qkv, qkv_out, n_heads: int, head_dim: int, workspace=None, stream=None) -> None:
+    """Unfused arm: unrotated q|k|v rows [R, 3*H*D]."""
+    dt = dtype_code(x)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dllm_qkv_project", load().dllm_qkv_project(
+        dt, x.shape[0], x.shape[1], n_heads, head_dim, _ptr(x), _ptr(w_qkv), _ptr(qkv_out),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def rope_apply(qkv, pos, q_out, n_heads: int, head_dim: int, rope_base: float, stream=None) -> None:
+    """Unfused arm: q rotated into q_out, k rotated in place inside qkv."""
+    _check("dllm_rope_apply", load().dllm_rope_apply(
+        dtype_code(qkv), qkv.shape[0], n_heads, head_dim, float(rope_base), _ptr(pos), _ptr(qkv),
+        _ptr(q_out), _stream(stream)))
+
+
+def cache_write(qkv, slot, k_cache, v_cache, n_heads: int, head_dim: int, stream=None) -> None:
+    """Unfused arm: qkv's k|v parts to their cache slots."""
+    _check("dllm_cache_write", load().dllm_cache_write(
+        dtype_code(qkv), qkv.shape[0], n_heads, head_dim, _ptr(qkv), _ptr(slot), _ptr(k_cache),
+        _ptr(v_cache), k_cache.shape[0], _stream(stream)))
 
 
 def sched_attention_workspace(dt: int, n_seq: int, n_rows: int, n_heads: int, head_dim: int,

@@ -40,6 +40,7 @@ class StepDevice:
     o: torch.Tensor
     ws_qkv: torch.Tensor
     ws_attn: torch.Tensor
+    qkv_raw: Optional[torch.Tensor] = None      # unfused arm: unrotated q|k|v rows
 
 
 class FlashCacheRunner:
@@ -118,6 +119,15 @@ class FlashCacheRunner:
                                        st.slot, st.q, self.k_cache[layer], self.v_cache[layer], self.H, self.D,
                                        self.wl.shape.rope_base, st.ws_qkv)
 
+    def cache_update_unfused(self, st: StepDevice, x: torch.Tensor, w: torch.Tensor, layer: int = 0) -> None:
+        """The unfused comparison arm of a1-a3: projection, rotary and cache write
+        as three launches with q|k|v in memory between them (slots from map_slots)."""
+        if st.qkv_raw is None:
+            st.qkv_raw = torch.empty(st.n_rows, 3 * self.n_out, dtype=self.dtype, device=self.device)
+        dllm.qkv_project(x, w, st.qkv_raw, self.H, self.D, st.ws_qkv)
+        dllm.rope_apply(st.qkv_raw, st.pos, st.q, self.H, self.D, self.wl.shape.rope_base)
+        dllm.cache_write(st.qkv_raw, st.slot, self.k_cache[layer], self.v_cache[layer], self.H, self.D)
+
     def attention(self, st: StepDevice, layer: int = 0, with_mass: bool = True) -> None:
         dllm.sched_attention(st.q, st.cu_q, self.k_cache[layer], self.v_cache[layer], self.page_table,
                              self.wl.max_pages, st.kv_len, st.o, st.ws_attn, self.H, self.D, st.max_kv,
@@ -131,10 +141,14 @@ class FlashCacheRunner:
                           self.top_cnt, clear_mass=clear_mass)
 
     def layer_step(self, st: StepDevice, x: torch.Tensor, w: torch.Tensor, layer: int = 0,
-                   fused_slots: bool = True) -> None:
+                   fused_slots: bool = True, unfused: bool = False) -> None:
         """a0..a5 of one layer: slots and the fused cache update (one call, or
-        the slot mapping as a call of its own), then attention + mass."""
-        if fused_slots:
+        the slot mapping as a call of its own; or the unfused three-launch arm),
+        then attention + mass."""
+        if unfused:
+            self.map_slots(st)
+            self.cache_update_unfused(st, x, w, layer)
+        elif fused_slots:
             self.cache_update_paged(st, x, w, layer)
         else:
             self.map_slots(st)

@@ -94,6 +94,18 @@ def test_kernel_entry_points_reject_bad_shapes(lib):
     assert paged(table=None) == -1                           # null block table
     assert paged(R=0) == 0                                   # empty: nothing to do
 
+    # the unfused comparison arm: bf16 only
+    assert lib.dllm_qkv_project(0, 8, 4096, 32, 128, fake, fake, fake, None, 0, None) == -2
+    assert lib.dllm_qkv_project(1, 8, 4096, 32, 96, fake, fake, fake, None, 0, None) == -2
+    assert lib.dllm_qkv_project(1, 8, 4096, 32, 128, None, fake, fake, None, 0, None) == -1
+    assert lib.dllm_qkv_project(1, 0, 4096, 32, 128, fake, fake, fake, None, 0, None) == 0
+    assert lib.dllm_rope_apply(1, 8, 32, 128, 0.0, fake, fake, fake, None) == -1
+    assert lib.dllm_rope_apply(1, 8, 32, 96, 5e5, fake, fake, fake, None) == -2
+    assert lib.dllm_rope_apply(1, 8, 32, 128, 5e5, fake, None, fake, None) == -1
+    assert lib.dllm_cache_write(0, 8, 32, 128, fake, fake, fake, fake, 1024, None) == -2
+    assert lib.dllm_cache_write(1, 8, 32, 128, fake, None, fake, fake, 1024, None) == -1
+    assert lib.dllm_cache_write(1, 0, 32, 128, fake, fake, fake, fake, 1024, None) == 0
+
     a = lib.dllm_sched_attention
     def att(dt=1, n_seq=1, R=8, H=32, D=128, page=16, max_kv=512, mask=None, off=None, words=0,
             mass=None, max_mass=0, macc=None, n_cap=512, ws=1 << 30, max_pages=32):
