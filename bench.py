@@ -344,13 +344,16 @@ def bench_layers(args, dev):
     sts = {"full": run.upload_step(rows["full"])}
     xs = {"full": [W.device_activations(wl, rows["full"], 0, l, dev) for l in range(L)]}
 
-    def step(kind, ev=None):
+    def step(kind, ev=None, unfused=False):
         st = sts[kind]
         run.map_slots(st)
         for l in range(L):
             if ev is not None:
                 ev[l][0].record()
-            run.cache_update(st, xs[kind][l], Ws[l], l)
+            if unfused:
+                run.cache_update_unfused(st, xs[kind][l], Ws[l], l)
+            else:
+                run.cache_update(st, xs[kind][l], Ws[l], l)
             if ev is not None:
                 ev[l][1].record()
             run.attention(st, l)
@@ -397,6 +400,23 @@ def bench_layers(args, dev):
                      "attn_bound": "mfma" if att_flops / 2.5e15 > att_bytes / 8e12 else "hbm",
                      "layer_roofline_frac": (b_qkv + b_att) / (ms * 1e3 / L)}
         eprint(f"[bench] llada_b32 {kind}: {res[kind]}")
+    # the unfused comparison arm on the cache-phase step (per-layer projection,
+    # rotary and cache write as three launches with q|k|v in memory)
+    step("cache", unfused=True)
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(L)] for _ in range(K)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(K):
+        step("cache", evs[i], unfused=True)
+    t1.record()
+    torch.cuda.synchronize()
+    ums = t0.elapsed_time(t1) / K
+    unfused = {"us_per_layer": ums * 1e3 / L,
+               "update_us": float(np.mean([evs[i][l][0].elapsed_time(evs[i][l][1]) for i in range(K) for l in range(L)])) * 1e3,
+               "fused_speedup_per_layer": ums / res["cache"]["ms_per_step"],
+               "fused_update_speedup": float(np.mean([evs[i][l][0].elapsed_time(evs[i][l][1]) for i in range(K) for l in range(L)])) * 1e3 / res["cache"]["qkv_us"]}
+    eprint(f"[bench] llada_b32 cache, unfused arm: {unfused}")
     tot_rows = sum(res[k]["rows_per_layer"] for k in res)
     tot_ms = sum(res[k]["ms_per_step"] for k in res)
     value = tot_rows / (tot_ms * 1e-3 / L)
@@ -411,6 +431,7 @@ def bench_layers(args, dev):
                                "cache-phase (72 rows/seq) steps, top-32 once per step",
                    "layers": L, "batch": wl.n_seq, "parallelism": "single GPU", "timing": "stream launches"},
         "steps_detail": res,
+        "unfused_arm_cache_phase": unfused,
         "roofline": {"bound": "mfma", "kernel": "qkv_rope_cachewrite (full refresh)",
                      "achieved": 2 * dom["rows_per_layer"] * sh.d_model * 3 * n / (dom["qkv_us"] * 1e-6) / 1e12,
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -10,7 +10,9 @@ code.
 from __future__ import annotations
 
 import glob
+import json
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -22,6 +24,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "libdllm.so")
+RESOURCES = os.path.join(OUT_DIR, "kernel_resources.json")
 OBJ_DIR = os.path.join(PKG, "_build")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -30,13 +33,30 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",
          "-I", INCLUDE, "-I", CSRC]
 
 
-def _compile(src: str) -> str:
+_REMARK = re.compile(r"remark: +(Function Name|TotalSGPRs|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|"
+                     r"Occupancy \[waves/SIMD\]|SGPRs Spill|VGPRs Spill|LDS Size \[bytes/block\]): (\S+)")
+
+
+def _resources(stderr: str) -> dict:
+    """Per-kernel register, scratch and LDS use from the compiler's
+    kernel-resource-usage remarks."""
+    out, cur = {}, None
+    for m in _REMARK.finditer(stderr):
+        key, val = m.group(1), m.group(2)
+        if key == "Function Name":
+            cur = out.setdefault(val, {})
+        elif cur is not None:
+            cur[key.split(" [")[0]] = int(val) if val.lstrip("-").isdigit() else val
+    return out
+
+
+def _compile(src: str):
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
-    return obj
+    return obj, _resources(r.stderr)
 
 
 def build(verbose: bool = False) -> str:
@@ -44,13 +64,19 @@ def build(verbose: bool = False) -> str:
     os.makedirs(OBJ_DIR, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
+        done = list(ex.map(_compile, srcs))
+    objs = [o for o, _ in done]
+    res = {}
+    for _, r in done:
+        res.update(r)
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    with open(RESOURCES, "w") as f:
+        json.dump(res, f, indent=1, sort_keys=True)
     if verbose:
         print(f"built {LIB}")
     return LIB

@@ -243,6 +243,9 @@ constexpr int kGroupM = 4;
 // of bank conflicts.
 __device__ __forceinline__ int gemm_swz(int row) { return ((row >> 2) ^ (row >> 1)) & 3; }
 
+// RAW: the unfused arm's plain row store (compile-time, so the rotating
+// instantiation keeps its registers)
+template <bool RAW>
 __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(QkvArgs a, int n_mtiles, int n_ntiles) {
     constexpr int BK = kGBK, NS = kGNS;
     constexpr int kSlots = BK / 8;                      // 16-byte slots per staged row
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(QkvArgs a, int n_mtile
     const int mt = first_m + local % gm_sz, nt = local / gm_sz;
     const int row0 = mt * kGBM, col0 = nt * kGBN;
     if (tid < a.head_dim / 2) s_theta[tid] = pow((double)a.rope_base, -2.0 * tid / a.head_dim);
-    if (!a.raw_out) {
+    if (!RAW) {
         const int grow = min(row0 + tid, a.R - 1);      // blockDim.x == kGBM
         s_pos[tid] = a.pos[grow];
         s_slot[tid] = a.slot[grow];
@@ -367,7 +370,7 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(QkvArgs a, int n_mtile
     // ---- epilogue: rotate in registers (pairs are n-tiles t and t+4), bf16, via LDS to rows ----
     const int part = col0 / a.n_out;                    // 0 = Q, 1 = K, 2 = V (tiles never straddle parts)
     const int cpart = col0 % a.n_out + wn * 128;        // first column of this wave's head within the part
-    if (part < 2 && !a.raw_out) {
+    if (part < 2 && !RAW) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -410,7 +413,7 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(QkvArgs a, int n_mtile
         if (grow >= a.R) break;
         const u32x4 v = *(const u32x4*)(&tile[r * 128 + ((pc ^ (r & 15)) << 3)]);
         uint16_t* dst;
-        if (a.raw_out) {
+        if (RAW) {
             dst = a.raw_out + (int64_t)grow * 3 * a.n_out + part * a.n_out;
         } else if (part == 0) {
             dst = a.q_out + (int64_t)grow * a.n_out;
@@ -869,8 +872,12 @@ int qkv_launch(dllm_dtype dt, int n_rows, int d_model, int n_heads, int head_dim
     if (p.kind == kGemm256) {
         const int64_t tiles = (int64_t)p.n_mtiles * p.n_ntiles;
         DLLM_CHECK_SUP(tiles < (1ll << 31));
-        hipLaunchKernelGGL(qkv_gemm_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, a,
-                           p.n_mtiles, p.n_ntiles);
+        if (a.raw_out)
+            hipLaunchKernelGGL(qkv_gemm_kernel<true>, dim3((unsigned)tiles), dim3(256), 0, stream, a,
+                               p.n_mtiles, p.n_ntiles);
+        else
+            hipLaunchKernelGGL(qkv_gemm_kernel<false>, dim3((unsigned)tiles), dim3(256), 0, stream, a,
+                               p.n_mtiles, p.n_ntiles);
     } else if (p.kind == kSkinny) {
         // pairs per workgroup: the most (up to 24) that still leaves >= 256 workgroups
         const int n_pairs = 3 * n_out / 2;
