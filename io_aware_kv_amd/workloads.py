@@ -32,6 +32,10 @@ Seeds: numpy PCG64 seeded with [1000 * workload_id + stream, ...]; streams are
 1 = weights (per layer), 2 = x (per step and layer), 3 = pool permutation,
 4 = decode positions (new / search rows), 5 = sequence lengths and progress,
 6 = planted heavy-hitter positions.
+Decode-side workloads (logits rows of masked window positions, width VOCAB)
+seed PCG64 with [7000 + seed, vocab] for the row structure and [7100 + seed,
+vocab] for host logits; device logits use torch's generator seeded from the
+same seed.
 """
 from __future__ import annotations
 
@@ -379,3 +383,77 @@ def seeded_tracked(wl: Workload, step: int) -> List[np.ndarray]:
         cand = np.flatnonzero(s.eligible(wl.n_cap))
         out.append(np.sort(r.choice(cand, size=min(wl.shape.top_k, len(cand)), replace=False)).astype(np.int32))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Decode-side inputs: one logits row per masked window position of a step.
+# ---------------------------------------------------------------------------
+
+# Assumed LM-head width.  The pages give no vocabulary size, so the decode-side
+# workloads take a round 128 Ki tokens; every kernel takes the width as an
+# argument.
+VOCAB = 131072
+
+
+@dataclass
+class DecodeRows:
+    cu: np.ndarray        # int32 [n_seq + 1]: rows of sequence b are cu[b] .. cu[b+1]-1
+    peak_tok: np.ndarray  # int32 [R]: token given the planted peak
+    peak_val: np.ndarray  # float32 [R]: height of the planted peak (before bf16 rounding)
+    twin_tok: np.ndarray  # int32 [R]: a second token given the same height, or -1
+    draft: np.ndarray     # int32 [R]: draft-view token of the row (Flash-Verify input)
+
+
+def decode_rows(seed: int, lens, vocab: int, twin_frac: float = 0.0, agree: float = 0.85) -> DecodeRows:
+    """Row structure of a decode-side workload: per row a planted peak whose
+    height spreads the softmax maximum over roughly 0.1 .. 0.99 for N(0,1)
+    background logits (ln(vocab) + 1/2 is where the peak equals the background
+    mass), optionally a twin peak of the same height at a random other token,
+    and a draft token that equals the peak token with probability `agree`."""
+    r = np.random.Generator(np.random.PCG64([7000 + int(seed), int(vocab)]))
+    lens = np.asarray(lens, dtype=np.int64)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    R = int(cu[-1])
+    peak_tok = r.integers(0, vocab, size=R).astype(np.int32)
+    base = np.log(vocab) + 0.5
+    peak_val = (base + r.uniform(-2.5, 5.5, size=R)).astype(np.float32)
+    twin_tok = np.full(R, -1, dtype=np.int32)
+    if vocab > 1:
+        pick = r.random(R) < twin_frac
+        other = (peak_tok + r.integers(1, vocab, size=R)) % vocab
+        twin_tok[pick] = other[pick]
+    draft = np.where(r.random(R) < agree, peak_tok, r.integers(0, vocab, size=R)).astype(np.int32)
+    return DecodeRows(cu=cu, peak_tok=peak_tok, peak_val=peak_val, twin_tok=twin_tok, draft=draft)
+
+
+def _plant(z: np.ndarray, rows: DecodeRows) -> None:
+    ar = np.arange(len(rows.peak_tok))
+    z[ar, rows.peak_tok] = rows.peak_val
+    t = rows.twin_tok >= 0
+    z[ar[t], rows.twin_tok[t]] = rows.peak_val[t]
+
+
+def decode_logits_host(seed: int, rows: DecodeRows, vocab: int, dtype: str = "bf16") -> np.ndarray:
+    """[R, vocab] logits: N(0,1) background drawn in fp32 with the planted peaks,
+    then rounded once to bf16 (returned as uint16 bit patterns) or kept fp32."""
+    r = np.random.Generator(np.random.PCG64([7100 + int(seed), int(vocab)]))
+    z = r.standard_normal((len(rows.peak_tok), vocab), dtype=np.float32)
+    _plant(z, rows)
+    return round_bf16_bits(z) if dtype == "bf16" else z
+
+
+def decode_logits_device(seed: int, rows: DecodeRows, vocab: int, device):
+    """The same structure drawn on the device (torch's seeded generator) for
+    full-size workloads: bf16 [R, vocab]."""
+    import torch
+    R = len(rows.peak_tok)
+    t = device_normal_bf16((R, vocab), 1.0, 7200 * 4096 + int(seed), device)
+    ar = torch.arange(R, device=device)
+    t[ar, torch.from_numpy(rows.peak_tok.astype(np.int64)).to(device)] = \
+        torch.from_numpy(rows.peak_val).to(device).to(torch.bfloat16)
+    tw = np.flatnonzero(rows.twin_tok >= 0)
+    if len(tw):
+        twi = torch.from_numpy(tw.astype(np.int64)).to(device)
+        t[twi, torch.from_numpy(rows.twin_tok[tw].astype(np.int64)).to(device)] = \
+            torch.from_numpy(rows.peak_val[tw]).to(device).to(torch.bfloat16)
+    return t

@@ -1,4 +1,5 @@
-"""CPU oracle for the Flash-Cache per-layer denoising step.
+"""CPU oracle for the Flash-Cache per-layer denoising step and the decode-side
+reductions that follow it.
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or run
 anything in this package: only the test suite, the smoke check of the graft
@@ -22,3 +23,4 @@ from .flashcache import (  # noqa: F401
     topk,
     layer_step,
 )
+from .decode import confidence_argmax, confidence_commit, verify_accept  # noqa: F401
