@@ -8,6 +8,8 @@
  *         研究动机 (motivation), 技术新颖性 (novelty).
  *   [AIP] "Flash-dLLM 是什麼？擴散語言模型推論快 11 倍" (aiposthub explainer):
  *         Flash-Cache, selective refresh and Flash-Verify sections.
+ *   [FST] Fast-dLLM article (senqingzn.com), section 并行解碼新策略 (confidence-aware
+ *         parallel decoding).
  *
  * One layer of one denoising step is
  *     dllm_map_slots            logical position -> flat cache row of each query row
@@ -16,6 +18,8 @@
  * and after the last layer of the step
  *     dllm_topk_tracked         next step's tracked positions
  * dllm_build_block_table sets up (and validates) the page table once.
+ * Decode side (after the model's head): dllm_decode_commit / dllm_decode_verify,
+ * or their pieces dllm_confidence_argmax, dllm_confidence_commit, dllm_verify_accept.
  *
  * Conventions shared by every entry point:
  *   - Ownership: the caller allocates and owns every buffer; the library never
@@ -254,6 +258,71 @@ int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_heads, int 
 int dllm_topk_tracked(int n_seq, int n_heads, int n_cap, int k, float* mass,
                       const uint8_t* eligible, int32_t* idx, float* val, int32_t* count,
                       int clear_mass, hipStream_t stream);
+
+/*
+ * Decode side, after the last layer of a step: one logits row per masked window
+ * position (or per search position of a verify step).
+ *
+ * [FD] 方法步骤详情 step 2: the confidence of a position is the largest
+ * probability of its predicted distribution, and positions whose confidence is
+ * at least epsilon (0.9 in the pages) are decoded; [FST] = Fast-dLLM article,
+ * 并行解碼新策略: a sequence where no position reaches epsilon decodes its most
+ * confident position.  [FD] 方法步骤详情 step 3 (Flash-Verify): draft tokens
+ * are accepted in position order while the draft equals the mask view's
+ * predicted token and the mask view's confidence is at least gamma (0.8 in the
+ * pages); the first position that fails ends acceptance for the sequence.
+ *
+ * Shared arguments:
+ *   logits   [n_rows, row_stride] of dt (DLLM_BF16 or DLLM_F32); the first
+ *            vocab entries of each row are read, which must be finite
+ *   cu_rows  device int32[n_seq+1]: rows cu_rows[b] .. cu_rows[b+1]-1 belong
+ *            to sequence b, in position order.  A malformed range (decreasing,
+ *            or outside 0..n_rows) is clipped to 0..n_rows and, if still
+ *            decreasing, treated as empty: no row outside 0..n_rows is touched.
+ *            A sequence longer than 2048 rows gets count -1 and no flags.
+ *   token    int32[n_rows]: the argmax token of each row (lowest id on ties)
+ *   conf     float[n_rows]: its softmax probability, 1 / sum_x exp(l_x - max l),
+ *            accumulated in fp32
+ * Thresholds compare the fp32 confidence with the float threshold (>=).
+ * Ties of the forced decode go to the lowest row.
+ * The logits calls need workspace of dllm_confidence_workspace(n_rows, vocab)
+ * bytes (16-byte aligned; a function of the two sizes only).
+ * Errors: INVALID_ARG for null pointers, negative sizes, row_stride < vocab, a
+ * dtype other than the two, or a short workspace; UNSUPPORTED when the launch
+ * would exceed the grid limit.  Asynchronous.
+ */
+size_t dllm_confidence_workspace(int n_rows, int vocab);
+
+/* Per row: token and conf. */
+int dllm_confidence_argmax(dllm_dtype dt, int n_rows, int vocab, const void* logits, int64_t row_stride,
+                           int32_t* token, float* conf, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* Threshold rule on given confidences: commit uint8[n_rows] out (1 = decode
+ * the row this step), n_commit int32[n_seq] out (rows committed per sequence;
+ * at least 1 for a non-empty sequence). */
+int dllm_confidence_commit(int n_seq, int n_rows, const int32_t* cu_rows, const float* conf, float eps,
+                           uint8_t* commit, int32_t* n_commit, hipStream_t stream);
+
+/* Verify scan on given predictions: draft int32[n_rows] (the draft view's
+ * tokens), token/conf of the mask view; accept uint8[n_rows] out, n_accept
+ * int32[n_seq] out (length of the accepted prefix of each sequence). */
+int dllm_verify_accept(int n_seq, int n_rows, const int32_t* cu_rows, const int32_t* draft,
+                       const int32_t* token, const float* conf, float gamma, uint8_t* accept,
+                       int32_t* n_accept, hipStream_t stream);
+
+/* Logits -> token, conf and the threshold rule in two launches. */
+int dllm_decode_commit(dllm_dtype dt, int n_seq, int n_rows, const int32_t* cu_rows, int vocab,
+                       const void* logits, int64_t row_stride, float eps, int32_t* token, float* conf,
+                       uint8_t* commit, int32_t* n_commit, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* Mask-view logits -> token, conf and the verify scan in two launches. */
+int dllm_decode_verify(dllm_dtype dt, int n_seq, int n_rows, const int32_t* cu_rows, int vocab,
+                       const void* logits, int64_t row_stride, const int32_t* draft, float gamma,
+                       int32_t* token, float* conf, uint8_t* accept, int32_t* n_accept,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 
 #ifdef __cplusplus
 }

@@ -23,6 +23,8 @@ EXPORTS = (
     "dllm_qkv_rope_cachewrite_workspace", "dllm_qkv_rope_cachewrite", "dllm_qkv_rope_cachewrite_paged",
     "dllm_qkv_project", "dllm_rope_apply", "dllm_cache_write",
     "dllm_sched_attention_workspace", "dllm_sched_attention", "dllm_topk_tracked",
+    "dllm_confidence_workspace", "dllm_confidence_argmax", "dllm_confidence_commit", "dllm_verify_accept",
+    "dllm_decode_commit", "dllm_decode_verify",
 )
 
 
@@ -66,9 +68,19 @@ def load() -> ctypes.CDLL:
                                          _i64, _vp, _i32, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _i32,
                                          _vp, _vp, _sz, _vp]
     lib.dllm_topk_tracked.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp]
+    lib.dllm_confidence_workspace.argtypes = [_i32, _i32]
+    lib.dllm_confidence_workspace.restype = _sz
+    lib.dllm_confidence_argmax.argtypes = [_i32, _i32, _i32, _vp, _i64, _vp, _vp, _vp, _sz, _vp]
+    lib.dllm_confidence_commit.argtypes = [_i32, _i32, _vp, _vp, _f32, _vp, _vp, _vp]
+    lib.dllm_verify_accept.argtypes = [_i32, _i32, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp]
+    lib.dllm_decode_commit.argtypes = [_i32, _i32, _i32, _vp, _i32, _vp, _i64, _f32, _vp, _vp, _vp, _vp,
+                                       _vp, _sz, _vp]
+    lib.dllm_decode_verify.argtypes = [_i32, _i32, _i32, _vp, _i32, _vp, _i64, _vp, _f32, _vp, _vp, _vp,
+                                       _vp, _vp, _sz, _vp]
     for name in ("dllm_build_block_table", "dllm_map_slots", "dllm_qkv_rope_cachewrite",
                  "dllm_qkv_rope_cachewrite_paged", "dllm_qkv_project", "dllm_rope_apply", "dllm_cache_write",
-                 "dllm_sched_attention", "dllm_topk_tracked"):
+                 "dllm_sched_attention", "dllm_topk_tracked", "dllm_confidence_argmax", "dllm_confidence_commit",
+                 "dllm_verify_accept", "dllm_decode_commit", "dllm_decode_verify"):
         getattr(lib, name).restype = _i32
     _lib = lib
     return lib
@@ -230,3 +242,55 @@ def pack_mask(visible: Sequence[np.ndarray]) -> Tuple[np.ndarray, np.ndarray]:
         offs.append(total)
         total += rows * w
     return np.concatenate(words).astype(np.uint32), np.asarray(offs, dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# Decode side: logits rows [R, >= vocab] (bf16 or fp32, rows may be strided).
+
+def confidence_workspace(n_rows: int, vocab: int) -> int:
+    return int(load().dllm_confidence_workspace(n_rows, vocab))
+
+
+def _logits_args(logits, vocab: Optional[int]):
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be 2-d with unit column stride")
+    v = logits.shape[1] if vocab is None else int(vocab)
+    return dtype_code(logits), logits.shape[0], v, logits.stride(0)
+
+
+def confidence_argmax(logits, token, conf, workspace, vocab: Optional[int] = None, stream=None) -> None:
+    """Per row: argmax token (lowest id on ties) and max softmax probability."""
+    dt, R, V, stride = _logits_args(logits, vocab)
+    _check("dllm_confidence_argmax", load().dllm_confidence_argmax(
+        dt, R, V, _ptr(logits), stride, _ptr(token), _ptr(conf), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def confidence_commit(cu_rows, conf, eps: float, commit, n_commit, stream=None) -> None:
+    _check("dllm_confidence_commit", load().dllm_confidence_commit(
+        cu_rows.numel() - 1, conf.numel(), _ptr(cu_rows), _ptr(conf), float(eps), _ptr(commit), _ptr(n_commit),
+        _stream(stream)))
+
+
+def verify_accept(cu_rows, draft, token, conf, gamma: float, accept, n_accept, stream=None) -> None:
+    _check("dllm_verify_accept", load().dllm_verify_accept(
+        cu_rows.numel() - 1, conf.numel(), _ptr(cu_rows), _ptr(draft), _ptr(token), _ptr(conf), float(gamma),
+        _ptr(accept), _ptr(n_accept), _stream(stream)))
+
+
+def decode_commit(logits, cu_rows, eps: float, token, conf, commit, n_commit, workspace,
+                  vocab: Optional[int] = None, stream=None) -> None:
+    dt, R, V, stride = _logits_args(logits, vocab)
+    _check("dllm_decode_commit", load().dllm_decode_commit(
+        dt, cu_rows.numel() - 1, R, _ptr(cu_rows), V, _ptr(logits), stride, float(eps), _ptr(token), _ptr(conf),
+        _ptr(commit), _ptr(n_commit), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def decode_verify(logits, cu_rows, draft, gamma: float, token, conf, accept, n_accept, workspace,
+                  vocab: Optional[int] = None, stream=None) -> None:
+    dt, R, V, stride = _logits_args(logits, vocab)
+    _check("dllm_decode_verify", load().dllm_decode_verify(
+        dt, cu_rows.numel() - 1, R, _ptr(cu_rows), V, _ptr(logits), stride, _ptr(draft), float(gamma),
+        _ptr(token), _ptr(conf), _ptr(accept), _ptr(n_accept), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))

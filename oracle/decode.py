@@ -12,7 +12,8 @@ Citation keys (as in flashcache.py):
         and the mask-view confidence is at least gamma = 0.8; the first failure
         stops acceptance); 前置知识 (the confidence is the maximum of the model's
         predicted distribution at the position).
-  [FST] Fast-dLLM article, 并行解碼新策略 (confidence-aware parallel decoding):
+  [FST] Fast-dLLM article (senqingzn.com), 并行解碼新策略 (confidence-aware
+        parallel decoding):
         when no position reaches the threshold, the most confident one is
         decoded anyway, so every step makes progress.
 

@@ -129,6 +129,29 @@ def test_kernel_entry_points_reject_bad_shapes(lib):
     assert t(1, 32, 512, 32, None, fake, fake, fake, fake, 0, None) == -1
     assert lib.dllm_map_slots(0, 8, 16, 4, 4, fake, fake, fake, fake, None) == -1
 
+    # decode side: sizes, dtype, stride, pointers and the workspace size are
+    # checked before any launch
+    c = lib.dllm_confidence_argmax
+    assert c(1, -1, 1000, fake, 1000, fake, fake, fake, 1 << 20, None) == -1
+    assert c(1, 4, 0, fake, 1000, fake, fake, fake, 1 << 20, None) == -1           # empty vocabulary
+    assert c(1, 4, 1000, fake, 999, fake, fake, fake, 1 << 20, None) == -1         # stride < vocab
+    assert c(5, 4, 1000, fake, 1000, fake, fake, fake, 1 << 20, None) == -1         # dtype
+    assert c(1, 4, 1000, None, 1000, fake, fake, fake, 1 << 20, None) == -1         # null logits
+    assert c(1, 4, 1000, fake, 1000, None, fake, fake, 1 << 20, None) == -1         # null token
+    assert c(1, 4, 1000, fake, 1000, fake, fake, fake, 16, None) == -1              # short workspace
+    assert c(1, 4, 1000, fake, 1000, fake, fake, None, 1 << 20, None) == -1         # no workspace
+    assert c(1, 0, 1000, None, 1000, None, None, None, 0, None) == 0                # empty: nothing to do
+    dc = lib.dllm_decode_commit
+    assert dc(1, 1, 4, None, 1000, fake, 1000, 0.9, fake, fake, fake, fake, fake, 1 << 20, None) == -1
+    assert dc(1, -1, 4, fake, 1000, fake, 1000, 0.9, fake, fake, fake, fake, fake, 1 << 20, None) == -1
+    assert dc(1, 0, 4, fake, 1000, fake, 1000, 0.9, fake, fake, fake, fake, fake, 1 << 20, None) == 0
+    dv = lib.dllm_decode_verify
+    assert dv(1, 1, 4, fake, 1000, fake, 1000, None, 0.8, fake, fake, fake, fake, fake, 1 << 20, None) == -1
+    assert dv(0, 1, 4, fake, 1000, fake, 999, fake, 0.8, fake, fake, fake, fake, fake, 1 << 20, None) == -1
+    assert lib.dllm_confidence_commit(1, 4, None, fake, 0.9, fake, fake, None) == -1
+    assert lib.dllm_confidence_commit(0, 4, None, None, 0.9, None, None, None) == 0
+    assert lib.dllm_verify_accept(1, 4, fake, fake, None, fake, 0.8, fake, fake, None) == -1
+
 
 def test_workspace_queries(lib):
     # the projection never needs scratch; attention needs it only when keys are
@@ -143,6 +166,16 @@ def test_workspace_queries(lib):
     small = w(1, 1, 72, 32, 128, 512, 512)                   # batch 1: keys split
     assert small > 0 and small % (128 * 130 * 4) == 0
     assert small == w(1, 1, 72, 32, 128, 512, 512)
+
+
+def test_confidence_workspace_is_one_partial_per_row_and_split(lib):
+    w = lib.dllm_confidence_workspace
+    assert w(0, 1000) == 0 and w(4, 0) == 0
+    assert w(1024, 131072) == 1024 * 16                       # many rows: one workgroup per row
+    assert w(32, 131072) == 32 * 16 * 16                       # few rows: rows split 16 ways
+    assert w(1, 1000) == 16                                    # narrow rows are never split
+    for R, V in ((3, 4099), (40, 262147), (7, 65539)):
+        assert w(R, V) % (16 * R) == 0 and w(R, V) // (16 * R) <= 64
 
 
 def test_pack_mask_layout():
