@@ -45,6 +45,8 @@ def parse():
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--no-decode", action="store_true",
+                   help="skip the decode-side reductions (logits -> confidence, threshold rule, verify scan)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="also run a plain device copy of this size (counter calibration)")
     return p.parse_args()
@@ -288,6 +290,11 @@ def main():
             b_.copy_(a)
         torch.cuda.synchronize()
 
+    # ---- decode side (after the model head), timed on its own ----
+    decode = None
+    if not args.no_decode and not args.no_graph:
+        decode = bench_decode(args, dev)
+
     # ---- CPU baseline: the oracle on host cores, bounded sample ----
     cpu = None
     if not args.no_cpu_baseline:
@@ -321,9 +328,75 @@ def main():
         "unfused_arm": None if unfused_ms is None else {
             "ms_per_step": unfused_ms, "fused_speedup": unfused_ms / step_ms,
             "note": "slot mapping, projection to memory, rotary, cache write as separate launches; same attention and top-k"},
+        "decode_side": decode,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_decode(args, dev):
+    """Decode-side reductions over one logits row per masked window position,
+    at the assumed LM-head width: batch 1 (32 rows) and batch 32 (32 x 32
+    rows).  Each call is the two-launch logits pass + decision; calls run back
+    to back in a captured graph over enough distinct logits copies (>= 1 GiB)
+    that the Infinity Cache cannot serve them.  Algorithmic bytes per call:
+    the logits (R x V bf16) plus the per-row outputs."""
+    import numpy as np
+    import torch
+    from io_aware_kv_amd import dllm
+    from io_aware_kv_amd import workloads as W
+    V = W.VOCAB
+    out = {"vocab_assumed": V, "eps": 0.9, "gamma": 0.8}
+    stream = torch.cuda.current_stream()
+    for name, lens in (("batch1", [32]), ("batch32", [32] * 32)):
+        rows = W.decode_rows(21, lens, V, twin_frac=0.05)
+        R = int(rows.cu[-1])
+        per = R * V * 2
+        copies = max(2, int(np.ceil((1 << 30) / per)))
+        L = [W.decode_logits_device(21 + c, rows, V, dev) for c in range(copies)]
+        cu = torch.from_numpy(rows.cu).to(dev)
+        draft = torch.from_numpy(rows.draft).to(dev)
+        tok = torch.empty(R, dtype=torch.int32, device=dev)
+        conf = torch.empty(R, dtype=torch.float32, device=dev)
+        flag = torch.empty(R, dtype=torch.uint8, device=dev)
+        cnt = torch.empty(len(lens), dtype=torch.int32, device=dev)
+        ws = torch.empty(dllm.confidence_workspace(R, V) // 4 + 4, dtype=torch.float32, device=dev)
+        res = {"rows": R, "sequences": len(lens), "logits_bytes": per, "rotated_copies": copies}
+        for kind in ("commit", "verify"):
+            def call(c):
+                if kind == "commit":
+                    dllm.decode_commit(L[c], cu, 0.9, tok, conf, flag, cnt, ws)
+                else:
+                    dllm.decode_verify(L[c], cu, draft, 0.8, tok, conf, flag, cnt, ws)
+            call(0)
+            torch.cuda.synchronize()
+            cs = torch.cuda.Stream()
+            cs.wait_stream(stream)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(cs):
+                with torch.cuda.graph(g, stream=cs):
+                    for c in range(copies):
+                        call(c)
+            stream.wait_stream(cs)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            reps = max(2, min(50, args.steps * 4 // copies))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / (reps * copies) * 1e3
+            alg = per + R * (4 + 4 + 1) + len(lens) * 4 + (R * 4 if kind == "verify" else 0)
+            gbs = alg / (us * 1e-6) / 1e9
+            res[kind] = {"us_per_call": us, "alg_bytes": alg, "achieved_GBs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                         "rows_per_s": R / (us * 1e-6)}
+        out[name] = res
+        del L
+        torch.cuda.synchronize()
+    return out
 
 
 def bench_layers(args, dev):

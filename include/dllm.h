@@ -279,7 +279,6 @@ int dllm_topk_tracked(int n_seq, int n_heads, int n_cap, int k, float* mass,
  *            to sequence b, in position order.  A malformed range (decreasing,
  *            or outside 0..n_rows) is clipped to 0..n_rows and, if still
  *            decreasing, treated as empty: no row outside 0..n_rows is touched.
- *            A sequence longer than 2048 rows gets count -1 and no flags.
  *   token    int32[n_rows]: the argmax token of each row (lowest id on ties)
  *   conf     float[n_rows]: its softmax probability, 1 / sum_x exp(l_x - max l),
  *            accumulated in fp32

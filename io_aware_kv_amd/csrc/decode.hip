@@ -20,10 +20,10 @@
 //                        argmax, sum of exp(l - max)) per lane, merged over the
 //                        workgroup into one partial.  Few rows get split
 //                        across several workgroups so the chip fills.
-//   decide_kernel        merges a row's partials in split order (so results
+//   decide_kernel        merges a row's partials in a fixed tree (so results
 //                        do not depend on scheduling) into token and
 //                        confidence = 1 / sum, and applies the per-sequence
-//                        rule: one workgroup per sequence.
+//                        rule: one workgroup per sequence, 16 lanes per row.
 // Ties: the lowest token id wins inside a row, the lowest row for the forced
 // decode.  exp is the hardware base-2 exponential of a pre-scaled argument.
 #include <math.h>
@@ -41,8 +41,6 @@ constexpr int kChunkQuantum = 2048;   // split boundaries are multiples of this 
 constexpr int kMinChunk = 8192;       // a split streams at least 16 KB of bf16 logits
 constexpr int kTargetBlocks = 1024;   // four workgroups per compute unit
 constexpr int kMaxSplits = 64;
-constexpr int kRowsPerThread = 8;
-constexpr int kMaxSeqRows = kThr * kRowsPerThread;
 constexpr float kLog2e = 1.4426950408889634f;
 
 enum Mode { kConfOnly = 0, kCommit = 1, kVerify = 2 };
@@ -166,19 +164,38 @@ __global__ __launch_bounds__(kThr) void conf_partial_kernel(int vocab, int64_t s
     }
 }
 
-__device__ __forceinline__ void merged_row(const f32x4* __restrict__ part, int n_split, int r, int& tok, float& conf) {
-    // in split order, eight loads in flight at a time
-    const f32x4* pr = part + (int64_t)r * n_split;
-    Online a{-INFINITY, 0.f, 0x7fffffff};
-    for (int s0 = 0; s0 < n_split; s0 += 8) {
-        f32x4 v[8];
+// Rows are handled by groups of 16 lanes (16 groups per workgroup, kSlots
+// rows per group in flight): lane l of a group merges the row's partials
+// l, l+16, l+32, l+48 in that order, then the 16 lanes merge by xor-shuffles
+// 8, 4, 2, 1.  Every partial of kSlots rows is loaded in one round, and the
+// fixed merge tree keeps results independent of scheduling.
+constexpr int kGroup = 16;
+constexpr int kGroups = kThr / kGroup;
+constexpr int kSlots = 4;
+constexpr int kPerLane = kMaxSplits / kGroup;
+constexpr int kRowsPerPass = kGroups * kSlots;
+
+__device__ __forceinline__ void merge_rows(const f32x4* __restrict__ part, int n_split, const int* r, const bool* valid,
+                                           Online* out) {
+    const int sl = threadIdx.x & (kGroup - 1);
+    f32x4 v[kSlots][kPerLane];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = s0 + u < n_split ? pr[s0 + u] : f32x4{-INFINITY, 0.f, __int_as_float(0x7fffffff), 0.f};
+    for (int i = 0; i < kSlots; ++i)
 #pragma unroll
-        for (int u = 0; u < 8; ++u) merge(a, Online{v[u][0], v[u][1], __float_as_int(v[u][2])});
+        for (int u = 0; u < kPerLane; ++u) {
+            const int sp = sl + u * kGroup;
+            v[i][u] = valid[i] && sp < n_split ? part[(int64_t)r[i] * n_split + sp]
+                                               : f32x4{-INFINITY, 0.f, __int_as_float(0x7fffffff), 0.f};
+        }
+#pragma unroll
+    for (int i = 0; i < kSlots; ++i) {
+        Online a{v[i][0][0], v[i][0][1], __float_as_int(v[i][0][2])};
+#pragma unroll
+        for (int u = 1; u < kPerLane; ++u) merge(a, Online{v[i][u][0], v[i][u][1], __float_as_int(v[i][u][2])});
+#pragma unroll
+        for (int mask = kGroup / 2; mask >= 1; mask >>= 1) merge(a, shfl_xor(a, mask));
+        out[i] = a;
     }
-    tok = a.idx;
-    conf = 1.f / a.s;
 }
 
 // block-wide (count, best) reduction: sum of counts, the largest key with the
@@ -204,14 +221,14 @@ __device__ Best block_reduce(Best v) {
     __shared__ Best s_b[kWaves];
     const int t = threadIdx.x;
     if ((t & 63) == 0) s_b[t >> 6] = v;
-    __syncthreads();
+    lds_sync();
     Best a = s_b[0];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) better(a, s_b[w]);
     return a;
 }
 
-// MODE kConfOnly: grid over rows, token/conf from the partials.
+// MODE kConfOnly: kRowsPerPass rows per workgroup, token/conf from the partials.
 // MODE kCommit / kVerify: one workgroup per sequence.  With FROM_PART the
 // row's token and confidence come from the partials (and are written out);
 // otherwise they are read from token/conf.
@@ -220,23 +237,33 @@ __device__ Best block_reduce(Best v) {
 //   kVerify: flag[r] = 1 for the rows before the first row with
 //            token != draft or conf < thr; count[b] = their number.
 // A sequence whose row range is malformed (cu[b+1] < cu[b], or outside
-// 0..n_rows) is treated as empty; one longer than kMaxSeqRows gets count -1
-// and no flags.
+// 0..n_rows) is clipped to 0..n_rows and, if still decreasing, is empty.
+// Each flag is written once, after the sequence's rows are reduced: from
+// registers when the sequence fits one pass (kRowsPerPass rows), else in a
+// second pass that re-reads the confidences written in the first.
 template <int MODE, bool FROM_PART>
 __global__ __launch_bounds__(kThr) void decide_kernel(int n_rows, const int32_t* __restrict__ cu, const f32x4* __restrict__ part,
-                                                      int n_split, int32_t* __restrict__ token, float* __restrict__ conf,
+                                                      int n_split, int32_t* __restrict__ token, float* conf,
                                                       float thr, const int32_t* __restrict__ draft,
                                                       uint8_t* __restrict__ flag, int32_t* __restrict__ count) {
     const int t = threadIdx.x;
+    const int g = t / kGroup, sl = t % kGroup;
     if (MODE == kConfOnly) {
-        const int r = blockIdx.x * kThr + t;
-        if (r < n_rows) {
-            int tk;
-            float c;
-            merged_row(part, n_split, r, tk, c);
-            token[r] = tk;
-            conf[r] = c;
+        int r[kSlots];
+        bool valid[kSlots];
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i) {
+            r[i] = blockIdx.x * kRowsPerPass + i * kGroups + g;
+            valid[i] = r[i] < n_rows;
         }
+        Online a[kSlots];
+        merge_rows(part, n_split, r, valid, a);
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i)
+            if (valid[i] && sl == 0) {
+                token[r[i]] = a[i].idx;
+                conf[r[i]] = 1.f / a[i].s;
+            }
         return;
     }
     const int b = blockIdx.x;
@@ -244,57 +271,70 @@ __global__ __launch_bounds__(kThr) void decide_kernel(int n_rows, const int32_t*
     r0 = max(r0, 0);
     r1 = min(r1, n_rows);
     if (r1 < r0) r1 = r0;
-    if (r1 - r0 > kMaxSeqRows) {
-        if (t == 0) count[b] = -1;
-        return;
-    }
-    bool ok[kRowsPerThread];
     Best loc{0, -INFINITY, 0x7fffffff};
+    int r[kSlots] = {};
+    bool valid[kSlots] = {}, ok[kSlots] = {};   // an empty sequence writes no flag
+    for (int base = r0; base < r1; base += kRowsPerPass) {
 #pragma unroll
-    for (int i = 0; i < kRowsPerThread; ++i) {
-        const int r = r0 + i * kThr + t;
-        ok[i] = false;
-        if (r < r1) {
-            int tk;
-            float c;
-            if (FROM_PART) {
-                merged_row(part, n_split, r, tk, c);
-                token[r] = tk;
-                conf[r] = c;
-            } else {
-                c = conf[r];
-                tk = MODE == kVerify ? token[r] : 0;
-            }
-            if (MODE == kCommit) {
-                ok[i] = c >= thr;
-                loc.cnt += ok[i];
-                if (c > loc.key) {          // rows visited in increasing order: strict keeps the lowest
-                    loc.key = c;
-                    loc.row = r;
+        for (int i = 0; i < kSlots; ++i) {
+            r[i] = base + i * kGroups + g;
+            valid[i] = r[i] < r1;
+        }
+        int tk[kSlots];
+        float c[kSlots];
+        if (FROM_PART) {
+            Online a[kSlots];
+            merge_rows(part, n_split, r, valid, a);
+#pragma unroll
+            for (int i = 0; i < kSlots; ++i) {
+                tk[i] = a[i].idx;
+                c[i] = 1.f / a[i].s;
+                if (valid[i] && sl == 0) {
+                    token[r[i]] = tk[i];
+                    conf[r[i]] = c[i];
                 }
-            } else {
-                ok[i] = tk == draft[r] && c >= thr;
-                if (!ok[i] && r < loc.row) loc.row = r;   // first failing row
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kSlots; ++i) {
+                c[i] = valid[i] && sl == 0 ? conf[r[i]] : 0.f;
+                tk[i] = MODE == kVerify && valid[i] && sl == 0 ? token[r[i]] : 0;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i) {
+            ok[i] = false;
+            if (!valid[i] || sl != 0) continue;
+            if (MODE == kCommit) {
+                ok[i] = c[i] >= thr;
+                loc.cnt += ok[i];
+                // rows of one lane come in increasing order: strict keeps the lowest
+                if (c[i] > loc.key) {
+                    loc.key = c[i];
+                    loc.row = r[i];
+                }
+            } else if (!(tk[i] == draft[r[i]] && c[i] >= thr)) {
+                loc.row = min(loc.row, r[i]);   // first failing row
             }
         }
     }
-    if (MODE == kVerify) loc.key = 0.f;     // equal keys: the reduction keeps the lowest row, the first failure
-    Best tot = block_reduce(loc);
+    if (MODE == kVerify) loc.key = 0.f;         // equal keys: the reduction keeps the lowest row
+    const Best tot = block_reduce(loc);
+    const bool one_pass = r1 - r0 <= kRowsPerPass;
     if (MODE == kCommit) {
         const bool forced = tot.cnt == 0;
+        if (one_pass) {
 #pragma unroll
-        for (int i = 0; i < kRowsPerThread; ++i) {
-            const int r = r0 + i * kThr + t;
-            if (r < r1) flag[r] = forced ? (r == tot.row) : ok[i];
+            for (int i = 0; i < kSlots; ++i)
+                if (valid[i] && sl == 0) flag[r[i]] = forced ? (r[i] == tot.row) : ok[i];
+        } else {
+            __syncthreads();                    // the first pass's conf stores are visible
+            for (int q = r0 + t; q < r1; q += kThr) flag[q] = forced ? (q == tot.row) : (conf[q] >= thr);
         }
         if (t == 0) count[b] = forced ? (r1 > r0 ? 1 : 0) : tot.cnt;
     } else {
         const int first_fail = min(tot.row, r1);
-#pragma unroll
-        for (int i = 0; i < kRowsPerThread; ++i) {
-            const int r = r0 + i * kThr + t;
-            if (r < r1) flag[r] = r < first_fail;
-        }
+        for (int q = r0 + t; q < r1; q += kThr) flag[q] = q < first_fail;
         if (t == 0) count[b] = first_fail - r0;
     }
 }
@@ -374,7 +414,8 @@ extern "C" int dllm_confidence_argmax(dllm_dtype dt, int n_rows, int vocab, cons
     DLLM_CHECK_ARG(token && conf);
     const Plan pl = plan(n_rows, vocab);
     if ((rc = run_partials(dt, n_rows, vocab, logits, row_stride, pl, ws, ws_bytes, stream))) return rc;
-    hipLaunchKernelGGL((decide_kernel<kConfOnly, true>), dim3((n_rows + kThr - 1) / kThr), dim3(kThr), 0, stream,
+    hipLaunchKernelGGL((decide_kernel<kConfOnly, true>), dim3((n_rows + kRowsPerPass - 1) / kRowsPerPass), dim3(kThr), 0,
+                       stream,
                        n_rows, (const int32_t*)nullptr, (const f32x4*)ws, pl.n_split, token, conf, 0.f,
                        (const int32_t*)nullptr, (uint8_t*)nullptr, (int32_t*)nullptr);
     DLLM_CHECK_LAUNCH();

@@ -187,7 +187,8 @@ def test_decisions_on_given_confidences(gpu):
 
 def test_row_ranges_outside_the_rows_and_long_sequences(gpu):
     """Malformed ranges are clipped to the rows (nothing outside is touched);
-    a sequence longer than 2048 rows reports -1 and writes no flag."""
+    sequences longer than one pass of the decision launch (64 rows) and than
+    a workgroup (256 threads) decide like the oracle."""
     import torch
     from io_aware_kv_amd import dllm
     conf = torch.full((8,), 0.95, dtype=torch.float32, device=gpu)
@@ -199,15 +200,31 @@ def test_row_ranges_outside_the_rows_and_long_sequences(gpu):
     assert n.cpu().tolist() == [5, 0, 5]       # seq 1 is empty, seq 2 is clipped to rows 3..7
     assert f.cpu().tolist() == [1] * 8
 
-    R = 2049
-    conf = torch.full((R,), 0.5, dtype=torch.float32, device=gpu)
-    cu = _dev(np.array([0, R], dtype=np.int32), gpu)
+    lens = [5000, 65, 300, 1]
+    rows = W.decode_rows(17, lens, 2048, twin_frac=0.2)
+    R = int(rows.cu[-1])
+    rng = np.random.default_rng(17)
+    cf = rng.choice(np.array([0.3, 0.6, 0.85, 0.9, 0.95], dtype=np.float32), size=R)
+    cf[:5000] = np.minimum(cf[:5000], np.float32(0.85))          # seq 0: forced decode
+    cf[4321] = np.float32(0.89)                                    # its most confident row
+    tk = rows.peak_tok.copy()
+    cu = _dev(rows.cu, gpu)
     f = torch.full((R,), 7, dtype=torch.uint8, device=gpu)
-    n = torch.full((1,), -7, dtype=torch.int32, device=gpu)
-    dllm.confidence_commit(cu, conf, EPS, f, n)
+    n = torch.full((len(lens),), -7, dtype=torch.int32, device=gpu)
+    dllm.confidence_commit(cu, _dev(cf, gpu), EPS, f, n)
     torch.cuda.synchronize()
-    assert n.cpu().tolist() == [-1]
-    assert torch.all(f == 7)
+    commit, wn = O.confidence_commit(cf.astype(np.float64), rows.cu, F32_EPS)
+    assert np.array_equal(f.cpu().numpy().astype(bool), commit)
+    assert np.array_equal(n.cpu().numpy(), wn)
+    assert commit[4321] and wn[0] == 1
+    vf = np.where(np.arange(R) % 997 == 996, np.float32(0.5), np.float32(0.9)).astype(np.float32)
+    f.fill_(7)
+    n.fill_(-7)
+    dllm.verify_accept(cu, _dev(rows.draft, gpu), _dev(tk, gpu), _dev(vf, gpu), GAMMA, f, n)
+    torch.cuda.synchronize()
+    acc, an = O.verify_accept(rows.draft, tk, vf.astype(np.float64), rows.cu, F32_GAMMA)
+    assert np.array_equal(f.cpu().numpy().astype(bool), acc)
+    assert np.array_equal(n.cpu().numpy(), an)
 
 
 def test_empty_rows(gpu):
