@@ -236,6 +236,48 @@ def main():
         torch.cuda.synchronize()
         unfused_ms = u0.elapsed_time(u1) / K
 
+    # ---- block-granular caching steps over the same layer, caches and kernels:
+    # DualCache (the current block only) and the active window of PrefixCache /
+    # FreeCache (the current block and every later block) ----
+    block = None
+    if not args.no_graph:
+        block = {}
+        for mode in W.BLOCK_CACHE_MODES:
+            rws = W.block_cache_rows(wl, mode)
+            stm = run.upload_step(rws)
+            xm = run.to_device_array(W.activations(wl, rws, 2))
+            Xm = [xm] + [xm.clone() for _ in range(copies - 1)]
+
+            def mstep(c, stm=stm, Xm=Xm):
+                dllm.qkv_rope_cachewrite_paged(Xm[c], Ws[c], stm.pos, stm.cu_q, stm.logical, run.page_table,
+                                               wl.max_pages, stm.slot, stm.q, Ks[c], Vs[c], sh.n_heads,
+                                               sh.head_dim, sh.rope_base, stm.ws_qkv)
+                dllm.sched_attention(stm.q, stm.cu_q, Ks[c], Vs[c], run.page_table, wl.max_pages, stm.kv_len,
+                                     stm.o, stm.ws_attn, sh.n_heads, sh.head_dim, stm.max_kv, n_cap=run.n_cap)
+            mg = []
+            with torch.cuda.stream(cs):
+                for c in range(copies):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=cs):
+                        mstep(c)
+                    mg.append(g)
+            stream.wait_stream(cs)
+            torch.cuda.synchronize()
+            for i in range(args.warmup):
+                mg[i % copies].replay()
+            torch.cuda.synchronize()
+            m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            m0.record(stream)
+            for i in range(K):
+                mg[i % copies].replay()
+            m1.record(stream)
+            torch.cuda.synchronize()
+            mms = m0.elapsed_time(m1) / K
+            block[mode] = {"rows": rws.n_rows, "kv_len": [int(k) for k in rws.kv_len], "us_per_step": mms * 1e3,
+                           "tokens_per_s": rws.n_rows / (mms * 1e-3)}
+            del mg, Xm, xm, stm
+        torch.cuda.synchronize()
+
     step_ms = graph_ms if graph_ms is not None else plain_ms
     value = R / (step_ms * 1e-3)
 
@@ -328,6 +370,7 @@ def main():
         "unfused_arm": None if unfused_ms is None else {
             "ms_per_step": unfused_ms, "fused_speedup": unfused_ms / step_ms,
             "note": "slot mapping, projection to memory, rotary, cache write as separate launches; same attention and top-k"},
+        "block_cache_steps": block,
         "decode_side": decode,
         "cpu_baseline": cpu,
     }
@@ -419,6 +462,7 @@ def bench_layers(args, dev):
 
     def step(kind, ev=None, unfused=False):
         st = sts[kind]
+        mass = kind in ("full", "cache")      # block-cache steps have no formula-(2) rows
         run.map_slots(st)
         for l in range(L):
             if ev is not None:
@@ -429,23 +473,28 @@ def bench_layers(args, dev):
                 run.cache_update(st, xs[kind][l], Ws[l], l)
             if ev is not None:
                 ev[l][1].record()
-            run.attention(st, l)
+            run.attention(st, l, with_mass=mass)
             if ev is not None:
                 ev[l][2].record()
-        run.topk(clear_mass=True)
+        if mass:
+            run.topk(clear_mass=True)
 
     step("full")
     idx = run.top_idx.cpu().numpy()
     rows["cache"] = W.config_step_rows(wl, [idx[b][idx[b] >= 0] for b in range(wl.n_seq)])
     sts["cache"] = run.upload_step(rows["cache"])
     xs["cache"] = [W.device_activations(wl, rows["cache"], 1, l, dev) for l in range(L)]
+    for mode in W.BLOCK_CACHE_MODES:
+        rows[mode] = W.block_cache_rows(wl, mode)
+        sts[mode] = run.upload_step(rows[mode])
+        xs[mode] = [W.device_activations(wl, rows[mode], 2, l, dev) for l in range(L)]
     for _ in range(max(1, args.warmup // 10)):
         step("cache")
         step("full")
     torch.cuda.synchronize()
     K = max(2, min(args.steps, 10))
     res = {}
-    for kind in ("full", "cache"):
+    for kind in ("full", "cache") + W.BLOCK_CACHE_MODES:
         evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(L)] for _ in range(K)]
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0.record()
@@ -490,8 +539,9 @@ def bench_layers(args, dev):
                "fused_speedup_per_layer": ums / res["cache"]["ms_per_step"],
                "fused_update_speedup": float(np.mean([evs[i][l][0].elapsed_time(evs[i][l][1]) for i in range(K) for l in range(L)])) * 1e3 / res["cache"]["qkv_us"]}
     eprint(f"[bench] llada_b32 cache, unfused arm: {unfused}")
-    tot_rows = sum(res[k]["rows_per_layer"] for k in res)
-    tot_ms = sum(res[k]["ms_per_step"] for k in res)
+    tot_rows = sum(res[k]["rows_per_layer"] for k in ("full", "cache"))
+    tot_ms = sum(res[k]["ms_per_step"] for k in ("full", "cache"))
+    block = {k: res.pop(k) for k in W.BLOCK_CACHE_MODES}
     value = tot_rows / (tot_ms * 1e-3 / L)
     dom = res["full"]
     out = {
@@ -504,6 +554,7 @@ def bench_layers(args, dev):
                                "cache-phase (72 rows/seq) steps, top-32 once per step",
                    "layers": L, "batch": wl.n_seq, "parallelism": "single GPU", "timing": "stream launches"},
         "steps_detail": res,
+        "block_cache_steps": block,
         "unfused_arm_cache_phase": unfused,
         "roofline": {"bound": "mfma", "kernel": "qkv_rope_cachewrite (full refresh)",
                      "achieved": 2 * dom["rows_per_layer"] * sh.d_model * 3 * n / (dom["qkv_us"] * 1e-6) / 1e12,

@@ -141,7 +141,7 @@ class FlashCacheRunner:
                           self.top_cnt, clear_mass=clear_mass)
 
     def layer_step(self, st: StepDevice, x: torch.Tensor, w: torch.Tensor, layer: int = 0,
-                   fused_slots: bool = True, unfused: bool = False) -> None:
+                   fused_slots: bool = True, unfused: bool = False, with_mass: bool = True) -> None:
         """a0..a5 of one layer: slots and the fused cache update (one call, or
         the slot mapping as a call of its own; or the unfused three-launch arm),
         then attention + mass."""
@@ -153,4 +153,4 @@ class FlashCacheRunner:
         else:
             self.map_slots(st)
             self.cache_update(st, x, w, layer)
-        self.attention(st, layer)
+        self.attention(st, layer, with_mass=with_mass)

@@ -12,6 +12,8 @@ Citation keys used below:
   [FD]  "Flash-dLLM: IO-Aware KV Caching and Parallel Decoding for Fast,
         Memory-Efficient Diffusion LLMs" (paper summary page, paper.rainbus.top)
   [AIP] "Flash-dLLM 是什麼？擴散語言模型推論快 11 倍" (aiposthub explainer)
+  [FST] Fast-dLLM article (senqingzn.com): block-wise PrefixCache / DualCache
+  [FDLM] FlashDLM notes (papernotes.org): FreeCache
 
 Workloads (all synthetic, random-init; LLaDA-8B-shaped where stated):
   tiny_f32   1 layer, d_model 256, 4 heads x 64, RoPE base 1e4, fp32;
@@ -303,6 +305,37 @@ def config_step_rows(wl: Workload, tracked: List[np.ndarray]) -> StepRows:
     return StepRows(cu_q=np.array(cu, dtype=np.int32), logical=np.concatenate(logical),
                     pos=np.concatenate(pos), mass_count=np.array(mass, dtype=np.int32),
                     kv_len=np.array(kv, dtype=np.int32), visible=vis if has_mask else None)
+
+
+BLOCK_CACHE_MODES = ("dual", "active")
+
+
+def block_cache_rows(wl: Workload, mode: str) -> StepRows:
+    """Query rows of a block-granular caching step, over the same cache and
+    kernels as the Flash-Cache step (no formula-(2) rows, no verify mask).
+
+    "dual":   only the current block (the masked window) is queried and
+              written; every other position, the masked suffix included, is
+              read from the cache ([FST] block-wise DualCache).
+    "active": the current block and every later generation block (the active
+              window B_i..B_N) are queried and written; the prompt and the
+              finished blocks before the window are frozen in the cache
+              ([FST] PrefixCache, which recomputes the suffix; [FDLM] FreeCache,
+              which freezes blocks once they are fully decoded).
+    Keys are the whole context in both modes."""
+    if mode not in BLOCK_CACHE_MODES:
+        raise ValueError(mode)
+    cu = [0]
+    logical = []
+    for s in wl.seqs:
+        w0 = int(s.window[0])
+        lg = s.window if mode == "dual" else np.arange(w0, s.ctx)
+        logical.append(np.asarray(lg, dtype=np.int32))
+        cu.append(cu[-1] + len(lg))
+    lg = np.concatenate(logical)
+    return StepRows(cu_q=np.array(cu, dtype=np.int32), logical=lg, pos=lg.copy(),
+                    mass_count=np.zeros(wl.n_seq, dtype=np.int32),
+                    kv_len=np.array([s.ctx for s in wl.seqs], dtype=np.int32))
 
 
 def weights(wl: Workload, layer: int = 0) -> np.ndarray:
