@@ -211,12 +211,22 @@ __global__ __launch_bounds__(kThreads) void qkv_bf16_kernel(QkvArgs a) {
     }
 }
 
-// Full-refresh projection (large R): 256 x 256 output tiles, 4 waves each
-// owning a 128 x 128 sub-tile, i.e. 128 rows by one whole head of 128
-// columns.  The MFMA computes the transposed tile (W rows as its A operand),
-// so a lane's four accumulator values are four consecutive output columns of
-// one row: they pack into one 8-byte LDS write, and the rotate-half partner
-// (column c + 64) of each sits in the same lane four n-tiles further on.
+// Projection for R > 128 rows: BM x BN output tiles, four waves each owning
+// WM = 16 WMF rows by one whole head of 128 columns (WGM waves along the rows,
+// 4 / WGM along the columns).  The MFMA computes the transposed tile (W rows
+// as its A operand), so a lane's four accumulator values are four consecutive
+// output columns of one row: they pack into one 8-byte LDS write, and the
+// rotate-half partner (column c + 64) of each sits in the same lane four
+// n-tiles further on.
+//
+// Tile shapes (GemmCfg): 256 x 256 (one workgroup per compute unit, four
+// 32 KiB stages) for large R; 128 x 256, 64 x 256, 256 x 128 and 128 x 128 so
+// that mid-size R still spreads over every compute unit, each either alone on
+// its compute unit with a deep ring (OCC 1: up to 150 KiB of stages, so the
+// copies run 5 to 7 stages ahead of the MFMAs: a smaller tile has less MFMA
+// work per stage to hide a copy's latency behind) or two per compute unit
+// (OCC 2: at most 78 KiB each).  A wave's fragment reuse falls with its row
+// count (LDS bytes per MFMA grow as 1/WM + 1/128).
 //
 // Operands reach LDS through 16-byte direct-to-LDS loads (no register
 // staging), NS stages of BK = 32 deep.  A direct-to-LDS load writes lane i's
@@ -224,18 +234,42 @@ __global__ __launch_bounds__(kThreads) void qkv_bf16_kernel(QkvArgs a) {
 // fragment reads free of bank conflicts is applied on the source side: lane i
 // fetches the logical 16-byte slot that belongs at its physical place.
 //
-// Pipeline (one wave per SIMD, so every stall idles that SIMD's matrix
-// unit): the fragments of stage kt+1 are read from LDS while the 64 MFMAs of
-// stage kt run, and one of the wave's copy instructions for stage kt+NS is
-// issued after each group of 8 MFMAs rather than all at once, which would
-// fill the address queue and hold up the wave.  One barrier per stage both
-// publishes stage kt+1 and frees stage kt's buffer for the copy of kt+NS.
+// Pipeline: the fragments of stage kt+1 are read from LDS while the MFMAs of
+// stage kt run, and the wave's copy instructions for stage kt+NS are spread
+// over its groups of 8 MFMAs rather than issued at once, which would fill the
+// address queue and hold up the wave.  One barrier per stage both publishes
+// stage kt+1 and frees stage kt's buffer for the copy of kt+NS.
 //
 // Tiles are ordered in groups of 4 row tiles x all column tiles, column
-// major inside a group, so the 32 workgroups one XCD runs at a time cover
-// 4 x 8 tiles and share their x and W slices in that XCD's L2.
-constexpr int kGBM = 256, kGBN = 256, kGBK = 32, kGNS = 4;
+// major inside a group, so the workgroups one XCD runs at a time share their
+// x and W slices in that XCD's L2.
+constexpr int kGBK = 32;
 constexpr int kGroupM = 4;
+constexpr int kGemmLdsPair = 78 * 1024;   // per workgroup when two share a compute unit
+constexpr int kGemmLdsOne = 150 * 1024;   // ring of a workgroup alone on its compute unit
+constexpr int kGemmMaxStages = 8;
+
+template <int WMF, int WGM, int OCC>
+struct GemmCfg {
+    static constexpr int WM = 16 * WMF;               // rows per wave
+    static constexpr int BM = WGM * WM;
+    static constexpr int BN = (4 / WGM) * 128;
+    static constexpr int BK = kGBK;
+    static constexpr int kStage = (BM + BN) * BK;      // halfwords per stage
+    static constexpr int kInst = (BM + BN) / 16 / 4;   // 1 KiB copy instructions per wave per stage
+    static constexpr bool kBig = BM == 256 && BN == 256;
+    static constexpr int kOcc = OCC;
+    static constexpr int kRing = (OCC == 2 ? kGemmLdsPair : kGemmLdsOne) / (2 * kStage);
+    static constexpr int NS = kBig ? 4 : (kRing < kGemmMaxStages ? kRing : kGemmMaxStages);
+    static constexpr int kCopyPerGroup = (kInst + WMF - 1) / WMF;
+    static constexpr int kWPerGroup = 8 / WMF > 2 ? 8 / WMF : 2;
+    static_assert(WGM == 1 || WGM == 2 || WGM == 4, "four waves");
+    static_assert(NS * kStage >= 4 * WM * 128, "the epilogue reuses the stages as one WM x 128 tile per wave");
+    static_assert(NS >= 3, "copies at least two stages ahead");
+    static_assert(OCC == 1 || NS * kStage * 2 + 8 * BM + 512 <= kGemmLdsPair, "two workgroups per compute unit");
+    static_assert(!kBig || OCC == 1, "one 256 x 256 workgroup per compute unit");
+    static_assert((NS - 2) * kInst < 64, "wait counts");
+};
 
 // Physical 16-byte slot of logical slot 0 in a 64-byte staged row: any 16
 // consecutive rows read at one logical slot hit 16 distinct bank groups (and
@@ -243,24 +277,34 @@ constexpr int kGroupM = 4;
 // of bank conflicts.
 __device__ __forceinline__ int gemm_swz(int row) { return ((row >> 2) ^ (row >> 1)) & 3; }
 
+// wait until at most `ahead` (<= MAXA) stages of this wave's copies are still
+// in flight (s_waitcnt takes an immediate: one branch per count)
+template <int KI, int MAXA>
+__device__ __forceinline__ void wait_stages_ahead(int ahead) {
+    if (MAXA >= 6 && ahead >= 6) __builtin_amdgcn_s_waitcnt(waitcnt_imm(6 * KI, 0));
+    else if (MAXA >= 5 && ahead == 5) __builtin_amdgcn_s_waitcnt(waitcnt_imm(5 * KI, 0));
+    else if (MAXA >= 4 && ahead == 4) __builtin_amdgcn_s_waitcnt(waitcnt_imm(4 * KI, 0));
+    else if (MAXA >= 3 && ahead == 3) __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * KI, 0));
+    else if (ahead >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * KI, 0));
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_imm(KI, 0));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+}
+
 // RAW: the unfused arm's plain row store (compile-time, so the rotating
 // instantiation keeps its registers)
-template <bool RAW>
-__global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(QkvArgs a, int n_mtiles, int n_ntiles) {
-    constexpr int BK = kGBK, NS = kGNS;
+template <int WMF, int WGM, int OCC, bool RAW>
+__global__ __launch_bounds__(256, OCC) void qkv_gemm_kernel(QkvArgs a, int n_mtiles, int n_ntiles) {
+    using C = GemmCfg<WMF, WGM, OCC>;
+    constexpr int BM = C::BM, BK = C::BK, NS = C::NS, WM = C::WM, kInst = C::kInst, kStage = C::kStage;
     constexpr int kSlots = BK / 8;                      // 16-byte slots per staged row
     constexpr int kRowsPerInst = 64 / kSlots;           // rows one 1 KiB copy instruction covers
-    constexpr int kInst = (kGBM + kGBN) / kRowsPerInst / 4;   // copy instructions per wave per stage
-    constexpr int kStage = (kGBM + kGBN) * BK;          // halfwords per stage
-    static_assert(NS * kStage == 4 * 128 * 128, "the epilogue reuses the stages as four 128 x 128 tiles");
-    static_assert(NS >= 2 && NS <= 4 && kInst == 8 && 2 * kInst < 64, "wait counts below");
     __shared__ __attribute__((aligned(16))) uint16_t smem[NS * kStage];
     __shared__ double s_theta[64];
-    __shared__ int s_pos[kGBM], s_slot[kGBM];
+    __shared__ int s_pos[BM], s_slot[BM];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, ln = lane & 15;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave % WGM, wn = wave / WGM;
     // ---- tile order: XCD-contiguous items, grouped 4 row tiles x all column tiles ----
     const int item = xcd_remap(blockIdx.x, n_mtiles * n_ntiles);
     const int per_group = kGroupM * n_ntiles;
@@ -268,10 +312,10 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(QkvArgs a, int n_mtile
     const int gm_sz = min(kGroupM, n_mtiles - first_m);
     const int local = item % per_group;
     const int mt = first_m + local % gm_sz, nt = local / gm_sz;
-    const int row0 = mt * kGBM, col0 = nt * kGBN;
+    const int row0 = mt * BM, col0 = nt * C::BN;
     if (tid < a.head_dim / 2) s_theta[tid] = pow((double)a.rope_base, -2.0 * tid / a.head_dim);
-    if (!RAW) {
-        const int grow = min(row0 + tid, a.R - 1);      // blockDim.x == kGBM
+    if (!RAW && tid < BM) {
+        const int grow = min(row0 + tid, a.R - 1);
         s_pos[tid] = a.pos[grow];
         s_slot[tid] = a.slot[grow];
     }
@@ -281,31 +325,33 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(QkvArgs a, int n_mtile
 #pragma unroll
     for (int i = 0; i < kInst; ++i) {
         const int j = wave * kInst + i;
-        const int r = (j * kRowsPerInst) % kGBM + lane / kSlots;
-        const int kc = (lane % kSlots) ^ gemm_swz(r);
-        if (j * kRowsPerInst < kGBM) {
+        const int r = (j * kRowsPerInst) % BM + lane / kSlots;
+        if (j * kRowsPerInst < BM) {
             int grow = row0 + r;
             grow = grow < a.R ? grow : a.R - 1;         // ragged tail: re-read a real row, never stored
-            src[i] = a.x + (int64_t)grow * a.d_model + kc * 8;
+            src[i] = a.x + (int64_t)grow * a.d_model + ((lane % kSlots) ^ gemm_swz(r)) * 8;
         } else {
-            src[i] = a.w + (int64_t)(col0 + r) * a.d_model + kc * 8;
+            const int c = j * kRowsPerInst - BM + lane / kSlots;
+            src[i] = a.w + (int64_t)(col0 + c) * a.d_model + ((lane % kSlots) ^ gemm_swz(c)) * 8;
         }
     }
+    // Copies are issued from inline assembly: the compiler cannot tell that a
+    // copy into one stage and a fragment read of another do not overlap, and
+    // with the builtin it waits for every copy before the next read.  The
+    // stage barrier below waits for exactly the copies a stage needs.
+    const uint32_t lds0 = lds_addr(smem);
     auto issue_one = [&](int stage, int kt, int i) __attribute__((always_inline)) {
         const int j = wave * kInst + i;
-        __builtin_amdgcn_global_load_lds((const void*)(src[i] + kt * BK),
-                                         (__attribute__((address_space(3))) void*)(smem + stage * kStage + j * 512),
-                                         16, 0, 0);
+        copy16_to_lds(src[i] + kt * BK, lds0 + (uint32_t)(stage * kStage + j * 512) * 2u);
     };
     // fragments: x rows (MFMA B operand, 16 tokens) and W rows (MFMA A operand, 16 features)
     auto read_x = [&](int kt, int i) __attribute__((always_inline)) {
-        const int r = wm * 128 + i * 16 + ln;
+        const int r = wm * WM + i * 16 + ln;
         return *(const bf16x8*)(smem + (kt % NS) * kStage + r * BK + ((g ^ gemm_swz(r)) % kSlots) * 8);
     };
     auto read_w = [&](int kt, int t) __attribute__((always_inline)) {
         const int c = wn * 128 + t * 16 + ln;
-        return *(const bf16x8*)(smem + (kt % NS) * kStage + kGBM * BK + c * BK +
-                                ((g ^ gemm_swz(c)) % kSlots) * 8);
+        return *(const bf16x8*)(smem + (kt % NS) * kStage + BM * BK + c * BK + ((g ^ gemm_swz(c)) % kSlots) * 8);
     };
     // This thread's copies of stage `next` have landed (later stages may stay
     // in flight) and its fragment reads have returned; then meet the other
@@ -313,17 +359,14 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(QkvArgs a, int n_mtile
     // the stages in flight.
     const int n_kt = a.d_model / BK;
     auto stage_barrier = [&](int next) __attribute__((always_inline)) {
-        const int ahead = min(NS - 2, n_kt - 1 - next);
-        if (NS >= 4 && ahead >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kInst, 0));
-        else if (NS >= 3 && ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_imm(kInst, 0));
-        else __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+        wait_stages_ahead<kInst, NS - 2>(min(NS - 2, n_kt - 1 - next));
         __builtin_amdgcn_s_barrier();
     };
 
-    // acc[i][t]: tokens wm*128 + 16 i + (lane % 16), features wn*128 + 16 t + 4 (lane / 16) + e
-    f32x4 acc[8][8];
+    // acc[i][t]: tokens wm*WM + 16 i + (lane % 16), features wn*128 + 16 t + 4 (lane / 16) + e
+    f32x4 acc[WMF][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < WMF; ++i)
 #pragma unroll
         for (int t = 0; t < 8; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -332,39 +375,40 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(QkvArgs a, int n_mtile
         if (s < n_kt)
 #pragma unroll
             for (int i = 0; i < kInst; ++i) issue_one(s, s, i);
-    bf16x8 cx[8], cw[8];
+    bf16x8 cx[WMF], cw[8];
     stage_barrier(0);
 #pragma unroll
     for (int t = 0; t < 8; ++t) cw[t] = read_w(0, t);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) cx[i] = read_x(0, i);
+    for (int i = 0; i < WMF; ++i) cx[i] = read_x(0, i);
     for (int kt = 0; kt < n_kt; ++kt) {
         // After the last stage the reads below are of a stale buffer and go
         // unused: kept unconditional so the fragment registers need no merge.
         stage_barrier(kt + 1);
         const bool more = kt + NS < n_kt;
-        bf16x8 nx[8], nw[8];
+        bf16x8 nx[WMF], nw[8];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < WMF; ++i) {
 #pragma unroll
             for (int t = 0; t < 8; ++t)
                 acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cw[t], cx[i], acc[i][t], 0, 0, 0);
-            if (more) issue_one(kt % NS, kt + NS, i);
+#pragma unroll
+            for (int c = 0; c < C::kCopyPerGroup; ++c)
+                if (more && i * C::kCopyPerGroup + c < kInst)
+                    issue_one(kt % NS, kt + NS, i * C::kCopyPerGroup + c);
             // the next step's W fragments early (its first group needs all
             // eight), x fragment i once this group has used its register
-            if (i < 4) {
-                nw[2 * i] = read_w(kt + 1, 2 * i);
-                nw[2 * i + 1] = read_w(kt + 1, 2 * i + 1);
-            }
+#pragma unroll
+            for (int c = 0; c < C::kWPerGroup; ++c)
+                if (i * C::kWPerGroup + c < 8) nw[i * C::kWPerGroup + c] = read_w(kt + 1, i * C::kWPerGroup + c);
             nx[i] = read_x(kt + 1, i);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            cx[i] = nx[i];
-            cw[i] = nw[i];
-        }
+        for (int i = 0; i < WMF; ++i) cx[i] = nx[i];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) cw[t] = nw[t];
     }
 
     // ---- epilogue: rotate in registers (pairs are n-tiles t and t+4), bf16, via LDS to rows ----
@@ -377,8 +421,8 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(QkvArgs a, int n_mtile
             for (int e = 0; e < 4; ++e) {
                 const double th = s_theta[t * 16 + g * 4 + e];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    double ang = (double)s_pos[wm * 128 + i * 16 + ln] * th;
+                for (int i = 0; i < WMF; ++i) {
+                    double ang = (double)s_pos[wm * WM + i * 16 + ln] * th;
                     ang -= rint(ang * (1.0 / kTwoPi)) * kTwoPi;
                     // hardware sin/cos take revolutions; |rev| <= 1/2 after the fp64
                     // reduction (library sincosf here would push the accumulators
@@ -392,11 +436,11 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(QkvArgs a, int n_mtile
             }
     }
     __syncthreads();                                    // every wave is done reading the stages
-    // this wave's 128 x 128 bf16 tile (32 KiB), rows of 16 pieces of 16 bytes,
-    // piece p of row r stored at piece p ^ (r % 16)
-    uint16_t* tile = smem + wave * (128 * 128);
+    // this wave's WM x 128 bf16 tile, rows of 16 pieces of 16 bytes, piece p
+    // of row r stored at piece p ^ (r % 16)
+    uint16_t* tile = smem + wave * (WM * 128);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < WMF; ++i)
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const int r = i * 16 + ln, c = t * 16 + g * 4;
@@ -406,10 +450,10 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(QkvArgs a, int n_mtile
             *(uint2*)(&tile[r * 128 + (((c >> 3) ^ (r & 15)) << 3) + (c & 7)]) = v;
         }
     __syncthreads();
-    // 128 rows x 16 pieces of 16 B; a pass covers 4 rows
-    for (int pass = 0; pass < 32; ++pass) {
+    // WM rows x 16 pieces of 16 B; a pass covers 4 rows
+    for (int pass = 0; pass < WM / 4; ++pass) {
         const int r = pass * 4 + (lane >> 4), pc = lane & 15;
-        const int grow = row0 + wm * 128 + r;
+        const int grow = row0 + wm * WM + r;
         if (grow >= a.R) break;
         const u32x4 v = *(const u32x4*)(&tile[r * 128 + ((pc ^ (r & 15)) << 3)]);
         uint16_t* dst;
@@ -418,7 +462,7 @@ __global__ __launch_bounds__(256, 1) void qkv_gemm_kernel(QkvArgs a, int n_mtile
         } else if (part == 0) {
             dst = a.q_out + (int64_t)grow * a.n_out;
         } else {
-            const int sl = s_slot[wm * 128 + r];
+            const int sl = s_slot[wm * WM + r];
             if (sl < 0 || (int64_t)sl >= a.cache_rows) continue;
             dst = (part == 1 ? a.k_cache : a.v_cache) + (int64_t)sl * a.n_out;
         }
@@ -734,35 +778,68 @@ __global__ void qkv_f32_kernel(int R, int d_model, int n_heads, int head_dim, fl
     dst[c_hi] = hi;
 }
 
-enum QkvKind { kSkinny, kTiled128, kGemm256 };
+enum QkvKind { kSkinny, kTiled128, kGemm };
+// tile shapes of qkv_gemm_kernel (rows x columns, workgroups per compute unit)
+enum GemmShape {
+    kG256x256, kG128x256, kG128x256o2, kG64x256, kG64x256o2, kG256x128, kG256x128o2, kG128x128, kG128x128o2,
+    kNumShapes
+};
+constexpr int kShapeBM[kNumShapes] = {256, 128, 128, 64, 64, 256, 256, 128, 128};
+constexpr int kShapeBN[kNumShapes] = {256, 256, 256, 256, 256, 128, 128, 128, 128};
+constexpr int kShapeOcc[kNumShapes] = {1, 1, 2, 1, 2, 1, 2, 1, 2};
+// Time of one workgroup alone on a compute unit (T1) and of two sharing one
+// (T2), measured on MI355X for the LLaDA-8B-shaped projection (d_model 4096,
+// 12288 columns; microseconds, used only to rank the shapes)
+constexpr double kShapeT1[kNumShapes] = {119, 89, 91, 73, 74, 87, 73, 57, 55};
+constexpr double kShapeT2[kNumShapes] = {0, 0, 125, 0, 110, 0, 133, 0, 85};
+constexpr const char* kShapeName[kNumShapes] = {"g256x256", "g128x256", "g128x256o2", "g64x256", "g64x256o2",
+                                                "g256x128", "g256x128o2", "g128x128", "g128x128o2"};
 
 struct QkvPlan {
     QkvKind kind;
+    GemmShape shape;
     int bm, n_mtiles, n_ntiles, n_ktiles;
 };
 
 // Cache-phase row counts (R <= 128) take the weight-streaming kernel
-// (d_model a multiple of 128).  Row counts that give at least one 256 x 256
-// tile per compute unit take the large-tile kernel (head_dim 128, whole
-// heads per wave; measured ahead of the 128 x 128 kernel from ~1800 rows);
-// the rest take the 128 x 128 LDS-tiled kernel.  None splits K across workgroups, so no
-// workspace is needed.
-// DLLM_QKV_KERNEL=tiled|gemm overrides the choice where the shape allows it.
+// (d_model a multiple of 128).  Larger R takes qkv_gemm_kernel (head_dim 128,
+// whole heads per wave) in the tile shape with the least estimated time: the
+// workgroups the busiest compute unit runs (tiles spread over 256 units),
+// alone or in pairs, at the measured time of each.  None splits K
+// across workgroups, so no workspace is needed.  Shapes the GEMM cannot take
+// fall back to the 128 x 128 LDS-tiled kernel.
+// DLLM_QKV_KERNEL=tiled|gemm|g128x256|... overrides the choice where the shape allows it.
 QkvPlan plan_bf16(int R, int d_model, int n_out, int head_dim) {
     QkvPlan p{};
-    const bool gemm_ok = head_dim == 128 && n_out % kGBN == 0 && d_model % kGBK == 0;
-    const int64_t tiles256 = (int64_t)((R + kGBM - 1) / kGBM) * (3 * n_out / kGBN);
+    const bool gemm_ok = head_dim == 128 && n_out % 256 == 0 && d_model % kGBK == 0;
     if (R <= 128 && d_model % 128 == 0) p.kind = kSkinny;
-    else if (gemm_ok && tiles256 >= kNumCu) p.kind = kGemm256;
-    else p.kind = kTiled128;
+    else p.kind = gemm_ok ? kGemm : kTiled128;
+    p.shape = kG256x256;
+    if (p.kind == kGemm) {
+        double best = 0.0;
+        for (int sh = 0; sh < kNumShapes; ++sh) {
+            const int64_t tiles = (int64_t)((R + kShapeBM[sh] - 1) / kShapeBM[sh]) * (3 * n_out / kShapeBN[sh]);
+            // workgroups the busiest compute unit runs, in pairs where two fit
+            const int64_t load = (tiles + kNumCu - 1) / kNumCu;
+            const double t = kShapeOcc[sh] == 2 ? (double)(load / 2) * kShapeT2[sh] + (double)(load % 2) * kShapeT1[sh]
+                                                : (double)load * kShapeT1[sh];
+            if (sh == 0 || t < best) {
+                best = t;
+                p.shape = (GemmShape)sh;
+            }
+        }
+    }
     if (const char* e = getenv("DLLM_QKV_KERNEL")) {
         if (!strcmp(e, "tiled")) p.kind = kTiled128;
-        else if (!strcmp(e, "gemm") && gemm_ok) p.kind = kGemm256;
+        else if (!strcmp(e, "gemm") && gemm_ok) p.kind = kGemm, p.shape = kG256x256;
+        else
+            for (int sh = 0; sh < kNumShapes; ++sh)
+                if (!strcmp(e, kShapeName[sh]) && gemm_ok) p.kind = kGemm, p.shape = (GemmShape)sh;
     }
-    if (p.kind == kGemm256) {
-        p.bm = kGBM;
-        p.n_mtiles = (R + kGBM - 1) / kGBM;
-        p.n_ntiles = 3 * n_out / kGBN;
+    if (p.kind == kGemm) {
+        p.bm = kShapeBM[p.shape];
+        p.n_mtiles = (R + p.bm - 1) / p.bm;
+        p.n_ntiles = 3 * n_out / kShapeBN[p.shape];
     } else {
         p.bm = R <= 64 ? 64 : 128;
         p.n_mtiles = (R + p.bm - 1) / p.bm;
@@ -770,6 +847,17 @@ QkvPlan plan_bf16(int R, int d_model, int n_out, int head_dim) {
     }
     p.n_ktiles = d_model / kBK;
     return p;
+}
+
+template <int WMF, int WGM, int OCC>
+void launch_gemm(const QkvArgs& a, const QkvPlan& p, hipStream_t stream) {
+    const unsigned tiles = (unsigned)((int64_t)p.n_mtiles * p.n_ntiles);
+    if (a.raw_out)
+        hipLaunchKernelGGL((qkv_gemm_kernel<WMF, WGM, OCC, true>), dim3(tiles), dim3(256), 0, stream, a,
+                           p.n_mtiles, p.n_ntiles);
+    else
+        hipLaunchKernelGGL((qkv_gemm_kernel<WMF, WGM, OCC, false>), dim3(tiles), dim3(256), 0, stream, a,
+                           p.n_mtiles, p.n_ntiles);
 }
 
 int check_shape(dllm_dtype dt, int n_rows, int d_model, int n_heads, int head_dim) {
@@ -869,15 +957,19 @@ int qkv_launch(dllm_dtype dt, int n_rows, int d_model, int n_heads, int head_dim
     a.v_cache = (uint16_t*)v_cache;
     a.cache_rows = cache_rows;
     a.raw_out = (uint16_t*)raw_out;
-    if (p.kind == kGemm256) {
-        const int64_t tiles = (int64_t)p.n_mtiles * p.n_ntiles;
-        DLLM_CHECK_SUP(tiles < (1ll << 31));
-        if (a.raw_out)
-            hipLaunchKernelGGL(qkv_gemm_kernel<true>, dim3((unsigned)tiles), dim3(256), 0, stream, a,
-                               p.n_mtiles, p.n_ntiles);
-        else
-            hipLaunchKernelGGL(qkv_gemm_kernel<false>, dim3((unsigned)tiles), dim3(256), 0, stream, a,
-                               p.n_mtiles, p.n_ntiles);
+    if (p.kind == kGemm) {
+        DLLM_CHECK_SUP((int64_t)p.n_mtiles * p.n_ntiles < (1ll << 31));
+        switch (p.shape) {
+            case kG256x256: launch_gemm<8, 2, 1>(a, p, stream); break;
+            case kG128x256: launch_gemm<4, 2, 1>(a, p, stream); break;
+            case kG128x256o2: launch_gemm<4, 2, 2>(a, p, stream); break;
+            case kG64x256: launch_gemm<2, 2, 1>(a, p, stream); break;
+            case kG64x256o2: launch_gemm<2, 2, 2>(a, p, stream); break;
+            case kG256x128: launch_gemm<4, 4, 1>(a, p, stream); break;
+            case kG256x128o2: launch_gemm<4, 4, 2>(a, p, stream); break;
+            case kG128x128: launch_gemm<2, 4, 1>(a, p, stream); break;
+            default: launch_gemm<2, 4, 2>(a, p, stream); break;
+        }
     } else if (p.kind == kSkinny) {
         // pairs per workgroup: the most (up to 24) that still leaves >= 256 workgroups
         const int n_pairs = 3 * n_out / 2;

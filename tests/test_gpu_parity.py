@@ -123,13 +123,19 @@ def test_attention_split_paths(name, splits, gpu, monkeypatch):
     compare_step(c, g, 1)
 
 
-@pytest.mark.parametrize("name,kernel", [("llada_b1", "gemm"), ("mixed_b8", "tiled"), ("tiny_bf16", "gemm")])
+@pytest.mark.parametrize("name,kernel", [("llada_b1", "gemm"), ("mixed_b8", "tiled"), ("tiny_bf16", "gemm"),
+                                         ("llada_b1", "g128x256"), ("llada_b1", "g128x256o2"),
+                                         ("mixed_b8", "g64x256"), ("llada_b1", "g64x256o2"),
+                                         ("mixed_b8", "g256x128"), ("mixed_b8", "g256x128o2"),
+                                         ("tiny_bf16", "g128x128"), ("mixed_b8", "g128x128o2")])
 def test_projection_kernel_paths(name, kernel, gpu, monkeypatch):
-    """The full-refresh projection has two tiled kernels (128 x 128 tiles, and
-    256 x 256 tiles for large row counts); forcing the one the shape would not
-    pick gives the same parity, ragged row tails included (512 rows is two
-    256-row tiles, 6297 rows leaves a tail of 153; tiny_bf16 is one row tile
-    by three column tiles over a contraction of 256)."""
+    """The projection for more than 128 rows has the 128 x 128 LDS-tiled
+    kernel and the whole-head GEMM in five tile shapes (256 x 256, 128 x 256,
+    64 x 256, 256 x 128, 128 x 128), the smaller four alone on a compute unit
+    with a deep ring or two per compute unit ("o2"); forcing one the shape would not pick
+    gives the same parity, ragged row tails included (6297 rows leaves tails
+    of 153, 25 and 25 rows at 256-, 64- and 128-row tiles; tiny_bf16 is one
+    row tile by three or six column tiles over a contraction of 256)."""
     log(f"[gpu] projection kernel {kernel} on {name}")
     monkeypatch.setenv("DLLM_QKV_KERNEL", kernel)
     c = case(name)

@@ -15,7 +15,7 @@ RES = os.path.join(ROOT, "io_aware_kv_amd", "_lib", "kernel_resources.json")
 
 # the rotating 256 x 256 projection keeps three values in scratch in its
 # epilogue (after the K loop); nothing else may spill
-ALLOWED_SPILL = {"qkv_gemm_kernelILb0E": 3}
+ALLOWED_SPILL = {"qkv_gemm_kernelILi8ELi2ELi1ELb0E": 3}
 LDS_LIMIT = 160 * 1024
 
 
