@@ -240,20 +240,27 @@ def main():
     # DualCache (the current block only) and the active window of PrefixCache /
     # FreeCache (the current block and every later block) ----
     block = None
+    full = None
     if not args.no_graph:
         block = {}
-        for mode in W.BLOCK_CACHE_MODES:
-            rws = W.block_cache_rows(wl, mode)
+        for mode in W.BLOCK_CACHE_MODES + ("full",):
+            rws = W.block_cache_rows(wl, mode) if mode != "full" else rows0
             stm = run.upload_step(rws)
             xm = run.to_device_array(W.activations(wl, rws, 2))
             Xm = [xm] + [xm.clone() for _ in range(copies - 1)]
+            mass = mode == "full"     # the full refresh forms the score and runs the top-k
 
-            def mstep(c, stm=stm, Xm=Xm):
+            def mstep(c, stm=stm, Xm=Xm, mass=mass):
                 dllm.qkv_rope_cachewrite_paged(Xm[c], Ws[c], stm.pos, stm.cu_q, stm.logical, run.page_table,
                                                wl.max_pages, stm.slot, stm.q, Ks[c], Vs[c], sh.n_heads,
                                                sh.head_dim, sh.rope_base, stm.ws_qkv)
                 dllm.sched_attention(stm.q, stm.cu_q, Ks[c], Vs[c], run.page_table, wl.max_pages, stm.kv_len,
-                                     stm.o, stm.ws_attn, sh.n_heads, sh.head_dim, stm.max_kv, n_cap=run.n_cap)
+                                     stm.o, stm.ws_attn, sh.n_heads, sh.head_dim, stm.max_kv,
+                                     mass_count=stm.mass_count if mass else None,
+                                     max_mass_rows=stm.max_mass if mass else 0,
+                                     mass_accum=run.mass if mass else None, n_cap=run.n_cap)
+                if mass:
+                    run.topk(clear_mass=True)
             mg = []
             with torch.cuda.stream(cs):
                 for c in range(copies):
@@ -273,8 +280,23 @@ def main():
             m1.record(stream)
             torch.cuda.synchronize()
             mms = m0.elapsed_time(m1) / K
-            block[mode] = {"rows": rws.n_rows, "kv_len": [int(k) for k in rws.kv_len], "us_per_step": mms * 1e3,
-                           "tokens_per_s": rws.n_rows / (mms * 1e-3)}
+            rec = {"rows": rws.n_rows, "kv_len": [int(k) for k in rws.kv_len], "us_per_step": mms * 1e3,
+                   "tokens_per_s": rws.n_rows / (mms * 1e-3)}
+            if mode == "full":
+                # step bound: projection max(W bytes, MFMA) + attention max(K/V bytes, MFMA), bf16 peaks
+                Rf = rws.n_rows
+                pb = max((3 * n_out * sh.d_model + 4 * Rf * n_out) * 2 / (HBM_PEAK_GBS * 1e9),
+                         2 * Rf * sh.d_model * 3 * n_out / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+                kv = rws.kv_len.astype(np.int64)
+                cu = rws.cu_q.astype(np.int64)
+                af = sum(4 * int(cu[b + 1] - cu[b]) * int(kv[b]) * n_out for b in range(wl.n_seq))
+                ab = max((int(kv.sum()) * 2 + 2 * Rf) * n_out * 2 / (HBM_PEAK_GBS * 1e9),
+                         af / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+                rec["step_roofline_us"] = (pb + ab) * 1e6
+                rec["step_roofline_frac"] = (pb + ab) * 1e6 / rec["us_per_step"]
+                full = rec
+            else:
+                block[mode] = rec
             del mg, Xm, xm, stm
         torch.cuda.synchronize()
 
@@ -370,6 +392,7 @@ def main():
         "unfused_arm": None if unfused_ms is None else {
             "ms_per_step": unfused_ms, "fused_speedup": unfused_ms / step_ms,
             "note": "slot mapping, projection to memory, rotary, cache write as separate launches; same attention and top-k"},
+        "full_refresh_step": full,
         "block_cache_steps": block,
         "decode_side": decode,
         "cpu_baseline": cpu,
@@ -462,7 +485,7 @@ def bench_layers(args, dev):
 
     def step(kind, ev=None, unfused=False):
         st = sts[kind]
-        mass = kind in ("full", "cache")      # block-cache steps have no formula-(2) rows
+        mass = kind in ("full", "cache", "cache_mid")    # block-cache steps have no formula-(2) rows
         run.map_slots(st)
         for l in range(L):
             if ev is not None:
@@ -473,7 +496,8 @@ def bench_layers(args, dev):
                 run.cache_update(st, xs[kind][l], Ws[l], l)
             if ev is not None:
                 ev[l][1].record()
-            run.attention(st, l, with_mass=mass)
+            # cache_mid: the score only from the middle layers 5..20 (1-based)
+            run.attention(st, l, with_mass=mass and (kind != "cache_mid" or 5 <= l + 1 <= 20))
             if ev is not None:
                 ev[l][2].record()
         if mass:
@@ -484,6 +508,7 @@ def bench_layers(args, dev):
     rows["cache"] = W.config_step_rows(wl, [idx[b][idx[b] >= 0] for b in range(wl.n_seq)])
     sts["cache"] = run.upload_step(rows["cache"])
     xs["cache"] = [W.device_activations(wl, rows["cache"], 1, l, dev) for l in range(L)]
+    rows["cache_mid"], sts["cache_mid"], xs["cache_mid"] = rows["cache"], sts["cache"], xs["cache"]
     for mode in W.BLOCK_CACHE_MODES:
         rows[mode] = W.block_cache_rows(wl, mode)
         sts[mode] = run.upload_step(rows[mode])
@@ -494,7 +519,7 @@ def bench_layers(args, dev):
     torch.cuda.synchronize()
     K = max(2, min(args.steps, 10))
     res = {}
-    for kind in ("full", "cache") + W.BLOCK_CACHE_MODES:
+    for kind in ("full", "cache", "cache_mid") + W.BLOCK_CACHE_MODES:
         evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(L)] for _ in range(K)]
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0.record()
@@ -542,6 +567,7 @@ def bench_layers(args, dev):
     tot_rows = sum(res[k]["rows_per_layer"] for k in ("full", "cache"))
     tot_ms = sum(res[k]["ms_per_step"] for k in ("full", "cache"))
     block = {k: res.pop(k) for k in W.BLOCK_CACHE_MODES}
+    mid = res.pop("cache_mid")
     value = tot_rows / (tot_ms * 1e-3 / L)
     dom = res["full"]
     out = {
@@ -555,6 +581,7 @@ def bench_layers(args, dev):
                    "layers": L, "batch": wl.n_seq, "parallelism": "single GPU", "timing": "stream launches"},
         "steps_detail": res,
         "block_cache_steps": block,
+        "cache_phase_middle_layer_score": mid,
         "unfused_arm_cache_phase": unfused,
         "roofline": {"bound": "mfma", "kernel": "qkv_rope_cachewrite (full refresh)",
                      "achieved": 2 * dom["rows_per_layer"] * sh.d_model * 3 * n / (dom["qkv_us"] * 1e-6) / 1e12,

@@ -20,6 +20,7 @@ from .flashcache import (  # noqa: F401
     scatter,
     attention,
     column_mass,
+    layer_range_score,
     topk,
     layer_step,
 )

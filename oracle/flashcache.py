@@ -205,6 +205,19 @@ def column_mass(probs: List[np.ndarray], mass_count: Sequence[int], n_cap: int) 
     return out
 
 
+def layer_range_score(terms: Sequence[np.ndarray], first: int, last: int) -> np.ndarray:
+    """The tracked-set score summed over layers first..last only (1-based,
+    inclusive) instead of every layer: the statistics taken from the middle
+    layers where [FD] 研究动机 reports the attention to be concentrated (5 to
+    20).  terms[l-1] is layer l's formula-(2) term."""
+    if not 1 <= first <= last <= len(terms):
+        raise OracleError("layer range outside the model")
+    out = np.zeros_like(np.asarray(terms[0], dtype=np.float64))
+    for layer in range(first, last + 1):
+        out = out + np.asarray(terms[layer - 1], dtype=np.float64)
+    return out
+
+
 def topk(mass: np.ndarray, eligible: np.ndarray, k: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Per sequence, the k eligible positions with the largest score, highest
     first, ties to the lower position; -1 / 0 padding when fewer are eligible

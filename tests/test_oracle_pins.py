@@ -474,3 +474,27 @@ def test_verify_mask_view_ignores_own_and_later_drafts():
             x = base_x.copy()
             x[m + i - 1] += 1.0                                 # draft i-1
             assert not np.allclose(run(x)[i], ref[i])
+
+
+def test_layer_range_score_sums_only_its_layers():
+    """Formula (2) over layers first..last: the full range is the plain sum of
+    every term; a term outside the range changes nothing; the score is linear
+    in the terms; a one-layer range is that layer's term."""
+    rng = np.random.default_rng(41)
+    L = 32
+    terms = [rng.random((3, 40)) for _ in range(L)]
+    full = O.layer_range_score(terms, 1, L)
+    np.testing.assert_allclose(full, np.sum(terms, axis=0), rtol=1e-13)
+    mid = O.layer_range_score(terms, 5, 20)
+    bumped = list(terms)
+    bumped[3] = terms[3] + 7.0          # layer 4
+    bumped[20] = terms[20] + 7.0        # layer 21
+    assert np.array_equal(O.layer_range_score(bumped, 5, 20), mid)
+    bumped[4] = terms[4] + 1.0          # layer 5 is inside
+    np.testing.assert_allclose(O.layer_range_score(bumped, 5, 20), mid + 1.0, rtol=1e-13)
+    np.testing.assert_allclose(O.layer_range_score(terms, 9, 9), terms[8], rtol=0)
+    doubled = [2 * t for t in terms]
+    np.testing.assert_allclose(O.layer_range_score(doubled, 5, 20), 2 * mid, rtol=1e-13)
+    for bad in ((0, 3), (5, 33), (7, 6)):
+        with pytest.raises(O.OracleError):
+            O.layer_range_score(terms, *bad)
