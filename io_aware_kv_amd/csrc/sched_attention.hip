@@ -602,9 +602,12 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     bf16x8 kr[kMR][4];
     uint32_t mw[kMR][kQT / 16];
     float mold[kMR][4];
+    // Groups are taken last to first: the main pass has just streamed the
+    // sequence's keys in ascending order, so its last tiles are the likeliest
+    // to be still in L2 or the Infinity Cache.
     auto gload = [&](auto S, int i) __attribute__((always_inline)) {
         constexpr int sl = decltype(S)::value;
-        const int kw0 = 16 * (wave + 4 * min(i, max(my_groups - 1, 0)));
+        const int kw0 = 16 * (wave + 4 * max(my_groups - 1 - i, 0));
         const int page = s_pages[min(kw0 >> 4, last_page)];
         const int key = kw0 + ln;
         const int64_t row = (page >= 0 && key < si.kv) ? (int64_t)page * 16 + (key & 15) : safe_row;
@@ -629,7 +632,7 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
         constexpr int sl = decltype(S)::value;                 // i % kMR
         gload(Ic<(sl + kMR - 1) % kMR>{}, i + kMR - 1);
         if (i < my_groups) {
-            const int kw0 = 16 * (wave + 4 * i);
+            const int kw0 = 16 * (wave + 4 * (my_groups - 1 - i));
             const int page = s_pages[min(kw0 >> 4, last_page)];
             uint32_t kvalid = 0;                               // C layout: register e of lane group g is key kw0 + 4g + e
 #pragma unroll
