@@ -24,4 +24,5 @@ from .flashcache import (  # noqa: F401
     topk,
     layer_step,
 )
+from .lowbit import E4M3_MAX, e4m3_decode, e4m3_encode, e4m3_round  # noqa: F401
 from .decode import confidence_argmax, confidence_commit, verify_accept  # noqa: F401

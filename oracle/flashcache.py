@@ -34,6 +34,8 @@ from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
 
+from .lowbit import e4m3_round
+
 
 class OracleError(ValueError):
     """An input the method cannot accept (bad table, range or duplicate)."""
@@ -243,15 +245,23 @@ def topk(mass: np.ndarray, eligible: np.ndarray, k: int) -> Tuple[np.ndarray, np
 
 def layer_step(x, w, pos, logical, cu_q, kv_len, mass_count, k_cache, v_cache, page_table,
                n_heads: int, head_dim: int, rope_base: float, page_size: int,
-               visible=None):
+               visible=None, kv_format: str = "plain"):
     """Steps a1..a5 of one layer in the method's order: project, rotate q and
     k, write K/V rows into the cache, attend over the updated cache, and form
-    this layer's formula-(2) term.  Returns a dict of float64 arrays."""
+    this layer's formula-(2) term.  Returns a dict of float64 arrays.
+
+    kv_format "e4m3": the rows are stored in the low-bit cache format of
+    oracle/lowbit.py, so the cache (and "k", "v" of the result) hold the
+    stored values, which the attention reads."""
     n = n_heads * head_dim
     q, k, v = project(x, w, n)
     R = q.shape[0]
     q = rope(q.reshape(R, n_heads, head_dim), pos, rope_base).reshape(R, n)
     k = rope(k.reshape(R, n_heads, head_dim), pos, rope_base).reshape(R, n)
+    if kv_format == "e4m3":
+        k, v = e4m3_round(k), e4m3_round(v)
+    elif kv_format != "plain":
+        raise OracleError(f"unknown cache format {kv_format}")
     slots = row_slots(page_table, cu_q, logical, page_size)
     kc = scatter(k_cache, slots, k)
     vc = scatter(v_cache, slots, v)
