@@ -38,7 +38,8 @@
  *     the pool, a slot outside the cache) are never dereferenced: the affected
  *     key is treated as hidden, the affected row is not written.
  *   - Dtypes: DLLM_BF16 means x, W, the caches, q and o are bf16 (accumulation
- *     in fp32); DLLM_F32 means they are all fp32.
+ *     in fp32); DLLM_F32 means they are all fp32; DLLM_BF16_E4M3KV is DLLM_BF16
+ *     with one-byte E4M3 caches (see below).
  *   - Layouts are row-major and dense.  A cache is [cache_rows, n_heads*head_dim]:
  *     one row per token slot, head h in columns h*head_dim .. h*head_dim+head_dim-1
  *     ([FD] 方法步骤详情 step 1: the flat per-layer cache of B*N_max rows).
@@ -63,7 +64,15 @@ typedef enum {
     DLLM_ERR_HIP = -4            /* a HIP runtime call or launch failed */
 } dllm_status;
 
-typedef enum { DLLM_F32 = 0, DLLM_BF16 = 1 } dllm_dtype;
+/*
+ * DLLM_BF16_E4M3KV: bf16 as DLLM_BF16 for x, W, q and o, with the K and V
+ * caches held as one byte per element: OCP 8-bit float E4M3 codes (unit scale;
+ * stored values rounded to nearest even, magnitudes beyond 448 saturating to
+ * 448).  [FD] paper summary page, 未来方向 item (3): fused kernels over a
+ * low-bit KV cache.  Accepted by dllm_qkv_rope_cachewrite(_paged) and
+ * dllm_sched_attention (head_dim 128); the attention decodes codes exactly.
+ */
+typedef enum { DLLM_F32 = 0, DLLM_BF16 = 1, DLLM_BF16_E4M3KV = 2 } dllm_dtype;
 
 /* Text for a status code (static storage). */
 const char* dllm_status_string(int status);

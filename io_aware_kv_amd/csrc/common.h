@@ -34,6 +34,31 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// Low-bit cache codes: OCP 8-bit float E4M3 (bit 7 sign, 4 exponent bits with
+// bias 7, 3 mantissa bits; no infinities).  Encoding rounds to nearest, ties
+// to even, and saturates at +-448 (the hardware conversion rounds the same
+// way but turns overflow into NaN, hence the clamp); decoding is exact, and
+// every code's value is also exactly a bf16 value.
+__device__ __forceinline__ float e4m3_clamp(float v) { return fminf(fmaxf(v, -448.f), 448.f); }
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), w, true);
+    return (uint32_t)w;
+}
+// eight codes (two words, code k in byte k % 4 of word k / 4) -> bf16x8
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, false);
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w0, true);
+    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, false);
+    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w1, true);
+    u32x4 u;
+    u[0] = pack_bf16x2(a[0], a[1]);
+    u[1] = pack_bf16x2(b[0], b[1]);
+    u[2] = pack_bf16x2(c[0], c[1]);
+    u[3] = pack_bf16x2(d[0], d[1]);
+    return __builtin_bit_cast(bf16x8, u);
+}
+
 // Sum over the 16 lanes of each row of the wave (lanes 16r .. 16r+15); every
 // lane of the row receives the sum.  Four DPP adds, no LDS traffic.
 __device__ __forceinline__ float row16_sum(float v) {
@@ -93,12 +118,22 @@ __device__ __forceinline__ u32x4 load_untracked_x4(const void* p) {
     asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
     return v;
 }
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 load_untracked_x2(const void* p) {
+    u32x2 v;
+    asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+    return v;
+}
 // Keeps later uses of v from being scheduled above the preceding wait.
 __device__ __forceinline__ int fence_value(int v) {
     asm volatile("" : "+v"(v));
     return v;
 }
 __device__ __forceinline__ u32x4 fence_value(u32x4 v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+__device__ __forceinline__ u32x2 fence_value(u32x2 v) {
     asm volatile("" : "+v"(v));
     return v;
 }

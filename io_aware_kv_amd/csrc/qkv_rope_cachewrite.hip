@@ -56,6 +56,7 @@ struct QkvArgs {
     // unfused comparison arm: unrotated q|k|v rows to raw_out [R, 3 n_out]; no
     // rotation and no cache write (nullptr otherwise)
     uint16_t* raw_out;
+    int kv_fp8;             // K/V caches hold E4M3 codes (one byte per element)
 };
 
 template <int BM>
@@ -178,6 +179,7 @@ __global__ __launch_bounds__(kThreads) void qkv_bf16_kernel(QkvArgs a) {
             hi[e] = Cs[r * kLDC + c_hi + e];
         }
         uint16_t* dst;
+        int64_t cache_off = 0;                           // element offset of a cache row's piece
         if (a.raw_out) {
             dst = a.raw_out + (int64_t)grow * 3 * a.n_out + part * a.n_out + cpart;
         } else if (part == 0) {
@@ -185,7 +187,8 @@ __global__ __launch_bounds__(kThreads) void qkv_bf16_kernel(QkvArgs a) {
         } else {
             int s = a.slot[grow];
             if (s < 0 || (int64_t)s >= a.cache_rows) continue;
-            dst = (part == 1 ? a.k_cache : a.v_cache) + (int64_t)s * a.n_out + cpart;
+            cache_off = (int64_t)s * a.n_out + cpart;
+            dst = (part == 1 ? a.k_cache : a.v_cache) + cache_off;
         }
         if (part < 2 && !a.raw_out) {
             const double p = (double)a.pos[grow];
@@ -205,6 +208,12 @@ __global__ __launch_bounds__(kThreads) void qkv_bf16_kernel(QkvArgs a) {
         for (int e = 0; e < 4; ++e) {
             plo[e] = pack_bf16x2(lo[2 * e], lo[2 * e + 1]);
             phi[e] = pack_bf16x2(hi[2 * e], hi[2 * e + 1]);
+        }
+        if (part > 0 && a.kv_fp8 && !a.raw_out) {
+            uint8_t* d8 = (uint8_t*)(part == 1 ? a.k_cache : a.v_cache) + cache_off;
+            *(uint2*)(d8 + c_lo) = make_uint2(e4m3x4(lo[0], lo[1], lo[2], lo[3]), e4m3x4(lo[4], lo[5], lo[6], lo[7]));
+            *(uint2*)(d8 + c_hi) = make_uint2(e4m3x4(hi[0], hi[1], hi[2], hi[3]), e4m3x4(hi[4], hi[5], hi[6], hi[7]));
+            continue;
         }
         *(u32x4*)(dst + c_lo) = plo;
         *(u32x4*)(dst + c_hi) = phi;
@@ -290,11 +299,14 @@ __device__ __forceinline__ void wait_stages_ahead(int ahead) {
     else __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
 }
 
-// RAW: the unfused arm's plain row store (compile-time, so the rotating
-// instantiation keeps its registers)
-template <int WMF, int WGM, int OCC, bool RAW>
+// EPI (compile-time, so the rotating instantiation keeps its registers):
+// kEpiRot rotates q and k and writes bf16 rows; kEpiRaw is the unfused arm's
+// plain row store; kEpiRotE4M3 rotates and writes the K/V rows as E4M3 codes.
+enum { kEpiRot = 0, kEpiRaw = 1, kEpiRotE4M3 = 2 };
+template <int WMF, int WGM, int OCC, int EPI>
 __global__ __launch_bounds__(256, OCC) void qkv_gemm_kernel(QkvArgs a, int n_mtiles, int n_ntiles) {
     using C = GemmCfg<WMF, WGM, OCC>;
+    constexpr bool RAW = EPI == kEpiRaw;
     constexpr int BM = C::BM, BK = C::BK, NS = C::NS, WM = C::WM, kInst = C::kInst, kStage = C::kStage;
     constexpr int kSlots = BK / 8;                      // 16-byte slots per staged row
     constexpr int kRowsPerInst = 64 / kSlots;           // rows one 1 KiB copy instruction covers
@@ -436,6 +448,32 @@ __global__ __launch_bounds__(256, OCC) void qkv_gemm_kernel(QkvArgs a, int n_mti
             }
     }
     __syncthreads();                                    // every wave is done reading the stages
+    if (EPI == kEpiRotE4M3 && part > 0) {
+        // this wave's WM x 128 tile of codes, rows of 8 pieces of 16 bytes,
+        // piece p of row r stored at piece p ^ (r % 8)
+        uint8_t* t8 = reinterpret_cast<uint8_t*>(smem) + wave * (WM * 128);
+#pragma unroll
+        for (int i = 0; i < WMF; ++i)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int r = i * 16 + ln, c = t * 16 + g * 4;
+                *(uint32_t*)(&t8[r * 128 + (((c >> 4) ^ (r & 7)) << 4) + (c & 15)]) =
+                    e4m3x4(acc[i][t][0], acc[i][t][1], acc[i][t][2], acc[i][t][3]);
+            }
+        __syncthreads();
+        // WM rows x 8 pieces of 16 B; a pass covers 8 rows
+        for (int pass = 0; pass < WM / 8; ++pass) {
+            const int r = pass * 8 + (lane >> 3), pc = lane & 7;
+            const int grow = row0 + wm * WM + r;
+            if (grow >= a.R) break;
+            const int sl = s_slot[wm * WM + r];
+            if (sl < 0 || (int64_t)sl >= a.cache_rows) continue;
+            const u32x4 v = *(const u32x4*)(&t8[r * 128 + ((pc ^ (r & 7)) << 4)]);
+            uint8_t* d8 = (uint8_t*)(part == 1 ? a.k_cache : a.v_cache) + (int64_t)sl * a.n_out;
+            *(u32x4*)(d8 + cpart + pc * 16) = v;
+        }
+        return;
+    }
     // this wave's WM x 128 bf16 tile, rows of 16 pieces of 16 bytes, piece p
     // of row r stored at piece p ^ (r % 16)
     uint16_t* tile = smem + wave * (WM * 128);
@@ -698,6 +736,7 @@ __global__ __launch_bounds__(256, 1) void qkv_stream2_kernel(QkvArgs a, int n_pa
         const int hp = p / half, i0 = p % half;            // a piece never straddles a head (half % 8 == 0)
         const int part = hp / H, head = hp % H;
         uint16_t* dst;
+        int64_t cache_off = 0;                           // element offset of the cache row
         if (!PAGED && a.raw_out) {
             dst = a.raw_out + (int64_t)r * 3 * a.n_out + part * a.n_out;
         } else if (part == 0) {
@@ -705,7 +744,8 @@ __global__ __launch_bounds__(256, 1) void qkv_stream2_kernel(QkvArgs a, int n_pa
         } else {
             const int sl = it_slot[k];
             if (sl < 0 || (int64_t)sl >= a.cache_rows) continue;
-            dst = (part == 1 ? a.k_cache : a.v_cache) + (int64_t)sl * a.n_out;
+            cache_off = (int64_t)sl * a.n_out;
+            dst = (part == 1 ? a.k_cache : a.v_cache) + cache_off;
         }
         if (part < 2 && (PAGED || !a.raw_out)) {
 #pragma unroll
@@ -725,6 +765,12 @@ __global__ __launch_bounds__(256, 1) void qkv_stream2_kernel(QkvArgs a, int n_pa
         for (int e = 0; e < 4; ++e) {
             plo[e] = pack_bf16x2(lo[2 * e], lo[2 * e + 1]);
             phi[e] = pack_bf16x2(hi[2 * e], hi[2 * e + 1]);
+        }
+        if (part > 0 && a.kv_fp8) {
+            uint8_t* d8 = (uint8_t*)(part == 1 ? a.k_cache : a.v_cache) + cache_off + head * D + i0;
+            *(uint2*)d8 = make_uint2(e4m3x4(lo[0], lo[1], lo[2], lo[3]), e4m3x4(lo[4], lo[5], lo[6], lo[7]));
+            *(uint2*)(d8 + half) = make_uint2(e4m3x4(hi[0], hi[1], hi[2], hi[3]), e4m3x4(hi[4], hi[5], hi[6], hi[7]));
+            continue;
         }
         *(u32x4*)(dst + head * D + i0) = plo;
         *(u32x4*)(dst + head * D + i0 + half) = phi;
@@ -853,18 +899,22 @@ template <int WMF, int WGM, int OCC>
 void launch_gemm(const QkvArgs& a, const QkvPlan& p, hipStream_t stream) {
     const unsigned tiles = (unsigned)((int64_t)p.n_mtiles * p.n_ntiles);
     if (a.raw_out)
-        hipLaunchKernelGGL((qkv_gemm_kernel<WMF, WGM, OCC, true>), dim3(tiles), dim3(256), 0, stream, a,
+        hipLaunchKernelGGL((qkv_gemm_kernel<WMF, WGM, OCC, kEpiRaw>), dim3(tiles), dim3(256), 0, stream, a,
+                           p.n_mtiles, p.n_ntiles);
+    else if (a.kv_fp8)
+        hipLaunchKernelGGL((qkv_gemm_kernel<WMF, WGM, OCC, kEpiRotE4M3>), dim3(tiles), dim3(256), 0, stream, a,
                            p.n_mtiles, p.n_ntiles);
     else
-        hipLaunchKernelGGL((qkv_gemm_kernel<WMF, WGM, OCC, false>), dim3(tiles), dim3(256), 0, stream, a,
+        hipLaunchKernelGGL((qkv_gemm_kernel<WMF, WGM, OCC, kEpiRot>), dim3(tiles), dim3(256), 0, stream, a,
                            p.n_mtiles, p.n_ntiles);
 }
 
 int check_shape(dllm_dtype dt, int n_rows, int d_model, int n_heads, int head_dim) {
     DLLM_CHECK_ARG(n_rows >= 0 && d_model > 0 && n_heads > 0 && head_dim > 0);
-    DLLM_CHECK_SUP(dt == DLLM_BF16 || dt == DLLM_F32);
+    DLLM_CHECK_SUP(dt == DLLM_BF16 || dt == DLLM_F32 || dt == DLLM_BF16_E4M3KV);
     DLLM_CHECK_SUP(head_dim == 64 || head_dim == 128);
-    if (dt == DLLM_BF16) {
+    DLLM_CHECK_SUP(dt != DLLM_BF16_E4M3KV || head_dim == 128);
+    if (dt != DLLM_F32) {
         DLLM_CHECK_SUP((n_heads * head_dim) % kBN == 0);
         DLLM_CHECK_SUP(d_model % kBK == 0);
     }
@@ -919,6 +969,8 @@ int qkv_launch(dllm_dtype dt, int n_rows, int d_model, int n_heads, int head_dim
     const int pool_pages = pg ? (int)(cache_rows / pg->page_size < (1ll << 30) ? cache_rows / pg->page_size
                                                                                : (1ll << 30))
                               : 0;
+    const bool e4m3 = dt == DLLM_BF16_E4M3KV;           // bf16 compute, one-byte caches
+    if (e4m3) dt = DLLM_BF16;
     const bool skinny = dt == DLLM_BF16 && plan_bf16(n_rows, d_model, n_out, head_dim).kind == kSkinny;
     if (pg && !skinny) {
         // slots first (the same rule, its own launch), then the slot-taking kernels
@@ -957,6 +1009,7 @@ int qkv_launch(dllm_dtype dt, int n_rows, int d_model, int n_heads, int head_dim
     a.v_cache = (uint16_t*)v_cache;
     a.cache_rows = cache_rows;
     a.raw_out = (uint16_t*)raw_out;
+    a.kv_fp8 = e4m3 ? 1 : 0;
     if (p.kind == kGemm) {
         DLLM_CHECK_SUP((int64_t)p.n_mtiles * p.n_ntiles < (1ll << 31));
         switch (p.shape) {
@@ -1047,7 +1100,7 @@ extern "C" int dllm_qkv_project(dllm_dtype dt, int n_rows, int d_model, int n_he
                                 size_t workspace_bytes, hipStream_t stream) {
     int st = check_shape(dt, n_rows, d_model, n_heads, head_dim);
     if (st != DLLM_OK) return st;
-    DLLM_CHECK_SUP(dt == DLLM_BF16);
+    DLLM_CHECK_SUP(dt == DLLM_BF16);                    // no cache: plain bf16 only
     if (n_rows == 0) return DLLM_OK;
     DLLM_CHECK_ARG(x && w_qkv && qkv_out);
     (void)workspace;

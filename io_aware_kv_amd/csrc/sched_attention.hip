@@ -180,7 +180,13 @@ __device__ __forceinline__ void wait_stages(int younger) {
 
 // NS: ring stages.  Two are launched (two workgroups per compute unit); four
 // stages with one workgroup per unit measured slower even on small grids.
-template <int RT, int NS, bool HAS_MASK>
+// KV8: the caches hold E4M3 codes.  Their tiles cannot use the
+// direct-to-LDS copies (the MFMA needs bf16): a wave loads its pieces of the
+// next tile into registers after the barrier, and before the following
+// barrier decodes them and writes the bf16 values to exactly the LDS places
+// the copies would fill, so every fragment read is the same as for bf16
+// caches.  One tile is in flight, as with the two-stage ring.
+template <int RT, int NS, bool HAS_MASK, bool KV8>
 __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kernel(AttnArgs a) {
     constexpr int kRing = NS * kStageBytes;
     constexpr int QT = 64 * RT;
@@ -290,6 +296,8 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     // ---- copies: K groups (waves 0, 1) or V groups (waves 2, 3) of 4 keys; mask words; query tile ----
     const bool is_v = wave >= 2;
     const uint16_t* kv_src = (is_v ? a.v : a.k) + h * kHD;
+    const uint8_t* kv_src8 = reinterpret_cast<const uint8_t*>(is_v ? a.v : a.k) + h * kHD;
+    u32x2 kv8[KV8 ? kDmaPerWave : 1];                   // KV8: this wave's codes of the tile in flight
     int lslot[kDmaPerWave];
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
@@ -305,7 +313,10 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
             const int page = s_pages[min(kg >> 4, last_page)];
             const bool ok = (t < t_end) & (kg < si.kv) & (page >= 0);
             const int64_t row = ok ? (int64_t)page * 16 + (kg & 15) : safe_row;
-            copy16_to_lds(kv_src + row * a.n_out + lslot[i] * 8, __builtin_amdgcn_readfirstlane(dst + q * 1024));
+            if constexpr (KV8)
+                kv8[i] = load_untracked_x2(kv_src8 + row * a.n_out + lslot[i] * 8);
+            else
+                copy16_to_lds(kv_src + row * a.n_out + lslot[i] * 8, __builtin_amdgcn_readfirstlane(dst + q * 1024));
         }
         if constexpr (HAS_MASK) {
             // words 2t, 2t+1 of every query row of the tile: [row][2]
@@ -318,6 +329,20 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
                 int64_t wi = mask_row0 + (int64_t)row * mwords + 2 * (int64_t)t + (idx & 1);
                 wi = min(max(wi, (int64_t)0), a.mask_words - 1);
                 copy4_to_lds(a.mask + wi, __builtin_amdgcn_readfirstlane(mdst + m * 256));
+            }
+        }
+    };
+
+    // KV8: decode the codes loaded by issue() (their wait is the caller's) into
+    // the bf16 places of stage sl
+    auto commit8 = [&](int sl) __attribute__((always_inline)) {
+        if constexpr (KV8) {
+            uint8_t* dst = reinterpret_cast<uint8_t*>(is_v ? v_tile(sl) : k_tile(sl));
+#pragma unroll
+            for (int i = 0; i < kDmaPerWave; ++i) {
+                const int q = (wave & 1) * kDmaPerWave + i;
+                const u32x2 w = fence_value(kv8[i]);
+                *(bf16x8*)(dst + q * 1024 + 16 * lane) = e4m3x8_to_bf16(w[0], w[1]);
             }
         }
     };
@@ -339,10 +364,15 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
             qraw[rt][ks] = load_untracked_x4(a.q + (int64_t)qrow * a.n_out + h * kHD + ks * 32 + g * 8);
     }
     const int n_main = t_end - t_begin;
-    const int n_pro = min(NS, n_main);                   // the ring's first fill: real tiles only
+    const int n_pro = KV8 ? min(1, n_main) : min(NS, n_main);   // the ring's first fill: real tiles only
     for (int s = 0; s < NS; ++s)
         if (s < n_pro) issue(s, t_begin + s);
-    wait_stages<NS, kPerStage>(n_pro);                   // the query fragments (older than every copy)
+    if constexpr (KV8) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));   // the query fragments and tile 0's codes
+        if (n_pro > 0) commit8(0);
+    } else {
+        wait_stages<NS, kPerStage>(n_pro);               // the query fragments (older than every copy)
+    }
     bf16x8 qf[RT][4];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -503,14 +533,29 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     // A step waits until its own tile has landed (the stages issued after it
     // may stay in flight), then an LDS-only barrier publishes it
     // (__syncthreads would also wait for the younger stages).
-    for (int i = 0; i < n_main; ++i) {
-        const int issued = min(n_main, NS + max(i - 1, 0));   // tiles issued before this step
-        wait_stages<NS, kPerStage>(issued - 1 - i);            // ... younger than tile i
-        lds_sync();
-        __builtin_amdgcn_sched_barrier(0);
-        if (i > 0 && i - 1 + NS < n_main) issue((i - 1) % NS, t_begin + i - 1 + NS);
-        __builtin_amdgcn_sched_barrier(0);
-        attend(i % NS, t_begin + i);
+    if constexpr (KV8) {
+        // tile i's codes were loaded in step i - 1; its stage was last read in step i - 2
+        for (int i = 0; i < n_main; ++i) {
+            if (i > 0) {
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+                commit8(i % NS);
+            }
+            lds_sync();
+            __builtin_amdgcn_sched_barrier(0);
+            if (i + 1 < n_main) issue((i + 1) % NS, t_begin + i + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            attend(i % NS, t_begin + i);
+        }
+    } else {
+        for (int i = 0; i < n_main; ++i) {
+            const int issued = min(n_main, NS + max(i - 1, 0));   // tiles issued before this step
+            wait_stages<NS, kPerStage>(issued - 1 - i);            // ... younger than tile i
+            lds_sync();
+            __builtin_amdgcn_sched_barrier(0);
+            if (i > 0 && i - 1 + NS < n_main) issue((i - 1) % NS, t_begin + i - 1 + NS);
+            __builtin_amdgcn_sched_barrier(0);
+            attend(i % NS, t_begin + i);
+        }
     }
     __syncthreads();                                    // every copy has been waited for above
 
@@ -599,7 +644,8 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     const int ngroups = (kmax + 15) / 16;
     const int my_groups = ngroups > wave ? (ngroups - 1 - wave) / 4 + 1 : 0;
     constexpr int kMR = HAS_MASK ? 2 : 4;                       // key groups in flight (registers)
-    bf16x8 kr[kMR][4];
+    bf16x8 kr[KV8 ? 1 : kMR][4];
+    uint2 kr8[KV8 ? kMR : 1][4];                                // KV8: codes, decoded when used
     uint32_t mw[kMR][kQT / 16];
     float mold[kMR][4];
     // Groups are taken last to first: the main pass has just streamed the
@@ -612,8 +658,13 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
         const int key = kw0 + ln;
         const int64_t row = (page >= 0 && key < si.kv) ? (int64_t)page * 16 + (key & 15) : safe_row;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            kr[sl][ks] = *(const bf16x8*)(a.k + row * a.n_out + h * kHD + ks * 32 + g * 8);
+        for (int ks = 0; ks < 4; ++ks) {
+            if constexpr (KV8)
+                kr8[sl][ks] = *(const uint2*)(reinterpret_cast<const uint8_t*>(a.k) + row * a.n_out + h * kHD +
+                                              ks * 32 + g * 8);
+            else
+                kr[sl][ks] = *(const bf16x8*)(a.k + row * a.n_out + h * kHD + ks * 32 + g * 8);
+        }
         if constexpr (HAS_MASK) {
 #pragma unroll
             for (int rt = 0; rt < kQT / 16; ++rt) {
@@ -638,6 +689,12 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
 #pragma unroll
             for (int e = 0; e < 4; ++e) kvalid |= (page >= 0 && kw0 + 4 * g + e < si.kv ? 1u : 0u) << e;
             float csum[4] = {0.f, 0.f, 0.f, 0.f};
+            bf16x8 kf[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                if constexpr (KV8) kf[ks] = e4m3x8_to_bf16(kr8[sl][ks].x, kr8[sl][ks].y);
+                else kf[ks] = kr[sl][ks];
+            }
 #pragma unroll
             for (int rt = 0; rt < kQT / 16; ++rt) {
                 if (rt >= rtiles) continue;
@@ -649,7 +706,7 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
                 f32x4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks)
-                    st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[sl][ks], qb[ks], st, 0, 0, 0);
+                    st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qb[ks], st, 0, 0, 0);
                 uint32_t vis = row < mb ? kvalid : 0u;
                 if constexpr (HAS_MASK) vis &= (mw[sl][rt] >> ((kw0 + 4 * g) & 31)) & 0xfu;
 #pragma unroll
@@ -703,7 +760,7 @@ constexpr int kMergeRows = kFinThreads / (kHD / 8);      // 16 rows per merge it
 // MAXS with clamped indices (loads in flight together; a loop to the runtime
 // count with a running maximum or sum would serialise them) and the values
 // past the split count are ignored.
-template <int MAXS>
+template <int MAXS, bool KV8>
 __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
     __shared__ int s_pref[kMaxSeq + 1];
     __shared__ int s_total;
@@ -864,9 +921,15 @@ __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
     const bool key_ok = kw < si.kv && page_ok;
     const int64_t krow = key_ok ? (int64_t)page * 16 + (kw & 15) : 0;
     bf16x8 kf[4];
+    uint2 kf8[4];                                            // KV8: codes, decoded after the waits
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-        kf[ks] = *(const bf16x8*)(a.k + krow * a.n_out + h * kHD + ks * 32 + g * 8);
+    for (int ks = 0; ks < 4; ++ks) {
+        if constexpr (KV8)
+            kf8[ks] = *(const uint2*)(reinterpret_cast<const uint8_t*>(a.k) + krow * a.n_out + h * kHD + ks * 32 +
+                                      g * 8);
+        else
+            kf[ks] = *(const bf16x8*)(a.k + krow * a.n_out + h * kHD + ks * 32 + g * 8);
+    }
 
     mb = max(0, min(mb, min(a.max_mass, min(si.rows, kQT))));
     if (mb == 0) return;                                     // uniform: nothing to add
@@ -883,6 +946,10 @@ __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
         s_lse[tid] = l > 0.f ? m + __log2f(l) : INFINITY;      // a row that sees nothing adds 0
     }
     __syncthreads();
+    if constexpr (KV8) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kf[ks] = e4m3x8_to_bf16(kf8[ks].x, kf8[ks].y);
+    }
     // C layout: register e of lane group g is key kw0 + 4g + e
     uint32_t kvalid = 0;
 #pragma unroll
@@ -1014,7 +1081,7 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a, const
 // DLLM_ATTN_SPLITS overrides the split count (a tuning knob; the workspace
 // query reads it too, so the two agree).
 int choose_splits(dllm_dtype dt, int n_seq, int n_rows, int n_heads, int max_kv) {
-    if (dt != DLLM_BF16) return 1;
+    if (dt != DLLM_BF16 && dt != DLLM_BF16_E4M3KV) return 1;
     const int ktiles = (max_kv + kKT - 1) / kKT;
     int s = 1;
     const int qtiles = (n_rows + kQT - 1) / kQT;
@@ -1041,13 +1108,27 @@ size_t split_workspace(int n_seq, int n_rows, int n_heads, int splits) {
     return (size_t)items * kQT * (kHD + 2) * sizeof(float);
 }
 
+template <bool KV8>
+void launch_attn(const AttnArgs& a, dim3 grid, dim3 block, bool mask, hipStream_t stream) {
+    if (mask) hipLaunchKernelGGL((attn_bf16_kernel<2, 2, true, KV8>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<2, 2, false, KV8>), grid, block, 0, stream, a);
+}
+
+template <bool KV8>
+void launch_finish(const AttnArgs& a, int splits, unsigned fin, hipStream_t stream) {
+    if (splits <= 2) hipLaunchKernelGGL((attn_finish_kernel<2, KV8>), dim3(fin), dim3(kFinThreads), 0, stream, a);
+    else if (splits <= 4) hipLaunchKernelGGL((attn_finish_kernel<4, KV8>), dim3(fin), dim3(kFinThreads), 0, stream, a);
+    else if (splits <= 8) hipLaunchKernelGGL((attn_finish_kernel<8, KV8>), dim3(fin), dim3(kFinThreads), 0, stream, a);
+    else hipLaunchKernelGGL((attn_finish_kernel<16, KV8>), dim3(fin), dim3(kFinThreads), 0, stream, a);
+}
+
 int check_attn(dllm_dtype dt, int n_seq, int n_rows, int n_heads, int head_dim, int page_size,
                int max_kv, int n_cap) {
     DLLM_CHECK_ARG(n_seq > 0 && n_rows >= 0 && n_heads > 0 && max_kv > 0 && n_cap >= 0);
-    DLLM_CHECK_SUP(dt == DLLM_BF16 || dt == DLLM_F32);
+    DLLM_CHECK_SUP(dt == DLLM_BF16 || dt == DLLM_F32 || dt == DLLM_BF16_E4M3KV);
     DLLM_CHECK_SUP(page_size == 16);
     DLLM_CHECK_SUP(n_seq <= kMaxSeq);
-    if (dt == DLLM_BF16) {
+    if (dt != DLLM_F32) {
         DLLM_CHECK_SUP(head_dim == kHD);
         DLLM_CHECK_SUP(max_kv <= kMaxPages * 16);
     } else {
@@ -1088,7 +1169,7 @@ extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_
         DLLM_CHECK_ARG(n_cap > 0);
         DLLM_CHECK_SUP(max_mass_rows >= 0 && max_mass_rows <= kQT);
         // the bf16 kernel sums a head's column mass in LDS: <= 8704 keys
-        if (dt == DLLM_BF16) DLLM_CHECK_SUP((max_kv < n_cap ? max_kv : n_cap) <= 8704);
+        if (dt != DLLM_F32) DLLM_CHECK_SUP((max_kv < n_cap ? max_kv : n_cap) <= 8704);
     }
     const int splits = choose_splits(dt, n_seq, n_rows, n_heads, max_kv);
     const size_t ws_need = split_workspace(n_seq, n_rows, n_heads, splits);
@@ -1124,26 +1205,24 @@ extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_
         a.part_o = (float*)workspace;
         a.part_ml = a.part_o + items * kQT * kHD;
     }
-    if (dt == DLLM_BF16) {
+    if (dt != DLLM_F32) {
         // 128-row query tiles: four waves of 32 rows (two 16-row MFMA tiles each)
         const int64_t items = (int64_t)n_heads * (n_rows / kQT + n_seq) * splits;
         DLLM_CHECK_SUP(items > 0 && items < (1ll << 30));
         const dim3 grid((unsigned)items), block(kAttnThreads);
-        if (mask_bits) hipLaunchKernelGGL((attn_bf16_kernel<2, 2, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((attn_bf16_kernel<2, 2, false>), grid, block, 0, stream, a);
+        if (dt == DLLM_BF16_E4M3KV)
+            launch_attn<true>(a, grid, block, mask_bits != nullptr, stream);
+        else
+            launch_attn<false>(a, grid, block, mask_bits != nullptr, stream);
         if (splits > 1) {
             DLLM_CHECK_LAUNCH();
             int64_t fin = (int64_t)n_heads * (n_rows / kMergeRows + n_seq);
             if (want_mass) fin += (int64_t)n_heads * n_seq * ((max_kv + kKT - 1) / kKT);
             DLLM_CHECK_SUP(fin < (1ll << 30));
-            if (splits <= 2)
-                hipLaunchKernelGGL(attn_finish_kernel<2>, dim3((unsigned)fin), dim3(kFinThreads), 0, stream, a);
-            else if (splits <= 4)
-                hipLaunchKernelGGL(attn_finish_kernel<4>, dim3((unsigned)fin), dim3(kFinThreads), 0, stream, a);
-            else if (splits <= 8)
-                hipLaunchKernelGGL(attn_finish_kernel<8>, dim3((unsigned)fin), dim3(kFinThreads), 0, stream, a);
+            if (dt == DLLM_BF16_E4M3KV)
+                launch_finish<true>(a, splits, (unsigned)fin, stream);
             else
-                hipLaunchKernelGGL(attn_finish_kernel<16>, dim3((unsigned)fin), dim3(kFinThreads), 0, stream, a);
+                launch_finish<false>(a, splits, (unsigned)fin, stream);
         }
     } else {
         hipLaunchKernelGGL(attn_f32_kernel, dim3(n_seq * n_heads), dim3(kF32Threads), 0, stream,

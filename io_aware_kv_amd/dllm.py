@@ -14,7 +14,7 @@ import numpy as np
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libdllm.so")
 
-F32, BF16 = 0, 1
+F32, BF16, BF16_E4M3KV = 0, 1, 2
 PAGE = 16
 
 # names in include/dllm.h, in declaration order
@@ -114,6 +114,17 @@ def dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def cache_dtype_code(t, k_cache) -> int:
+    """The dtype code of a call that takes caches: one-byte (uint8) caches
+    hold E4M3 codes next to bf16 activations."""
+    import torch
+    if k_cache is not None and k_cache.dtype == torch.uint8:
+        if t.dtype != torch.bfloat16:
+            raise TypeError("E4M3 caches go with bf16 activations")
+        return BF16_E4M3KV
+    return dtype_code(t)
+
+
 def version() -> int:
     return load().dllm_version()
 
@@ -152,7 +163,7 @@ def qkv_rope_cachewrite_workspace(dt: int, n_rows: int, d_model: int, n_heads: i
 
 def qkv_rope_cachewrite(x, w_qkv, pos, slot, q_out, k_cache, v_cache, n_heads: int, head_dim: int,
                         rope_base: float, workspace=None, stream=None) -> None:
-    dt = dtype_code(x)
+    dt = cache_dtype_code(x, k_cache)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("dllm_qkv_rope_cachewrite", load().dllm_qkv_rope_cachewrite(
         dt, x.shape[0], x.shape[1], n_heads, head_dim, float(rope_base), _ptr(x), _ptr(w_qkv),
@@ -165,7 +176,7 @@ def qkv_rope_cachewrite_paged(x, w_qkv, pos, cu_q, q_logical, page_table, max_pa
                               workspace=None, page_size: int = PAGE, stream=None) -> None:
     """qkv_rope_cachewrite with each row's cache slot formed from its logical
     position and the block table (written to slot as well)."""
-    dt = dtype_code(x)
+    dt = cache_dtype_code(x, k_cache)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("dllm_qkv_rope_cachewrite_paged", load().dllm_qkv_rope_cachewrite_paged(
         dt, cu_q.shape[0] - 1, x.shape[0], x.shape[1], n_heads, head_dim, float(rope_base), _ptr(x),
@@ -206,7 +217,7 @@ def sched_attention(q, cu_q, k_cache, v_cache, page_table, max_pages: int, kv_le
                     n_heads: int, head_dim: int, max_kv: int, mask_bits=None, mask_off=None,
                     mass_count=None, max_mass_rows: int = 0, mass_accum=None, n_cap: int = 0,
                     page_size: int = PAGE, stream=None) -> None:
-    dt = dtype_code(q)
+    dt = cache_dtype_code(q, k_cache)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     mask_words = 0 if mask_bits is None else mask_bits.numel()
     _check("dllm_sched_attention", load().dllm_sched_attention(

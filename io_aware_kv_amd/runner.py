@@ -45,12 +45,18 @@ class StepDevice:
 
 class FlashCacheRunner:
     def __init__(self, wl: Workload, device="cuda", layers: Optional[int] = None,
-                 cache_copies: int = 1):
+                 cache_copies: int = 1, kv_format: str = "plain"):
+        """kv_format "e4m3": the caches hold one-byte E4M3 codes (bf16 layers)."""
         sh = wl.shape
         self.wl = wl
         self.device = torch.device(device)
         self.dtype = torch.bfloat16 if sh.dtype == "bf16" else torch.float32
         self.dt = dllm.BF16 if sh.dtype == "bf16" else dllm.F32
+        if kv_format not in ("plain", "e4m3") or (kv_format == "e4m3" and sh.dtype != "bf16"):
+            raise ValueError(f"cache format {kv_format} for a {sh.dtype} layer")
+        self.kv_format = kv_format
+        cache_dtype = torch.uint8 if kv_format == "e4m3" else self.dtype
+        self.dt_cache = dllm.BF16_E4M3KV if kv_format == "e4m3" else self.dt
         self.H, self.D = sh.n_heads, sh.head_dim
         self.n_out = sh.n_heads * sh.head_dim
         self.layers = sh.layers if layers is None else layers
@@ -60,8 +66,8 @@ class FlashCacheRunner:
         self.k_cache: List[torch.Tensor] = []
         self.v_cache: List[torch.Tensor] = []
         for _ in range(self.layers * cache_copies):
-            self.k_cache.append(torch.zeros(self.cache_rows, self.n_out, dtype=self.dtype, device=self.device))
-            self.v_cache.append(torch.zeros(self.cache_rows, self.n_out, dtype=self.dtype, device=self.device))
+            self.k_cache.append(torch.zeros(self.cache_rows, self.n_out, dtype=cache_dtype, device=self.device))
+            self.v_cache.append(torch.zeros(self.cache_rows, self.n_out, dtype=cache_dtype, device=self.device))
         self.page_table = torch.empty(wl.n_seq * wl.max_pages, dtype=torch.int32, device=self.device)
         dllm.build_block_table(wl.seq_pages, wl.pool_perm, wl.pool_pages, wl.max_pages, self.page_table)
         # formula (2) per-head running scores [B, H, n_cap]; top-k sums the heads
@@ -92,7 +98,7 @@ class FlashCacheRunner:
         max_kv = int(rows.kv_len.max())
         max_mass = int(rows.mass_count.max())
         ws_qkv_b = dllm.qkv_rope_cachewrite_workspace(self.dt, R, self.wl.shape.d_model, self.H, self.D)
-        ws_attn_b = dllm.sched_attention_workspace(self.dt, self.wl.n_seq, R, self.H, self.D, max_kv,
+        ws_attn_b = dllm.sched_attention_workspace(self.dt_cache, self.wl.n_seq, R, self.H, self.D, max_kv,
                                                    self.n_cap)
         return StepDevice(
             n_rows=R, cu_q=i32(rows.cu_q), logical=i32(rows.logical), pos=i32(rows.pos),
