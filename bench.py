@@ -300,6 +300,49 @@ def main():
             del mg, Xm, xm, stm
         torch.cuda.synchronize()
 
+    # ---- the same step over one-byte E4M3 caches (filled by a full refresh in that format) ----
+    lowbit = None
+    if not args.no_graph and sh.dtype == "bf16":
+        run8 = FlashCacheRunner(wl, device=dev, layers=1, kv_format="e4m3")
+        st8_0 = run8.upload_step(rows0)
+        run8.layer_step(st8_0, run8.to_device_array(W.activations(wl, rows0, 0)), w0, 0)
+        run8.topk(clear_mass=True)
+        st8 = run8.upload_step(rows1)
+        K8 = [run8.k_cache[0]] + [run8.k_cache[0].clone() for _ in range(copies - 1)]
+        V8 = [run8.v_cache[0]] + [run8.v_cache[0].clone() for _ in range(copies - 1)]
+
+        def step8(c):
+            dllm.qkv_rope_cachewrite_paged(Xs[c], Ws[c], st8.pos, st8.cu_q, st8.logical, run8.page_table,
+                                           wl.max_pages, st8.slot, st8.q, K8[c], V8[c], sh.n_heads,
+                                           sh.head_dim, sh.rope_base, st8.ws_qkv)
+            dllm.sched_attention(st8.q, st8.cu_q, K8[c], V8[c], run8.page_table, wl.max_pages, st8.kv_len,
+                                 st8.o, st8.ws_attn, sh.n_heads, sh.head_dim, st8.max_kv,
+                                 mask_bits=st8.mask_bits, mask_off=st8.mask_off, mass_count=st8.mass_count,
+                                 max_mass_rows=st8.max_mass, mass_accum=run8.mass, n_cap=run8.n_cap)
+            run8.topk(clear_mass=True)
+        g8 = []
+        with torch.cuda.stream(cs):
+            for c in range(copies):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cs):
+                    step8(c)
+                g8.append(g)
+        stream.wait_stream(cs)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            g8[i % copies].replay()
+        torch.cuda.synchronize()
+        l0, l1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        l0.record(stream)
+        for i in range(K):
+            g8[i % copies].replay()
+        l1.record(stream)
+        torch.cuda.synchronize()
+        lms = l0.elapsed_time(l1) / K
+        lowbit = {"cache_format": "E4M3 (one byte per K/V element)", "us_per_step": lms * 1e3,
+                  "tokens_per_s": R / (lms * 1e-3), "vs_bf16_cache": graph_ms / lms if graph_ms else None}
+        del g8, K8, V8
+
     step_ms = graph_ms if graph_ms is not None else plain_ms
     value = R / (step_ms * 1e-3)
 
@@ -393,6 +436,7 @@ def main():
             "ms_per_step": unfused_ms, "fused_speedup": unfused_ms / step_ms,
             "note": "slot mapping, projection to memory, rotary, cache write as separate launches; same attention and top-k"},
         "full_refresh_step": full,
+        "e4m3_cache_step": lowbit,
         "block_cache_steps": block,
         "decode_side": decode,
         "cpu_baseline": cpu,
@@ -513,30 +557,56 @@ def bench_layers(args, dev):
         rows[mode] = W.block_cache_rows(wl, mode)
         sts[mode] = run.upload_step(rows[mode])
         xs[mode] = [W.device_activations(wl, rows[mode], 2, l, dev) for l in range(L)]
+    # the same cache-phase step over one-byte E4M3 caches (a second set of
+    # caches, filled by a full refresh in that format)
+    run8 = FlashCacheRunner(wl, device=dev, kv_format="e4m3")
+    st8 = {"full": run8.upload_step(rows["full"]), "cache": run8.upload_step(rows["cache"])}
+
+    def step8(kind, ev=None):
+        st = st8[kind]
+        run8.map_slots(st)
+        for l in range(L):
+            if ev is not None:
+                ev[l][0].record()
+            run8.cache_update(st, xs[kind][l], Ws[l], l)
+            if ev is not None:
+                ev[l][1].record()
+            run8.attention(st, l)
+            if ev is not None:
+                ev[l][2].record()
+        run8.topk(clear_mass=True)
+
+    step8("full")
     for _ in range(max(1, args.warmup // 10)):
         step("cache")
         step("full")
+        step8("cache")
     torch.cuda.synchronize()
     K = max(2, min(args.steps, 10))
     res = {}
-    for kind in ("full", "cache", "cache_mid") + W.BLOCK_CACHE_MODES:
+    for kind in ("full", "cache", "cache_mid", "cache_e4m3") + W.BLOCK_CACHE_MODES:
         evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(L)] for _ in range(K)]
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0.record()
         for i in range(K):
-            step(kind, evs[i])
+            if kind == "cache_e4m3":
+                step8("cache", evs[i])
+            else:
+                step(kind, evs[i])
         t1.record()
         torch.cuda.synchronize()
         ms = t0.elapsed_time(t1) / K
         qkv_us = float(np.mean([evs[i][l][0].elapsed_time(evs[i][l][1]) for i in range(K) for l in range(L)])) * 1e3
         att_us = float(np.mean([evs[i][l][1].elapsed_time(evs[i][l][2]) for i in range(K) for l in range(L)])) * 1e3
-        R = rows[kind].n_rows
-        kv = rows[kind].kv_len.astype(np.int64)
-        cu = rows[kind].cu_q.astype(np.int64)
+        rk = rows["cache"] if kind == "cache_e4m3" else rows[kind]
+        R = rk.n_rows
+        kv = rk.kv_len.astype(np.int64)
+        cu = rk.cu_q.astype(np.int64)
+        cache_el = 1 if kind == "cache_e4m3" else 2        # bytes per cached K/V element
         qkv_flops = 2 * R * sh.d_model * 3 * n
-        qkv_bytes = 3 * n * sh.d_model * 2 + R * 32 * 1024
+        qkv_bytes = 3 * n * sh.d_model * 2 + R * (16 + 8 * cache_el) * 1024
         att_flops = int(sum(4 * (cu[b + 1] - cu[b]) * kv[b] * n for b in range(wl.n_seq)))
-        att_bytes = int(kv.sum()) * 2 * n * 2 + 2 * R * n * 2
+        att_bytes = int(kv.sum()) * 2 * n * cache_el + 2 * R * n * 2
         b_qkv = max(qkv_bytes / (HBM_PEAK_GBS * 1e9), qkv_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
         b_att = max(att_bytes / (HBM_PEAK_GBS * 1e9), att_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
         res[kind] = {"rows_per_layer": R, "ms_per_step": ms, "us_per_layer": ms * 1e3 / L,
@@ -568,6 +638,7 @@ def bench_layers(args, dev):
     tot_ms = sum(res[k]["ms_per_step"] for k in ("full", "cache"))
     block = {k: res.pop(k) for k in W.BLOCK_CACHE_MODES}
     mid = res.pop("cache_mid")
+    e4m3 = res.pop("cache_e4m3")
     value = tot_rows / (tot_ms * 1e-3 / L)
     dom = res["full"]
     out = {
@@ -582,6 +653,7 @@ def bench_layers(args, dev):
         "steps_detail": res,
         "block_cache_steps": block,
         "cache_phase_middle_layer_score": mid,
+        "cache_phase_e4m3_cache": e4m3,
         "unfused_arm_cache_phase": unfused,
         "roofline": {"bound": "mfma", "kernel": "qkv_rope_cachewrite (full refresh)",
                      "achieved": 2 * dom["rows_per_layer"] * sh.d_model * 3 * n / (dom["qkv_us"] * 1e-6) / 1e12,
