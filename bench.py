@@ -45,6 +45,11 @@ def parse():
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--probe", default=None,
+                   help="profiling aid: launch one kernel a few times and print no bench line; "
+                        "attn_full_b32 | attn_cache_b32 (batch-32 attention, full refresh or cache phase) | "
+                        "qkv:<rows>[:<shape>] (the projection of <rows> LLaDA-8B-shaped rows, optionally forcing "
+                        "a tile shape such as g256x128o2)")
     p.add_argument("--no-decode", action="store_true",
                    help="skip the decode-side reductions (logits -> confidence, threshold rule, verify scan)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
@@ -67,6 +72,8 @@ def main():
     dllm.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.probe:
+        return probe(args.probe, dev)
     if args.workload == "llada_b32":
         return bench_layers(args, dev)
     wl = W.make_workload(args.workload)
@@ -442,6 +449,41 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def probe(what, dev, launches=3):
+    """Launch one kernel a few times on a fixed shape (for rocprofv3 counter
+    passes); inputs are random, outputs unused."""
+    import torch
+    from io_aware_kv_amd import dllm
+    from io_aware_kv_amd import workloads as W
+    from io_aware_kv_amd.runner import FlashCacheRunner
+    if what.startswith("attn_"):
+        wl = W.make_workload("llada_b32")
+        run = FlashCacheRunner(wl, device=dev, layers=1)
+        rows = W.full_refresh_rows(wl) if what == "attn_full_b32" else W.config_step_rows(wl, W.seeded_tracked(wl, 1))
+        st = run.upload_step(rows)
+        for c in (run.k_cache[0], run.v_cache[0], st.q):
+            c.copy_(torch.randn(c.shape, device=dev).to(c.dtype))
+        for _ in range(launches):
+            run.attention(st, 0)
+    elif what.startswith("qkv:"):
+        parts = what.split(":")
+        R = int(parts[1])
+        if len(parts) > 2:
+            os.environ["DLLM_QKV_KERNEL"] = parts[2]
+        H, D, d = 32, 128, 4096
+        w = torch.randn(3 * H * D, d, device=dev).mul_(d ** -0.5).to(torch.bfloat16)
+        x = torch.randn(R, d, device=dev).to(torch.bfloat16)
+        pos = torch.arange(R, dtype=torch.int32, device=dev)
+        q = torch.empty(R, H * D, dtype=torch.bfloat16, device=dev)
+        kc, vc = torch.empty_like(q), torch.empty_like(q)
+        for _ in range(launches):
+            dllm.qkv_rope_cachewrite(x, w, pos, pos, q, kc, vc, H, D, 5e5)
+    else:
+        raise SystemExit(f"unknown probe {what}")
+    torch.cuda.synchronize()
+    eprint(f"[probe] {what}: {launches} launches")
 
 
 def bench_decode(args, dev):

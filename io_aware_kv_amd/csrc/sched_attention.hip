@@ -49,6 +49,7 @@ constexpr int kMaxSeq = 1024;
 constexpr int kMaxPages = 1024;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;
+constexpr float kRescaleSlack = 8.f;      // base-2 headroom of the online-softmax reference
 
 struct AttnArgs {
     int n_seq, n_rows, H, n_out, max_kv, max_pages, n_cap, max_mass, pool_pages;
@@ -306,17 +307,38 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     }
     auto issue = [&](int sl, int t) __attribute__((always_inline)) {
         const uint32_t dst = lds_addr(is_v ? v_tile(sl) : k_tile(sl));
+        // (the masked and E4M3 kernels keep only the general path: their
+        // register budget has no room for both)
+        if (!HAS_MASK && !KV8 && t < t_end && __builtin_amdgcn_readfirstlane(s_tile_full[t])) {
+            // every key valid: a wave's copies touch two pages (wave-uniform), so
+            // a copy's source is a page base plus a fixed 32-bit lane offset
+            const int p0 = __builtin_amdgcn_readfirstlane(s_pages[t * 4 + 2 * (wave & 1)]);
+            const int p1 = __builtin_amdgcn_readfirstlane(s_pages[t * 4 + 2 * (wave & 1) + 1]);
+            const int64_t b0 = (int64_t)p0 * 16 * a.n_out, b1 = (int64_t)p1 * 16 * a.n_out;
 #pragma unroll
-        for (int i = 0; i < kDmaPerWave; ++i) {
-            const int q = (wave & 1) * kDmaPerWave + i;            // 4-key group of the tile
-            const int kg = t * kKT + 4 * q + (lane >> 4);
-            const int page = s_pages[min(kg >> 4, last_page)];
-            const bool ok = (t < t_end) & (kg < si.kv) & (page >= 0);
-            const int64_t row = ok ? (int64_t)page * 16 + (kg & 15) : safe_row;
-            if constexpr (KV8)
-                kv8[i] = load_untracked_x2(kv_src8 + row * a.n_out + lslot[i] * 8);
-            else
-                copy16_to_lds(kv_src + row * a.n_out + lslot[i] * 8, __builtin_amdgcn_readfirstlane(dst + q * 1024));
+            for (int i = 0; i < kDmaPerWave; ++i) {
+                const int q = (wave & 1) * kDmaPerWave + i;        // 4-key group of the tile
+                const uint32_t off = (uint32_t)((4 * (q & 3) + (lane >> 4)) * a.n_out + lslot[i] * 8);
+                const int64_t base = i < kDmaPerWave / 2 ? b0 : b1;
+                if constexpr (KV8)
+                    kv8[i] = load_untracked_x2(kv_src8 + base + off);
+                else
+                    copy16_to_lds(kv_src + base + off, __builtin_amdgcn_readfirstlane(dst + q * 1024));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kDmaPerWave; ++i) {
+                const int q = (wave & 1) * kDmaPerWave + i;        // 4-key group of the tile
+                const int kg = t * kKT + 4 * q + (lane >> 4);
+                const int page = s_pages[min(kg >> 4, last_page)];
+                const bool ok = (t < t_end) & (kg < si.kv) & (page >= 0);
+                const int64_t row = ok ? (int64_t)page * 16 + (kg & 15) : safe_row;
+                if constexpr (KV8)
+                    kv8[i] = load_untracked_x2(kv_src8 + row * a.n_out + lslot[i] * 8);
+                else
+                    copy16_to_lds(kv_src + row * a.n_out + lslot[i] * 8,
+                                  __builtin_amdgcn_readfirstlane(dst + q * 1024));
+            }
         }
         if constexpr (HAS_MASK) {
             // words 2t, 2t+1 of every query row of the tile: [row][2]
@@ -465,7 +487,14 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
 #pragma unroll
                 for (int e = 0; e < 4; ++e) mx = fmaxf(mx, st[rt][t4][e]);
             mx = wave_max16(mx);
-            const float m_new = fmaxf(m_run[rt], mx * a.scale_log2);
+            // The exponent reference moves only when the row maximum passes it by
+            // more than kRescaleSlack (base 2): probabilities relative to it stay
+            // below 2^kRescaleSlack, sums and outputs use the same reference, and
+            // the rescale of the accumulators (most of this step's ALU work
+            // while maxima still grow) is mostly skipped.
+            const float mt = mx * a.scale_log2;
+            const bool grow = mt > m_run[rt] + kRescaleSlack;
+            const float m_new = grow ? mt : m_run[rt];
             float rs = 0.f;
 #pragma unroll
             for (int t4 = 0; t4 < 4; ++t4)
@@ -476,7 +505,7 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
                     rs += p;
                 }
             rs = wave_sum16(rs);
-            if (m_new != m_run[rt]) {                     // a row maximum moved: rescale that row
+            if (grow) {                                   // the reference moved: rescale that row
                 const float alpha = __builtin_amdgcn_exp2f(m_run[rt] - m_new);
                 l_run[rt] *= alpha;
 #pragma unroll
