@@ -257,6 +257,7 @@ constexpr int kGroupM = 4;
 constexpr int kGemmLdsPair = 78 * 1024;   // per workgroup when two share a compute unit
 constexpr int kGemmLdsOne = 150 * 1024;   // ring of a workgroup alone on its compute unit
 constexpr int kGemmMaxStages = 8;
+constexpr int kGemmKB = 2;                // stages (of BK) per barrier
 
 template <int WMF, int WGM, int OCC>
 struct GemmCfg {
@@ -274,10 +275,15 @@ struct GemmCfg {
     static constexpr int kWPerGroup = 8 / WMF > 2 ? 8 / WMF : 2;
     static_assert(WGM == 1 || WGM == 2 || WGM == 4, "four waves");
     static_assert(NS * kStage >= 4 * WM * 128, "the epilogue reuses the stages as one WM x 128 tile per wave");
-    static_assert(NS >= 3, "copies at least two stages ahead");
+    // stages per barrier: kGemmKB for the deep-ring small tiles (fewer
+    // barriers per MFMA); one for the 256 x 256 tile, whose copies need the
+    // latency hiding of a new stage every barrier (two per barrier measured
+    // 15% slower), and for the two-per-unit tiles (three-stage rings)
+    static constexpr int KB = (!kBig && NS >= 2 * kGemmKB) ? kGemmKB : 1;
+    static_assert(NS >= 2 * KB && NS >= 3, "two iterations of stages in the ring");
     static_assert(OCC == 1 || NS * kStage * 2 + 8 * BM + 512 <= kGemmLdsPair, "two workgroups per compute unit");
     static_assert(!kBig || OCC == 1, "one 256 x 256 workgroup per compute unit");
-    static_assert((NS - 2) * kInst < 64, "wait counts");
+    static_assert((NS - KB) * kInst < 64, "wait counts");
 };
 
 // Physical 16-byte slot of logical slot 0 in a 64-byte staged row: any 16
@@ -369,9 +375,16 @@ __global__ __launch_bounds__(256, OCC) void qkv_gemm_kernel(QkvArgs a, int n_mti
     // in flight) and its fragment reads have returned; then meet the other
     // waves.  A plain barrier: the fence of __syncthreads would also wait for
     // the stages in flight.
-    const int n_kt = a.d_model / BK;
-    auto stage_barrier = [&](int next) __attribute__((always_inline)) {
-        wait_stages_ahead<kInst, NS - 2>(min(NS - 2, n_kt - 1 - next));
+    // Barriers come every KB stages.  At the barrier before stages kt .. kt+KB-1
+    // every wave has read stages up to kt (stage s's fragments are read while
+    // stage s-1 computes), so their buffers take the copies of this iteration;
+    // stages kt+1 .. kt+KB (read in this iteration) must have landed, while the
+    // copies issued after them may stay in flight.
+    constexpr int KB = C::KB;
+    const int n_kt = a.d_model / BK;                    // a multiple of KB
+    auto stage_barrier = [&](int kt) __attribute__((always_inline)) {
+        const int issued = min(n_kt - 1, max(NS - 1, kt - KB + NS));
+        wait_stages_ahead<kInst, NS - KB>(max(0, issued - min(kt + KB, n_kt - 1)));
         __builtin_amdgcn_s_barrier();
     };
 
@@ -388,39 +401,89 @@ __global__ __launch_bounds__(256, OCC) void qkv_gemm_kernel(QkvArgs a, int n_mti
 #pragma unroll
             for (int i = 0; i < kInst; ++i) issue_one(s, s, i);
     bf16x8 cx[WMF], cw[8];
-    stage_barrier(0);
+    if constexpr (KB == 1) {
+        // one stage per barrier: the copies for stage kt + NS go out during
+        // stage kt, into the buffer stage kt was read from before the barrier
+        auto stage_barrier1 = [&](int next) __attribute__((always_inline)) {
+            wait_stages_ahead<kInst, NS - 2>(min(NS - 2, n_kt - 1 - next));
+            __builtin_amdgcn_s_barrier();
+        };
+        stage_barrier1(0);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) cw[t] = read_w(0, t);
+#pragma unroll
+        for (int i = 0; i < WMF; ++i) cx[i] = read_x(0, i);
+        for (int kt = 0; kt < n_kt; ++kt) {
+            // After the last stage the reads below are of a stale buffer and go
+            // unused: kept unconditional so the fragment registers need no merge.
+            stage_barrier1(kt + 1);
+            const bool more = kt + NS < n_kt;
+            bf16x8 nx[WMF], nw[8];
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < WMF; ++i) {
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cw[t], cx[i], acc[i][t], 0, 0, 0);
+#pragma unroll
+                for (int c = 0; c < C::kCopyPerGroup; ++c)
+                    if (more && i * C::kCopyPerGroup + c < kInst)
+                        issue_one(kt % NS, kt + NS, i * C::kCopyPerGroup + c);
+                // the next step's W fragments early (its first group needs all
+                // eight), x fragment i once this group has used its register
+#pragma unroll
+                for (int c = 0; c < C::kWPerGroup; ++c)
+                    if (i * C::kWPerGroup + c < 8) nw[i * C::kWPerGroup + c] = read_w(kt + 1, i * C::kWPerGroup + c);
+                nx[i] = read_x(kt + 1, i);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int i = 0; i < WMF; ++i) cx[i] = nx[i];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) cw[t] = nw[t];
+        }
+    } else {
+    wait_stages_ahead<kInst, NS - KB>(min(NS - KB, n_kt - 1));   // stage 0 (and maybe more) landed
+    __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int t = 0; t < 8; ++t) cw[t] = read_w(0, t);
 #pragma unroll
     for (int i = 0; i < WMF; ++i) cx[i] = read_x(0, i);
-    for (int kt = 0; kt < n_kt; ++kt) {
-        // After the last stage the reads below are of a stale buffer and go
-        // unused: kept unconditional so the fragment registers need no merge.
-        stage_barrier(kt + 1);
-        const bool more = kt + NS < n_kt;
-        bf16x8 nx[WMF], nw[8];
-        __builtin_amdgcn_sched_barrier(0);
+    for (int kt = 0; kt < n_kt; kt += KB) {
+        stage_barrier(kt);
 #pragma unroll
-        for (int i = 0; i < WMF; ++i) {
-#pragma unroll
-            for (int t = 0; t < 8; ++t)
-                acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cw[t], cx[i], acc[i][t], 0, 0, 0);
-#pragma unroll
-            for (int c = 0; c < C::kCopyPerGroup; ++c)
-                if (more && i * C::kCopyPerGroup + c < kInst)
-                    issue_one(kt % NS, kt + NS, i * C::kCopyPerGroup + c);
-            // the next step's W fragments early (its first group needs all
-            // eight), x fragment i once this group has used its register
-#pragma unroll
-            for (int c = 0; c < C::kWPerGroup; ++c)
-                if (i * C::kWPerGroup + c < 8) nw[i * C::kWPerGroup + c] = read_w(kt + 1, i * C::kWPerGroup + c);
-            nx[i] = read_x(kt + 1, i);
+        for (int sub = 0; sub < KB; ++sub) {
+            const int s = kt + sub;
+            // the stage whose buffer (read before this barrier) takes copies now
+            const int refill = s - KB + 1 + NS;
+            const bool more = refill >= NS && refill < n_kt;
+            bf16x8 nx[WMF], nw[8];
             __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < WMF; ++i) {
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cw[t], cx[i], acc[i][t], 0, 0, 0);
+#pragma unroll
+                for (int c = 0; c < C::kCopyPerGroup; ++c)
+                    if (more && i * C::kCopyPerGroup + c < kInst)
+                        issue_one(refill % NS, refill, i * C::kCopyPerGroup + c);
+                // the next stage's W fragments early (its first group needs all
+                // eight), x fragment i once this group has used its register.
+                // After the last stage these read a stale buffer and go unused:
+                // kept unconditional so the fragment registers need no merge.
+#pragma unroll
+                for (int c = 0; c < C::kWPerGroup; ++c)
+                    if (i * C::kWPerGroup + c < 8) nw[i * C::kWPerGroup + c] = read_w(s + 1, i * C::kWPerGroup + c);
+                nx[i] = read_x(s + 1, i);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int i = 0; i < WMF; ++i) cx[i] = nx[i];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) cw[t] = nw[t];
         }
-#pragma unroll
-        for (int i = 0; i < WMF; ++i) cx[i] = nx[i];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) cw[t] = nw[t];
+    }
     }
 
     // ---- epilogue: rotate in registers (pairs are n-tiles t and t+4), bf16, via LDS to rows ----
@@ -836,7 +899,7 @@ constexpr int kShapeOcc[kNumShapes] = {1, 1, 2, 1, 2, 1, 2, 1, 2};
 // Time of one workgroup alone on a compute unit (T1) and of two sharing one
 // (T2), measured on MI355X for the LLaDA-8B-shaped projection (d_model 4096,
 // 12288 columns; microseconds, used only to rank the shapes)
-constexpr double kShapeT1[kNumShapes] = {119, 89, 91, 73, 74, 87, 73, 57, 55};
+constexpr double kShapeT1[kNumShapes] = {119, 85, 91, 69, 74, 83, 73, 55, 55};
 constexpr double kShapeT2[kNumShapes] = {0, 0, 125, 0, 110, 0, 133, 0, 85};
 constexpr const char* kShapeName[kNumShapes] = {"g256x256", "g128x256", "g128x256o2", "g64x256", "g64x256o2",
                                                 "g256x128", "g256x128o2", "g128x128", "g128x128o2"};
@@ -857,7 +920,7 @@ struct QkvPlan {
 // DLLM_QKV_KERNEL=tiled|gemm|g128x256|... overrides the choice where the shape allows it.
 QkvPlan plan_bf16(int R, int d_model, int n_out, int head_dim) {
     QkvPlan p{};
-    const bool gemm_ok = head_dim == 128 && n_out % 256 == 0 && d_model % kGBK == 0;
+    const bool gemm_ok = head_dim == 128 && n_out % 256 == 0 && d_model % (kGBK * kGemmKB) == 0;
     if (R <= 128 && d_model % 128 == 0) p.kind = kSkinny;
     else p.kind = gemm_ok ? kGemm : kTiled128;
     p.shape = kG256x256;
