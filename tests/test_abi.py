@@ -129,6 +129,18 @@ def test_kernel_entry_points_reject_bad_shapes(lib):
     assert t(1, 32, 512, 32, None, fake, fake, fake, fake, 0, None) == -1
     assert lib.dllm_map_slots(0, 8, 16, 4, 4, fake, fake, fake, fake, None) == -1
 
+    # the E4M3-cache dtype (2): accepted by the cache-writing projection and the
+    # attention with head_dim 128; refused by the calls that have no cache
+    assert lib.dllm_qkv_project(2, 8, 4096, 32, 128, fake, fake, fake, None, 0, None) == -2
+    assert lib.dllm_rope_apply(2, 8, 32, 128, 5e5, fake, fake, fake, None) == -2
+    assert lib.dllm_cache_write(2, 8, 32, 128, fake, fake, fake, fake, 1024, None) == -2
+    assert f(*args(2, 8, 4096, 32, 64, 5e5)) == -2              # E4M3 caches need head_dim 128
+    assert f(*args(2, 0, 4096, 32, 128, 5e5)) == 0               # accepted (empty: nothing to do)
+    assert f(*args(3, 8, 4096, 32, 128, 5e5)) == -2              # no such dtype
+    assert att(dt=2, D=64) == -2
+    assert att(dt=3) == -2
+    assert lib.dllm_qkv_rope_cachewrite_workspace(2, 72, 4096, 32, 128) == 0
+
     # decode side: sizes, dtype, stride, pointers and the workspace size are
     # checked before any launch
     c = lib.dllm_confidence_argmax
