@@ -117,8 +117,8 @@ def main():
         dllm.sched_attention(st.q, st.cu_q, Ks[c], Vs[c], run.page_table, wl.max_pages, st.kv_len, st.o,
                              st.ws_attn, sh.n_heads, sh.head_dim, st.max_kv, mask_bits=st.mask_bits,
                              mask_off=st.mask_off, mass_count=st.mass_count, max_mass_rows=st.max_mass,
-                             mass_accum=run.mass, n_cap=run.n_cap)
-        run.topk(clear_mass=True)
+                             mass_accum=run.mass, n_cap=run.n_cap, mass_overwrite=True)
+        run.topk(clear_mass=False)
 
     # the unfused comparison arm of the same step: slot mapping, projection to
     # memory, rotary, cache write as launches of their own, then attention, top-k
@@ -133,8 +133,8 @@ def main():
         dllm.sched_attention(st.q, st.cu_q, Ks[c], Vs[c], run.page_table, wl.max_pages, st.kv_len, st.o,
                              st.ws_attn, sh.n_heads, sh.head_dim, st.max_kv, mask_bits=st.mask_bits,
                              mask_off=st.mask_off, mass_count=st.mass_count, max_mass_rows=st.max_mass,
-                             mass_accum=run.mass, n_cap=run.n_cap)
-        run.topk(clear_mass=True)
+                             mass_accum=run.mass, n_cap=run.n_cap, mass_overwrite=True)
+        run.topk(clear_mass=False)
 
     stream = torch.cuda.current_stream()
     for i in range(args.warmup):
@@ -158,9 +158,9 @@ def main():
         dllm.sched_attention(st.q, st.cu_q, Ks[c], Vs[c], run.page_table, wl.max_pages, st.kv_len, st.o,
                              st.ws_attn, sh.n_heads, sh.head_dim, st.max_kv, mask_bits=st.mask_bits,
                              mask_off=st.mask_off, mass_count=st.mass_count, max_mass_rows=st.max_mass,
-                             mass_accum=run.mass, n_cap=run.n_cap)
+                             mass_accum=run.mass, n_cap=run.n_cap, mass_overwrite=True)
         e[2].record(stream)
-        run.topk(clear_mass=True)
+        run.topk(clear_mass=False)
         e[3].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
@@ -265,9 +265,10 @@ def main():
                                      stm.o, stm.ws_attn, sh.n_heads, sh.head_dim, stm.max_kv,
                                      mass_count=stm.mass_count if mass else None,
                                      max_mass_rows=stm.max_mass if mass else 0,
-                                     mass_accum=run.mass if mass else None, n_cap=run.n_cap)
+                                     mass_accum=run.mass if mass else None, n_cap=run.n_cap,
+                                     mass_overwrite=mass)
                 if mass:
-                    run.topk(clear_mass=True)
+                    run.topk(clear_mass=False)
             mg = []
             with torch.cuda.stream(cs):
                 for c in range(copies):
@@ -325,8 +326,9 @@ def main():
             dllm.sched_attention(st8.q, st8.cu_q, K8[c], V8[c], run8.page_table, wl.max_pages, st8.kv_len,
                                  st8.o, st8.ws_attn, sh.n_heads, sh.head_dim, st8.max_kv,
                                  mask_bits=st8.mask_bits, mask_off=st8.mask_off, mass_count=st8.mass_count,
-                                 max_mass_rows=st8.max_mass, mass_accum=run8.mass, n_cap=run8.n_cap)
-            run8.topk(clear_mass=True)
+                                 max_mass_rows=st8.max_mass, mass_accum=run8.mass, n_cap=run8.n_cap,
+                                 mass_overwrite=True)
+            run8.topk(clear_mass=False)
         g8 = []
         with torch.cuda.stream(cs):
             for c in range(copies):
@@ -582,12 +584,15 @@ def bench_layers(args, dev):
                 run.cache_update(st, xs[kind][l], Ws[l], l)
             if ev is not None:
                 ev[l][1].record()
-            # cache_mid: the score only from the middle layers 5..20 (1-based)
-            run.attention(st, l, with_mass=mass and (kind != "cache_mid" or 5 <= l + 1 <= 20))
+            # cache_mid: the score only from the middle layers 5..20 (1-based); the
+            # first scoring layer stores its term, the others add theirs
+            first = 4 if kind == "cache_mid" else 0
+            run.attention(st, l, with_mass=mass and (kind != "cache_mid" or 5 <= l + 1 <= 20),
+                          mass_overwrite=l == first)
             if ev is not None:
                 ev[l][2].record()
         if mass:
-            run.topk(clear_mass=True)
+            run.topk(clear_mass=False)
 
     step("full")
     idx = run.top_idx.cpu().numpy()
@@ -613,10 +618,10 @@ def bench_layers(args, dev):
             run8.cache_update(st, xs[kind][l], Ws[l], l)
             if ev is not None:
                 ev[l][1].record()
-            run8.attention(st, l)
+            run8.attention(st, l, mass_overwrite=l == 0)
             if ev is not None:
                 ev[l][2].record()
-        run8.topk(clear_mass=True)
+        run8.topk(clear_mass=False)
 
     step8("full")
     for _ in range(max(1, args.warmup // 10)):

@@ -228,6 +228,10 @@ int dllm_cache_write(dllm_dtype dt, int n_rows, int n_heads, int head_dim, const
  *              mass_count[b]); keys i >= n_cap are not recorded.  Summed over
  *              heads (dllm_topk_tracked does) and over layers (by calling once
  *              per layer) this is formula (2)'s a_i.
+ *   mass_overwrite  nonzero: store the term (= instead of +=), for the first
+ *              scoring layer of a step, so the score needs no clearing between
+ *              steps; entries at or past kv_len[b], and every entry of a
+ *              sequence with no score rows, are then left as they were
  *   o          [R, H*D]            out: attention output
  * Scores are q.k/sqrt(D); a row that sees no key outputs zeros.  When the
  * batch has too few (sequence, head) pairs to fill the GPU, keys are split
@@ -244,8 +248,8 @@ int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_heads, int 
                          const int32_t* page_table, int max_pages, const int32_t* kv_len,
                          const uint32_t* mask_bits, const int64_t* mask_off, int64_t mask_words,
                          const int32_t* mass_count, int max_mass_rows, float* mass_accum,
-                         int n_cap, void* o, void* workspace, size_t workspace_bytes,
-                         hipStream_t stream);
+                         int mass_overwrite, int n_cap, void* o, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
 
 /*
  * a6: per-sequence top-k of the accumulated score over eligible positions.

@@ -66,6 +66,7 @@ struct AttnArgs {
     int64_t mask_words;
     const int32_t* mass_count;
     float* mass_accum;      // [n_seq, H, n_cap], this head's term added per layer
+    int mass_overwrite;     // store the term instead of adding it (first scoring layer)
     uint16_t* o;
     int splits;             // key splits per (sequence, head, query tile); 1 = fused path
     float* part_o;          // split mode: [item][kQT][kHD] unnormalised outputs
@@ -705,7 +706,7 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int kk = kw0 + 4 * g + e;
-            mold[sl][e] = (ln == 0 && kk < kmax) ? macc[kk] : 0.f;
+            mold[sl][e] = (ln == 0 && kk < kmax && !a.mass_overwrite) ? macc[kk] : 0.f;
         }
     };
     auto gstep = [&](auto S, int i) __attribute__((always_inline)) {
@@ -943,7 +944,8 @@ __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
     }
     float* macc = a.mass_accum + ((int64_t)b * a.H + h) * a.n_cap;
     const int key_t = kt * kKT + tid;
-    const float mold = (tid < kKT && key_t < si.kv && key_t < a.n_cap) ? macc[key_t] : 0.f;
+    const float mold =
+        (tid < kKT && key_t < si.kv && key_t < a.n_cap && !a.mass_overwrite) ? macc[key_t] : 0.f;
     // keys: need the page entry
     const bool page_ok = page >= 0 && page < a.pool_pages;
     const int kw = kw0 + ln;                                 // this lane's key row for the A operand
@@ -1097,7 +1099,8 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a, const
     __syncthreads();
     const float norm = 1.f / ((float)a.H * (float)mb);
     float* macc = a.mass_accum + ((int64_t)b * a.H + h) * a.n_cap;
-    for (int j = tid; j < si.kv && j < a.n_cap; j += kF32Threads) macc[j] += s_colsum[j] * norm;
+    for (int j = tid; j < si.kv && j < a.n_cap; j += kF32Threads)
+        macc[j] = (a.mass_overwrite ? 0.f : macc[j]) + s_colsum[j] * norm;
 }
 
 // Items = (sequence, head, 128-row query tile[, key split]); the launch is
@@ -1183,7 +1186,7 @@ extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_
                                     const int32_t* kv_len, const uint32_t* mask_bits,
                                     const int64_t* mask_off, int64_t mask_words,
                                     const int32_t* mass_count, int max_mass_rows,
-                                    float* mass_accum, int n_cap, void* o, void* workspace,
+                                    float* mass_accum, int mass_overwrite, int n_cap, void* o, void* workspace,
                                     size_t workspace_bytes, hipStream_t stream) {
     int st = check_attn(dt, n_seq, n_rows, n_heads, head_dim, page_size, max_kv, n_cap);
     if (st != DLLM_OK) return st;
@@ -1227,6 +1230,7 @@ extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_
     a.mask_words = mask_words;
     a.mass_count = want_mass ? mass_count : nullptr;
     a.mass_accum = want_mass ? mass_accum : nullptr;
+    a.mass_overwrite = mass_overwrite != 0;
     a.o = (uint16_t*)o;
     a.splits = splits;
     if (splits > 1) {

@@ -66,7 +66,7 @@ def load() -> ctypes.CDLL:
     lib.dllm_sched_attention_workspace.restype = _sz
     lib.dllm_sched_attention.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                          _i64, _vp, _i32, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _i32,
-                                         _vp, _vp, _sz, _vp]
+                                         _i32, _vp, _vp, _sz, _vp]
     lib.dllm_topk_tracked.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp]
     lib.dllm_confidence_workspace.argtypes = [_i32, _i32]
     lib.dllm_confidence_workspace.restype = _sz
@@ -216,7 +216,7 @@ def sched_attention_workspace(dt: int, n_seq: int, n_rows: int, n_heads: int, he
 def sched_attention(q, cu_q, k_cache, v_cache, page_table, max_pages: int, kv_len, o, workspace,
                     n_heads: int, head_dim: int, max_kv: int, mask_bits=None, mask_off=None,
                     mass_count=None, max_mass_rows: int = 0, mass_accum=None, n_cap: int = 0,
-                    page_size: int = PAGE, stream=None) -> None:
+                    page_size: int = PAGE, mass_overwrite: bool = False, stream=None) -> None:
     dt = cache_dtype_code(q, k_cache)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     mask_words = 0 if mask_bits is None else mask_bits.numel()
@@ -224,7 +224,7 @@ def sched_attention(q, cu_q, k_cache, v_cache, page_table, max_pages: int, kv_le
         dt, cu_q.numel() - 1, q.shape[0], n_heads, head_dim, page_size, max_kv, _ptr(q), _ptr(cu_q),
         _ptr(k_cache), _ptr(v_cache), k_cache.shape[0], _ptr(page_table), max_pages, _ptr(kv_len),
         _ptr(mask_bits), _ptr(mask_off), mask_words, _ptr(mass_count), max_mass_rows,
-        _ptr(mass_accum), n_cap, _ptr(o), _ptr(workspace), ws_bytes, _stream(stream)))
+        _ptr(mass_accum), int(bool(mass_overwrite)), n_cap, _ptr(o), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def topk_tracked(mass, eligible, k: int, idx, val, count, clear_mass: bool = False, stream=None) -> None:

@@ -134,20 +134,25 @@ class FlashCacheRunner:
         dllm.rope_apply(st.qkv_raw, st.pos, st.q, self.H, self.D, self.wl.shape.rope_base)
         dllm.cache_write(st.qkv_raw, st.slot, self.k_cache[layer], self.v_cache[layer], self.H, self.D)
 
-    def attention(self, st: StepDevice, layer: int = 0, with_mass: bool = True) -> None:
+    def attention(self, st: StepDevice, layer: int = 0, with_mass: bool = True,
+                  mass_overwrite: bool = False) -> None:
+        """mass_overwrite: this layer's term replaces the score (the first
+        scoring layer of a step; then the top-k need not clear it)."""
         dllm.sched_attention(st.q, st.cu_q, self.k_cache[layer], self.v_cache[layer], self.page_table,
                              self.wl.max_pages, st.kv_len, st.o, st.ws_attn, self.H, self.D, st.max_kv,
                              mask_bits=st.mask_bits, mask_off=st.mask_off,
                              mass_count=st.mass_count if with_mass else None,
                              max_mass_rows=st.max_mass if with_mass else 0,
-                             mass_accum=self.mass if with_mass else None, n_cap=self.n_cap)
+                             mass_accum=self.mass if with_mass else None, n_cap=self.n_cap,
+                             mass_overwrite=mass_overwrite)
 
     def topk(self, clear_mass: bool = True) -> None:
         dllm.topk_tracked(self.mass, self.eligible, self.wl.shape.top_k, self.top_idx, self.top_val,
                           self.top_cnt, clear_mass=clear_mass)
 
     def layer_step(self, st: StepDevice, x: torch.Tensor, w: torch.Tensor, layer: int = 0,
-                   fused_slots: bool = True, unfused: bool = False, with_mass: bool = True) -> None:
+                   fused_slots: bool = True, unfused: bool = False, with_mass: bool = True,
+                   mass_overwrite: bool = False) -> None:
         """a0..a5 of one layer: slots and the fused cache update (one call, or
         the slot mapping as a call of its own; or the unfused three-launch arm),
         then attention + mass."""
@@ -159,4 +164,4 @@ class FlashCacheRunner:
         else:
             self.map_slots(st)
             self.cache_update(st, x, w, layer)
-        self.attention(st, layer, with_mass=with_mass)
+        self.attention(st, layer, with_mass=with_mass, mass_overwrite=mass_overwrite)

@@ -110,7 +110,7 @@ def test_kernel_entry_points_reject_bad_shapes(lib):
     def att(dt=1, n_seq=1, R=8, H=32, D=128, page=16, max_kv=512, mask=None, off=None, words=0,
             mass=None, max_mass=0, macc=None, n_cap=512, ws=1 << 30, max_pages=32):
         return a(dt, n_seq, R, H, D, page, max_kv, fake, fake, fake, fake, 1 << 16, fake, max_pages,
-                 fake, mask, off, words, mass, max_mass, macc, n_cap, fake, fake, ws, None)
+                 fake, mask, off, words, mass, max_mass, macc, 0, n_cap, fake, fake, ws, None)
     assert att(D=64) == -2                                   # bf16 kernel is D = 128
     assert att(page=32) == -2
     assert att(max_kv=0) == -1

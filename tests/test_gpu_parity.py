@@ -167,3 +167,30 @@ def test_unfused_arm_parity(name, step, gpu):
     c = case(name)
     g = run_gpu_step(c, step, gpu, unfused=True)
     compare_step(c, g, step)
+
+
+@pytest.mark.parametrize("name", ["llada_b1", "mixed_b8", "tiny_f32"])
+def test_score_overwrite(name, gpu):
+    """mass_overwrite stores the layer's term instead of adding it: from a
+    score buffer full of a sentinel, the step's score equals the oracle's term
+    for keys below each sequence's kv_len (the split merge launch, the fused
+    score pass and the fp32 kernel), and the sentinel stays past kv_len."""
+    import torch
+    from io_aware_kv_amd.runner import FlashCacheRunner
+    c = case(name)
+    wl = c.wl
+    log(f"[gpu] score overwrite {name}")
+    run = FlashCacheRunner(wl, device=gpu, layers=1)
+    run.k_cache[0].copy_(run.to_device_array(c.to_cache_raw(c.k1_in)))
+    run.v_cache[0].copy_(run.to_device_array(c.to_cache_raw(c.v1_in)))
+    run.mass.fill_(5.0)
+    st = run.upload_step(c.rows1)
+    run.layer_step(st, run.to_device_array(c.x1_raw), run.to_device_array(c.w_raw), 0, mass_overwrite=True)
+    torch.cuda.synchronize()
+    m = run.mass.cpu().numpy()
+    kv = c.rows1.kv_len
+    ma, mr = MASS_TOL[c.kind]
+    for b in range(wl.n_seq):
+        k = min(int(kv[b]), run.n_cap)
+        close(head_sum(m[b:b + 1, :, :k])[0], c.out1["mass"][b, :k], ma, mr, f"{name} seq {b} score")
+        assert np.all(m[b, :, k:] == 5.0)
