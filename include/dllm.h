@@ -236,12 +236,18 @@ int dllm_cache_write(dllm_dtype dt, int n_rows, int n_heads, int head_dim, const
  * Scores are q.k/sqrt(D); a row that sees no key outputs zeros.  When the
  * batch has too few (sequence, head) pairs to fill the GPU, keys are split
  * over workgroups and a second kernel merges them (workspace: per split, fp32
- * partial outputs and row statistics).
- * Errors: INVALID_ARG (also cache_rows < 16), UNSUPPORTED (dtype/D/page_size/
- * n_seq > 1024/max_pages > 1024/bf16 score over more than 8704 keys).
+ * partial outputs and row statistics).  Otherwise, when a score is formed
+ * (bf16 paths), the workspace holds the window rows' bf16 probabilities of
+ * every key tile (B*H*ceil(max_kv/64)*max_mass_rows*(128+4) bytes), so the
+ * score needs no second read of K.  dllm_sched_attention_workspace reports
+ * the bytes a call with these sizes needs (max_mass_rows = 0: no score; the
+ * fp32 path needs none); the call checks workspace_bytes against it.
+ * Errors: INVALID_ARG (also cache_rows < 16, a short workspace), UNSUPPORTED
+ * (dtype/D/page_size/n_seq > 1024/max_pages > 1024/bf16 score over more than
+ * 8704 keys).
  */
 size_t dllm_sched_attention_workspace(dllm_dtype dt, int n_seq, int n_rows, int n_heads,
-                                      int head_dim, int max_kv, int n_cap);
+                                      int head_dim, int max_kv, int n_cap, int max_mass_rows);
 int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_heads, int head_dim,
                          int page_size, int max_kv, const void* q, const int32_t* cu_q,
                          const void* k_cache, const void* v_cache, int64_t cache_rows,

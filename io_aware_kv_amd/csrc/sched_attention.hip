@@ -25,12 +25,16 @@
 // matching V^T fragment is read from the row-major V tile with the gfx950 LDS
 // transpose read.  Softmax is online in fp32 (base 2).
 //
-// Formula (2) needs the masked-window rows' final log-sum-exp, so their
-// scores are recomputed after the main pass: by the workgroup of the
-// sequence's first query tile when keys are not split, else by the merge
-// launch.  Either way each (sequence, head, key) term is added to
-// mass_accum[b][h][key] by exactly one workgroup, in a fixed order: no
-// atomics, no cross-workgroup synchronisation, deterministic results.
+// Formula (2) needs the masked-window rows' final log-sum-exp.  When keys are
+// not split, the workgroup of the sequence's first query tile keeps those
+// rows' bf16 probabilities of every key tile (the values its P V product
+// uses) and their exponent references in a workspace, and after the main pass
+// rescales them with the final log-sum-exp and sums the columns: the keys are
+// read once.  When keys are split, the merge launch recomputes the rows'
+// scores from the merged statistics.  Either way each (sequence, head, key)
+// term is added to mass_accum[b][h][key] by exactly one workgroup, in a fixed
+// order: no atomics, no cross-workgroup synchronisation, deterministic
+// results.
 #include <math.h>
 #include <stdlib.h>
 
@@ -50,6 +54,7 @@ constexpr int kMaxPages = 1024;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;
 constexpr float kRescaleSlack = 8.f;      // base-2 headroom of the online-softmax reference
+constexpr int kMassChunk = 16;            // key tiles per round of the score pass (256 threads x 4 keys)
 
 struct AttnArgs {
     int n_seq, n_rows, H, n_out, max_kv, max_pages, n_cap, max_mass, pool_pages;
@@ -67,6 +72,12 @@ struct AttnArgs {
     const int32_t* mass_count;
     float* mass_accum;      // [n_seq, H, n_cap], this head's term added per layer
     int mass_overwrite;     // store the term instead of adding it (first scoring layer)
+    // unsplit path: the window rows' probabilities of every key tile (bf16,
+    // [b*H + h][tile][max_mass][64 keys]) and each row's exponent reference
+    // after that tile ([b*H + h][tile][max_mass]), for the score pass
+    uint16_t* mass_p;
+    float* mass_ref;
+    int mass_tiles;
     uint16_t* o;
     int splits;             // key splits per (sequence, head, query tile); 1 = fused path
     float* part_o;          // split mode: [item][kQT][kHD] unnormalised outputs
@@ -159,8 +170,8 @@ constexpr int kAttnThreads = 256;       // 4 waves
 constexpr int kMaskStageBytes = 2048;   // up to 256 rows x 2 mask words per stage
 constexpr int kStageBytes = 2 * kTileH * 2 + kMaskStageBytes;
 constexpr int kMaxSplits = 16;          // key splits per (sequence, head, query tile)
-constexpr int kMassQOffset = 1024;      // after the main pass: window-row queries at this LDS offset
-static_assert(kQT * 4 <= kMassQOffset && kMassQOffset + kQT * kHD * 2 <= 2 * kStageBytes, "tail LDS layout");
+constexpr int kMassQOffset = 1024;      // after the main pass: the score pass's factors at this LDS offset
+static_assert(kQT * 4 <= kMassQOffset && kMassQOffset + kMassChunk * kQT * 4 <= 2 * kStageBytes, "tail LDS layout");
 
 __device__ __forceinline__ int swz_k(int key) { return (key + 4 * (key >> 4)) & 15; }
 __device__ __forceinline__ int swz_v(int key) { return 2 * ((key & 3) + 4 * ((key >> 3) & 1)); }
@@ -197,6 +208,7 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     static_assert(QT * 8 <= kMaskStageBytes, "layout");
     static_assert(NS * kPerStage + 4 * RT < 64, "wait counts");
     static_assert(kRing >= (4 * kMaxSeq + 1) * 4, "the schedule scan borrows the ring");
+    static_assert(QT == kQT, "the window rows of formula (2) fit the first query tile");
     // one LDS allocation: the ring (which the schedule scan borrows first), then the page tables
     __shared__ __attribute__((aligned(16))) uint8_t lds[kRing + (kMaxPages + 1) * 4 + kMaxPages / 4];
     int* s_pref = reinterpret_cast<int*>(lds);                                    // [kMaxSeq + 1], scheduling only
@@ -294,12 +306,22 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     // window rows of formula (2) (query tile 0 only); loaded before any copy is issued
     const bool want_mass = qt == 0 && a.mass_accum != nullptr && a.mass_count != nullptr;
     const int mb_in = want_mass ? a.mass_count[b] : 0;
+    // unsplit: window rows whose probabilities the main pass keeps
+    const int mbp = a.splits == 1 ? max(0, min(mb_in, min(a.max_mass, min(si.rows, kQT)))) : 0;
+    // this (sequence, head)'s probability rows and references (wave-uniform bases)
+    const int64_t mass_item0 = (int64_t)(b * a.H + h) * a.mass_tiles * a.max_mass;
+    uint16_t* const mp_item = mbp > 0 ? a.mass_p + mass_item0 * kKT : nullptr;
+    float* const mr_item = mbp > 0 ? a.mass_ref + mass_item0 : nullptr;
 
     // ---- copies: K groups (waves 0, 1) or V groups (waves 2, 3) of 4 keys; mask words; query tile ----
     const bool is_v = wave >= 2;
     const uint16_t* kv_src = (is_v ? a.v : a.k) + h * kHD;
     const uint8_t* kv_src8 = reinterpret_cast<const uint8_t*>(is_v ? a.v : a.k) + h * kHD;
-    u32x2 kv8[KV8 ? kDmaPerWave : 1];                   // KV8: this wave's codes of the tile in flight
+    // KV8: this wave's codes of the tile in flight.  Ordinary loads, which the
+    // compiler tracks: it waits before any use or register copy of them (with
+    // a load it cannot see, the register allocator once copied a code pair
+    // ahead of the wait and staged stale codes).
+    u32x2 kv8[KV8 ? kDmaPerWave : 1];
     int lslot[kDmaPerWave];
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
@@ -322,7 +344,7 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
                 const uint32_t off = (uint32_t)((4 * (q & 3) + (lane >> 4)) * a.n_out + lslot[i] * 8);
                 const int64_t base = i < kDmaPerWave / 2 ? b0 : b1;
                 if constexpr (KV8)
-                    kv8[i] = load_untracked_x2(kv_src8 + base + off);
+                    kv8[i] = *(const u32x2*)(kv_src8 + base + off);
                 else
                     copy16_to_lds(kv_src + base + off, __builtin_amdgcn_readfirstlane(dst + q * 1024));
             }
@@ -335,7 +357,7 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
                 const bool ok = (t < t_end) & (kg < si.kv) & (page >= 0);
                 const int64_t row = ok ? (int64_t)page * 16 + (kg & 15) : safe_row;
                 if constexpr (KV8)
-                    kv8[i] = load_untracked_x2(kv_src8 + row * a.n_out + lslot[i] * 8);
+                    kv8[i] = *(const u32x2*)(kv_src8 + row * a.n_out + lslot[i] * 8);
                 else
                     copy16_to_lds(kv_src + row * a.n_out + lslot[i] * 8,
                                   __builtin_amdgcn_readfirstlane(dst + q * 1024));
@@ -364,8 +386,7 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
 #pragma unroll
             for (int i = 0; i < kDmaPerWave; ++i) {
                 const int q = (wave & 1) * kDmaPerWave + i;
-                const u32x2 w = fence_value(kv8[i]);
-                *(bf16x8*)(dst + q * 1024 + 16 * lane) = e4m3x8_to_bf16(w[0], w[1]);
+                *(bf16x8*)(dst + q * 1024 + 16 * lane) = e4m3x8_to_bf16(kv8[i][0], kv8[i][1]);
             }
         }
     };
@@ -523,6 +544,17 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
                 u[3] = pack_bf16x2(st[rt][2 * c + 1][2], st[rt][2 * c + 1][3]);
                 pf[rt][c] = __builtin_bit_cast(bf16x8, u);
             }
+            // the window rows keep this tile's probabilities for the score pass
+            if (wrow + rt * 16 < mbp) {                   // uniform per wave
+                const int my_row = wrow + rt * 16 + ln;
+                if (my_row < mbp) {
+                    const uint32_t pt = (uint32_t)(t * a.max_mass + my_row);   // < 2^15 rows per item
+                    uint16_t* prow = mp_item + (pt * kKT + 8 * g);
+                    *(bf16x8*)prow = pf[rt][0];
+                    *(bf16x8*)(prow + 32) = pf[rt][1];
+                    if (g == 0) mr_item[pt] = m_run[rt];
+                }
+            }
         }
         // O^T += V^T P^T.  V^T fragments: source lane ln of group g points at key
         // c*32 + 8g + 4*hf + (ln >> 2), column dt*16 + 4*(ln & 3)
@@ -590,9 +622,8 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     __syncthreads();                                    // every copy has been waited for above
 
     // LDS after the main pass (the ring is free): final log-sum-exp (base 2) of
-    // the tile's rows, the window rows' queries
+    // the tile's rows, then the score pass's factors
     float* s_lse = reinterpret_cast<float*>(lds);                        // [kQT]
-    uint16_t* s_qm = reinterpret_cast<uint16_t*>(lds + kMassQOffset);    // [kQT][kHD], row-swizzled
 
     if (a.splits > 1) {
         // ---- split mode (QT == kQT): publish the unnormalised partial; attn_finish_kernel
@@ -634,141 +665,55 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     }
 
     // ---- formula (2): this head's column mass over every key of the sequence ----
-    // The window rows' log-sum-exp is final only now, so their scores are
-    // recomputed.  Their queries are staged in LDS; wave w takes the 16-key
-    // groups w, w + 4, ...: the group's key fragments come straight from the
-    // cache rows into registers (A operand, keys as rows; the 16 keys share one
-    // page), up to four groups ahead, with the mask words and the running score they
-    // add to.  S^T = K Q^T gives a lane four keys of one window row; a row
-    // tile's column sums are DPP sums over its 16 lanes.  No LDS traffic for
-    // keys and no barrier in the loop; each key's sum is formed in a fixed
-    // order and added to mass_accum once, by this workgroup only.
+    // The main pass kept the window rows' probabilities of every key tile
+    // relative to the row's exponent reference at that tile; with the final
+    // log-sum-exp each is rescaled by exp2(reference - lse).  Each thread owns
+    // four consecutive keys of a tile and sums over the window rows in a fixed
+    // order; each key's term is added to mass_accum once, by this workgroup
+    // only.  No K re-read and no score recompute.
     if (!want_mass) return;
-    const int mb = max(0, min(mb_in, min(a.max_mass, min(si.rows, kQT))));
+    const int mb = mbp;
     if (mb == 0 || si.kv == 0) return;
-    {
-        u32x4 qv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = min(tid + i * kAttnThreads, mb * 16 - 1);
-            qv[i] = *(const u32x4*)(a.q + (int64_t)(seq_r0 + (c >> 4)) * a.n_out + h * kHD + (c & 15) * 8);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = tid + i * kAttnThreads;
-            const int row = c >> 4;
-            if (c < mb * 16) *(u32x4*)(s_qm + row * kHD + (((c & 15) ^ swz_k(row)) * 8)) = qv[i];
-        }
-    }
-    lds_sync();                                              // s_qm, and s_lse of every window row
+    __syncthreads();                                         // every wave's probabilities and s_lse
     const float norm = 1.f / ((float)a.H * (float)mb);
     float* macc = a.mass_accum + ((int64_t)b * a.H + h) * a.n_cap;
     const int kmax = min(si.kv, a.n_cap);
-    const int rtiles = (mb + 15) / 16;
-    float lse_l[kQT / 16];
-#pragma unroll
-    for (int rt = 0; rt < kQT / 16; ++rt) {
-        const int row = rt * 16 + ln;
-        lse_l[rt] = row < mb ? s_lse[row] : INFINITY;
-    }
-    const int ngroups = (kmax + 15) / 16;
-    const int my_groups = ngroups > wave ? (ngroups - 1 - wave) / 4 + 1 : 0;
-    constexpr int kMR = HAS_MASK ? 2 : 4;                       // key groups in flight (registers)
-    bf16x8 kr[KV8 ? 1 : kMR][4];
-    uint2 kr8[KV8 ? kMR : 1][4];                                // KV8: codes, decoded when used
-    uint32_t mw[kMR][kQT / 16];
-    float mold[kMR][4];
-    // Groups are taken last to first: the main pass has just streamed the
-    // sequence's keys in ascending order, so its last tiles are the likeliest
-    // to be still in L2 or the Infinity Cache.
-    auto gload = [&](auto S, int i) __attribute__((always_inline)) {
-        constexpr int sl = decltype(S)::value;
-        const int kw0 = 16 * (wave + 4 * max(my_groups - 1 - i, 0));
-        const int page = s_pages[min(kw0 >> 4, last_page)];
-        const int key = kw0 + ln;
-        const int64_t row = (page >= 0 && key < si.kv) ? (int64_t)page * 16 + (key & 15) : safe_row;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            if constexpr (KV8)
-                kr8[sl][ks] = *(const uint2*)(reinterpret_cast<const uint8_t*>(a.k) + row * a.n_out + h * kHD +
-                                              ks * 32 + g * 8);
-            else
-                kr[sl][ks] = *(const bf16x8*)(a.k + row * a.n_out + h * kHD + ks * 32 + g * 8);
+    const int ntiles_m = (kmax + kKT - 1) / kKT;
+    float* s_fac = reinterpret_cast<float*>(lds + kMassQOffset);   // [kMassChunk][mb]
+    for (int t0 = 0; t0 < ntiles_m; t0 += kMassChunk) {
+        for (int j = tid; j < kMassChunk * mb; j += kAttnThreads) {
+            const int tc = j / mb, i = j % mb;
+            const int t = t0 + tc;
+            s_fac[j] = t < ntiles_m ? exp2f(mr_item[t * a.max_mass + i] - s_lse[i]) : 0.f;
         }
-        if constexpr (HAS_MASK) {
+        __syncthreads();
+        const int tc = tid / (kKT / 4), kq = tid % (kKT / 4);
+        const int t = t0 + tc;
+        if (t < ntiles_m) {
+            const uint16_t* pcol = mp_item + ((uint32_t)(t * a.max_mass) * kKT + 4 * kq);
+            float cs[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int i0 = 0; i0 < mb; i0 += 8) {
+                uint2 w[8];
 #pragma unroll
-            for (int rt = 0; rt < kQT / 16; ++rt) {
-                const int64_t wi = mask_row0 + (int64_t)min(rt * 16 + ln, mb - 1) * mwords + kw0 / 32;
-                mw[sl][rt] = (rt < rtiles && wi >= 0 && wi < a.mask_words) ? a.mask[wi] : 0u;
-            }
-        }
-        // running scores of keys kw0 + 4g + e (the lanes with ln == 0 update them)
+                for (int u = 0; u < 8; ++u)
+                    w[u] = i0 + u < mb ? *(const uint2*)(pcol + (i0 + u) * kKT) : make_uint2(0u, 0u);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int kk = kw0 + 4 * g + e;
-            mold[sl][e] = (ln == 0 && kk < kmax && !a.mass_overwrite) ? macc[kk] : 0.f;
-        }
-    };
-    auto gstep = [&](auto S, int i) __attribute__((always_inline)) {
-        constexpr int sl = decltype(S)::value;                 // i % kMR
-        gload(Ic<(sl + kMR - 1) % kMR>{}, i + kMR - 1);
-        if (i < my_groups) {
-            const int kw0 = 16 * (wave + 4 * (my_groups - 1 - i));
-            const int page = s_pages[min(kw0 >> 4, last_page)];
-            uint32_t kvalid = 0;                               // C layout: register e of lane group g is key kw0 + 4g + e
-#pragma unroll
-            for (int e = 0; e < 4; ++e) kvalid |= (page >= 0 && kw0 + 4 * g + e < si.kv ? 1u : 0u) << e;
-            float csum[4] = {0.f, 0.f, 0.f, 0.f};
-            bf16x8 kf[4];
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                if constexpr (KV8) kf[ks] = e4m3x8_to_bf16(kr8[sl][ks].x, kr8[sl][ks].y);
-                else kf[ks] = kr[sl][ks];
-            }
-#pragma unroll
-            for (int rt = 0; rt < kQT / 16; ++rt) {
-                if (rt >= rtiles) continue;
-                const int row = rt * 16 + ln;                  // this lane's window row (B operand / C column)
-                bf16x8 qb[4];
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    qb[ks] = *(const bf16x8*)(s_qm + row * kHD + (((ks * 4 + g) ^ swz_k(row)) * 8));
-                f32x4 st = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qb[ks], st, 0, 0, 0);
-                uint32_t vis = row < mb ? kvalid : 0u;
-                if constexpr (HAS_MASK) vis &= (mw[sl][rt] >> ((kw0 + 4 * g) & 31)) & 0xfu;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float p = ((vis >> e) & 1u) ? exp2f(fmaf(st[e], a.scale_log2, -lse_l[rt])) : 0.f;
-                    csum[e] += row16_sum(p);
+                for (int u = 0; u < 8; ++u) {
+                    if (i0 + u >= mb) continue;
+                    const float f = s_fac[tc * mb + i0 + u];
+                    cs[0] += bf16_bits_to_f32(w[u].x & 0xffffu) * f;
+                    cs[1] += bf16_bits_to_f32(w[u].x >> 16) * f;
+                    cs[2] += bf16_bits_to_f32(w[u].y & 0xffffu) * f;
+                    cs[3] += bf16_bits_to_f32(w[u].y >> 16) * f;
                 }
             }
-            if (ln == 0) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int kk = kw0 + 4 * g + e;
-                    if (kk < kmax) macc[kk] = mold[sl][e] + csum[e] * norm;
-                }
+            for (int e = 0; e < 4; ++e) {
+                const int kk = t * kKT + 4 * kq + e;
+                if (kk < kmax) macc[kk] = (a.mass_overwrite ? 0.f : macc[kk]) + cs[e] * norm;
             }
         }
-    };
-    gload(Ic<0>{}, 0);
-    if constexpr (kMR == 4) {
-        gload(Ic<1>{}, 1);
-        gload(Ic<2>{}, 2);
-        for (int i = 0; i < my_groups; i += 4) {
-            gstep(Ic<0>{}, i);
-            gstep(Ic<1>{}, i + 1);
-            gstep(Ic<2>{}, i + 2);
-            gstep(Ic<3>{}, i + 3);
-        }
-    } else {
-        for (int i = 0; i < my_groups; i += 2) {
-            gstep(Ic<0>{}, i);
-            gstep(Ic<1>{}, i + 1);
-        }
+        __syncthreads();
     }
 }
 
@@ -1140,6 +1085,20 @@ size_t split_workspace(int n_seq, int n_rows, int n_heads, int splits) {
     return (size_t)items * kQT * (kHD + 2) * sizeof(float);
 }
 
+int mass_tiles(int max_kv) { return (max_kv + kKT - 1) / kKT; }
+
+// fused path with a score: the window rows' bf16 probabilities of every key
+// tile and their exponent references, per (sequence, head)
+size_t mass_workspace(int n_seq, int n_heads, int max_kv, int max_mass, int splits) {
+    if (splits > 1 || max_mass <= 0) return 0;
+    return (size_t)n_seq * n_heads * mass_tiles(max_kv) * max_mass * (kKT * sizeof(uint16_t) + sizeof(float));
+}
+
+size_t bf16_workspace(int n_seq, int n_rows, int n_heads, int max_kv, int max_mass, int splits) {
+    return split_workspace(n_seq, n_rows, n_heads, splits) +
+           mass_workspace(n_seq, n_heads, max_kv, max_mass, splits);
+}
+
 template <bool KV8>
 void launch_attn(const AttnArgs& a, dim3 grid, dim3 block, bool mask, hipStream_t stream) {
     if (mask) hipLaunchKernelGGL((attn_bf16_kernel<2, 2, true, KV8>), grid, block, 0, stream, a);
@@ -1174,9 +1133,11 @@ int check_attn(dllm_dtype dt, int n_seq, int n_rows, int n_heads, int head_dim, 
 
 extern "C" size_t dllm_sched_attention_workspace(dllm_dtype dt, int n_seq, int n_rows,
                                                  int n_heads, int head_dim, int max_kv,
-                                                 int n_cap) {
+                                                 int n_cap, int max_mass_rows) {
     if (check_attn(dt, n_seq, n_rows, n_heads, head_dim, 16, max_kv, n_cap) != DLLM_OK) return 0;
-    return split_workspace(n_seq, n_rows, n_heads, choose_splits(dt, n_seq, n_rows, n_heads, max_kv));
+    if (dt == DLLM_F32 || max_mass_rows < 0 || max_mass_rows > kQT) return 0;
+    return bf16_workspace(n_seq, n_rows, n_heads, max_kv, max_mass_rows,
+                          choose_splits(dt, n_seq, n_rows, n_heads, max_kv));
 }
 
 extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_heads,
@@ -1204,7 +1165,8 @@ extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_
         if (dt != DLLM_F32) DLLM_CHECK_SUP((max_kv < n_cap ? max_kv : n_cap) <= 8704);
     }
     const int splits = choose_splits(dt, n_seq, n_rows, n_heads, max_kv);
-    const size_t ws_need = split_workspace(n_seq, n_rows, n_heads, splits);
+    const int mass_rows = want_mass ? max_mass_rows : 0;
+    const size_t ws_need = dt == DLLM_F32 ? 0 : bf16_workspace(n_seq, n_rows, n_heads, max_kv, mass_rows, splits);
     DLLM_CHECK_ARG(workspace_bytes >= ws_need && (ws_need == 0 || workspace != nullptr));
 
     AttnArgs a{};
@@ -1237,6 +1199,10 @@ extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_
         const int64_t items = first_items(n_seq, n_rows, n_heads, splits);
         a.part_o = (float*)workspace;
         a.part_ml = a.part_o + items * kQT * kHD;
+    } else if (dt != DLLM_F32 && mass_rows > 0) {
+        a.mass_tiles = mass_tiles(max_kv);
+        a.mass_p = (uint16_t*)workspace;
+        a.mass_ref = (float*)(a.mass_p + (int64_t)n_seq * n_heads * a.mass_tiles * mass_rows * kKT);
     }
     if (dt != DLLM_F32) {
         // 128-row query tiles: four waves of 32 rows (two 16-row MFMA tiles each)

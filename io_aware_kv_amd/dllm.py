@@ -62,7 +62,7 @@ def load() -> ctypes.CDLL:
     lib.dllm_qkv_project.argtypes = [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
     lib.dllm_rope_apply.argtypes = [_i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp]
     lib.dllm_cache_write.argtypes = [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp]
-    lib.dllm_sched_attention_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32]
+    lib.dllm_sched_attention_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]
     lib.dllm_sched_attention_workspace.restype = _sz
     lib.dllm_sched_attention.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                          _i64, _vp, _i32, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _i32,
@@ -209,8 +209,9 @@ def cache_write(qkv, slot, k_cache, v_cache, n_heads: int, head_dim: int, stream
 
 
 def sched_attention_workspace(dt: int, n_seq: int, n_rows: int, n_heads: int, head_dim: int,
-                              max_kv: int, n_cap: int) -> int:
-    return int(load().dllm_sched_attention_workspace(dt, n_seq, n_rows, n_heads, head_dim, max_kv, n_cap))
+                              max_kv: int, n_cap: int, max_mass_rows: int = 0) -> int:
+    return int(load().dllm_sched_attention_workspace(dt, n_seq, n_rows, n_heads, head_dim, max_kv, n_cap,
+                                                     max_mass_rows))
 
 
 def sched_attention(q, cu_q, k_cache, v_cache, page_table, max_pages: int, kv_len, o, workspace,

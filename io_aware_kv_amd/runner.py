@@ -99,7 +99,7 @@ class FlashCacheRunner:
         max_mass = int(rows.mass_count.max())
         ws_qkv_b = dllm.qkv_rope_cachewrite_workspace(self.dt, R, self.wl.shape.d_model, self.H, self.D)
         ws_attn_b = dllm.sched_attention_workspace(self.dt_cache, self.wl.n_seq, R, self.H, self.D, max_kv,
-                                                   self.n_cap)
+                                                   self.n_cap, max_mass)
         return StepDevice(
             n_rows=R, cu_q=i32(rows.cu_q), logical=i32(rows.logical), pos=i32(rows.pos),
             slot=torch.empty(R, dtype=torch.int32, device=dev), mass_count=i32(rows.mass_count),

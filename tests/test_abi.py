@@ -120,6 +120,10 @@ def test_kernel_entry_points_reject_bad_shapes(lib):
     assert att(mass=fake, macc=fake, max_mass=200) == -2     # more than 128 window rows
     assert att(max_pages=5000) == -2
     assert att(dt=0, D=64, max_kv=10000) == -2               # fp32 path key limit
+    # a score on the fused path needs the probability scratch; a short one is refused
+    need = lib.dllm_sched_attention_workspace(1, 32, 2304, 32, 128, 2048, 2048, 32)
+    assert att(n_seq=32, R=2304, max_kv=2048, n_cap=2048, mass=fake, macc=fake, max_mass=32,
+               ws=need - 1, max_pages=128) == -1
 
     t = lib.dllm_topk_tracked
     assert t(1, 32, 512, 0, fake, fake, fake, fake, fake, 0, None) == -1
@@ -173,11 +177,16 @@ def test_workspace_queries(lib):
     for shape in ((1, 72, 4096, 32, 128), (0, 88, 256, 4, 64), (1, 65536, 4096, 32, 128)):
         assert q(*shape) == 0
     w = lib.dllm_sched_attention_workspace
-    assert w(1, 32, 2304, 32, 128, 2048, 2048) == 0          # 1024 pairs: fused path
-    assert w(0, 2, 88, 4, 64, 128, 128) == 0                 # fp32 path
-    small = w(1, 1, 72, 32, 128, 512, 512)                   # batch 1: keys split
+    assert w(1, 32, 2304, 32, 128, 2048, 2048, 0) == 0       # 1024 pairs: fused path, no score
+    # fused path with a score: bf16 probabilities (128 B per 64-key tile) and an
+    # fp32 reference per window row, key tile, sequence and head
+    assert w(1, 32, 2304, 32, 128, 2048, 2048, 32) == 32 * 32 * 32 * 32 * (128 + 4)
+    assert w(2, 32, 2304, 32, 128, 2000, 2048, 7) == 32 * 32 * 32 * 7 * (128 + 4)
+    assert w(0, 2, 88, 4, 64, 128, 128, 32) == 0             # fp32 path
+    assert w(1, 32, 2304, 32, 128, 2048, 2048, 129) == 0     # more window rows than a query tile: refused
+    small = w(1, 1, 72, 32, 128, 512, 512, 0)                # batch 1: keys split
     assert small > 0 and small % (128 * 130 * 4) == 0
-    assert small == w(1, 1, 72, 32, 128, 512, 512)
+    assert small == w(1, 1, 72, 32, 128, 512, 512, 32)       # the split path forms the score from its partials
 
 
 def test_confidence_workspace_is_one_partial_per_row_and_split(lib):
