@@ -100,6 +100,12 @@ __device__ __forceinline__ void copy16_to_lds(const void* gptr, uint32_t base) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :: "v"(gptr), "s"(base) : "memory", "m0");
 }
+// The same with the non-temporal hint, for data read once: the lines do not
+// displace what the caches hold for data that is read again.
+__device__ __forceinline__ void copy16_to_lds_nt(const void* gptr, uint32_t base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :: "v"(gptr), "s"(base) : "memory", "m0");
+}
 __device__ __forceinline__ void copy4_to_lds(const void* gptr, uint32_t base) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                  :: "v"(gptr), "s"(base) : "memory", "m0");

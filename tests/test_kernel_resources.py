@@ -15,10 +15,9 @@ RES = os.path.join(ROOT, "io_aware_kv_amd", "_lib", "kernel_resources.json")
 
 # the rotating 256 x 256 projection keeps three values in scratch in its
 # epilogue (after the K loop); nothing else may spill
-# (the E4M3 epilogue of the same kernel keeps 14; the masked E4M3 attention 7,
-# three of them reloaded once per key tile)
+# (the E4M3 epilogue of the same kernel keeps 14, the masked E4M3 attention 1)
 ALLOWED_SPILL = {"qkv_gemm_kernelILi8ELi2ELi1ELi0E": 3, "qkv_gemm_kernelILi8ELi2ELi1ELi2E": 14,
-                 "attn_bf16_kernelILi2ELi2ELb1ELb1E": 7}
+                 "attn_bf16_kernelILi2ELi2ELb1ELb1E": 1}
 LDS_LIMIT = 160 * 1024
 
 
