@@ -208,6 +208,52 @@ __global__ __launch_bounds__(kThr) void topk_kernel(int n_heads, int n_cap, int 
     }
     const int kk = min(k, total);
 
+    if constexpr (kPer == 1) {
+        // ---- one position per thread: sort, then rank by searching ----
+        // Each wave sorts its 64 composites (key << 32 | position; positions that
+        // are not candidates take the largest value) ascending with a bitonic
+        // network over lane exchanges, and publishes the sorted list.  A
+        // composite's rank among all of them is the number of smaller ones, found
+        // by a binary search in every wave's list (the eight searches
+        // interleaved); candidates ranked below kk write their output there.
+        // Composites of candidates are distinct, so ranks are too.
+        __shared__ unsigned long long s_sorted[kWaves][64];
+        unsigned long long c = cand[0] ? (((unsigned long long)key[0] << 32) | (uint32_t)tid) : ~0ull;
+#pragma unroll
+        for (int kb = 2; kb <= 64; kb <<= 1)
+#pragma unroll
+            for (int j = kb >> 1; j > 0; j >>= 1) {
+                const unsigned long long o = __shfl_xor(c, j);
+                const bool keep_min = ((lane & j) == 0) == ((lane & kb) == 0);
+                c = keep_min ? (o < c ? o : c) : (o > c ? o : c);
+            }
+        s_sorted[wave][lane] = c;
+        lds_barrier();
+        int pos[kWaves];
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) pos[w] = 0;
+#pragma unroll
+        for (int step = 32; step > 0; step >>= 1)
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) pos[w] += s_sorted[w][pos[w] + step - 1] < c ? step : 0;
+        int rank = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) rank += pos[w] + (s_sorted[w][pos[w]] < c ? 1 : 0);
+        // the score travels with its composite: fetch it from the lane the
+        // position started in (same wave), with every lane taking part
+        const float cv = __shfl(sc[0], (int)((uint32_t)c & 63u));
+        if (c != ~0ull && rank < kk) {
+            idx[(int64_t)b * k + rank] = (int32_t)(uint32_t)(c & 0xffffffffu);
+            val[(int64_t)b * k + rank] = cv;
+        }
+        for (int j = kk + tid; j < k; j += kThr) {
+            idx[(int64_t)b * k + j] = -1;
+            val[(int64_t)b * k + j] = 0.f;
+        }
+        if (tid == 0) count[b] = kk;
+        return;
+    }
+
     // ---- radix select: take keys below t_strict, plus (ties) krem keys equal to prefix ----
     int krem = kk;
     unsigned long long t_strict = 1ull << 32;             // take key < t_strict
