@@ -20,6 +20,7 @@ CASES = [
     # (n_seq, n_heads, n_cap, k, eligible fraction, tie-heavy)
     (1, 32, 512, 32, 0.6, False),
     (2, 32, 512, 32, 0.6, True),
+    (2, 32, 512, 256, 0.9, True),      # one per thread, ranks across all eight waves
     (1, 1, 1, 1, 1.0, False),
     (2, 3, 7, 4, 1.0, True),
     (3, 32, 1001, 32, 0.5, True),      # two per thread, ragged tail
