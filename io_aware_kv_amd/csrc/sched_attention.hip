@@ -224,6 +224,20 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, ln = lane & 15;
 
+    // A single sequence's page-table row does not depend on the schedule: it is
+    // fetched together with the schedule's loads (one round trip fewer).
+    constexpr int kPrePages = kMaxPages / kAttnThreads;
+    static_assert(kPrePages * kAttnThreads == kMaxPages, "every page entry has a thread");
+    const bool one_seq = a.n_seq == 1;
+    int pre_pages[kPrePages];
+    if (one_seq) {
+#pragma unroll
+        for (int i = 0; i < kPrePages; ++i) {
+            const int j = tid + i * kAttnThreads;
+            pre_pages[i] = j < a.max_pages ? a.page_table[j] : -1;
+        }
+    }
+
     // ---- schedule: per-sequence item counts (query tiles x heads x splits), prefix-summed by wave 0 ----
     if (wave == 0) {
         int base = 0;
@@ -283,9 +297,17 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     const int t_begin = min(sp * tiles_per, ntiles);    // this item's key tiles
     const int t_end = min(t_begin + tiles_per, ntiles);
     const int npages = (si.kv + 15) / 16;
-    for (int j = tid; j < npages; j += kAttnThreads) {
-        int p = a.page_table[(int64_t)b * a.max_pages + j];
-        s_pages[j] = (p >= 0 && p < a.pool_pages) ? p : -1;
+    if (one_seq) {
+#pragma unroll
+        for (int i = 0; i < kPrePages; ++i) {
+            const int j = tid + i * kAttnThreads, p = pre_pages[i];
+            if (j < npages) s_pages[j] = (p >= 0 && p < a.pool_pages) ? p : -1;
+        }
+    } else {
+        for (int j = tid; j < npages; j += kAttnThreads) {
+            int p = a.page_table[(int64_t)b * a.max_pages + j];
+            s_pages[j] = (p >= 0 && p < a.pool_pages) ? p : -1;
+        }
     }
     __syncthreads();
     for (int t = tid; t < kMaxPages / 4; t += kAttnThreads) {
