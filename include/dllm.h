@@ -235,7 +235,7 @@ int dllm_cache_write(dllm_dtype dt, int n_rows, int n_heads, int head_dim, const
  *   o          [R, H*D]            out: attention output
  * Scores are q.k/sqrt(D); a row that sees no key outputs zeros.  When the
  * batch has too few (sequence, head) pairs to fill the GPU, keys are split
- * over workgroups and a second kernel merges them (workspace: per split, fp32
+ * over workgroups and a second kernel merges them (workspace: per split, bf16
  * partial outputs and row statistics).  Otherwise, when a score is formed
  * (bf16 paths), the workspace holds the window rows' bf16 probabilities of
  * every key tile (B*H*ceil(max_kv/64)*max_mass_rows*(128+4) bytes), so the

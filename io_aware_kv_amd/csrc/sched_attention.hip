@@ -80,12 +80,14 @@ struct AttnArgs {
     int mass_tiles;
     uint16_t* o;
     int splits;             // key splits per (sequence, head, query tile); 1 = fused path
-    float* part_o;          // split mode: [item][kQT][kHD] unnormalised outputs
+    uint16_t* part_o;       // split mode: [item][kQT][kHD] unnormalised outputs, bf16
     float* part_ml;         // split mode: [item][kQT][2] running max (base 2) and sum
 };
 
-// split partial outputs, fragment-major: float offset of lane `lane`'s four
-// values of (item, wave, row tile rt, 16-column tile dt).  Row wave*32 +
+// split partial outputs, fragment-major: element offset of lane `lane`'s four
+// values of (item, wave, row tile rt, 16-column tile dt).  They are stored in
+// bf16 (the merged output is rounded to bf16 anyway): half the bytes the
+// merge moves, which at batch 1 is most of the split path's cost.  Row wave*32 +
 // rt*16 + lane%16, columns dt*16 + (lane/16)*4 .. +3.
 __host__ __device__ __forceinline__ int64_t part_frag(int64_t item, int wave, int rt, int dt, int lane) {
     return ((((item * 4 + wave) * 2 + rt) * 8 + dt) * 64 + lane) * 4;
@@ -671,15 +673,20 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
         // ---- split mode (QT == kQT): publish the unnormalised partial; attn_finish_kernel
         // merges the splits and forms the column mass ----
         // fragment-major: [item][wave][rt][dt][lane][4], so every store
-        // instruction writes 1 KiB of whole lines (row-major stores would
-        // scatter 64-byte half lines over 16 rows)
+        // instruction writes 512 B of whole lines (row-major stores would
+        // scatter 32-byte pieces over 16 rows)
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             if (!rt_active[rt]) continue;
             const int my_row = wrow + rt * 16 + ln;
-            float* po = a.part_o + part_frag(item, wave, rt, 0, lane);
+            uint16_t* po = a.part_o + part_frag(item, wave, rt, 0, lane);
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) *(f32x4*)(po + dt * 256) = acc[rt][dt];
+            for (int dt = 0; dt < 8; ++dt) {
+                uint2 u;
+                u.x = pack_bf16x2(acc[rt][dt][0], acc[rt][dt][1]);
+                u.y = pack_bf16x2(acc[rt][dt][2], acc[rt][dt][3]);
+                *(uint2*)(po + dt * 256) = u;
+            }
             if (g == 0) {
                 a.part_ml[((int64_t)item * kQT + my_row) * 2] = m_run[rt];
                 a.part_ml[((int64_t)item * kQT + my_row) * 2 + 1] = l_run[rt];
@@ -852,7 +859,7 @@ __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
         if (row >= si.rows) return;
         const int qt = row / kQT, r = row % kQT;
         float ms[MAXS], ls[MAXS];
-        f32x4 v[MAXS][2];
+        uint2 pw[MAXS][2];
 #pragma unroll
         for (int spl = 0; spl < MAXS; ++spl) {
             const int64_t it = split_item(h, min(spl, a.splits - 1), qt);
@@ -860,8 +867,8 @@ __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
             ls[spl] = a.part_ml[(it * kQT + r) * 2 + 1];
             // columns c8*8 .. +7: tile dt = c8/2, lane groups 2 (c8 % 2) and +1
             const int w = r >> 5, rt = (r >> 4) & 1, lr = r & 15, g0 = 2 * (c8 & 1);
-            v[spl][0] = *(const f32x4*)(a.part_o + part_frag(it, w, rt, c8 >> 1, g0 * 16 + lr));
-            v[spl][1] = *(const f32x4*)(a.part_o + part_frag(it, w, rt, c8 >> 1, (g0 + 1) * 16 + lr));
+            pw[spl][0] = *(const uint2*)(a.part_o + part_frag(it, w, rt, c8 >> 1, g0 * 16 + lr));
+            pw[spl][1] = *(const uint2*)(a.part_o + part_frag(it, w, rt, c8 >> 1, (g0 + 1) * 16 + lr));
         }
         float m = -INFINITY;
 #pragma unroll
@@ -874,9 +881,11 @@ __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
             const float f = exp2f(ms[spl] - m);
             l += ls[spl] * f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                o8[e] += v[spl][0][e] * f;
-                o8[4 + e] += v[spl][1][e] * f;
+            for (int hf = 0; hf < 2; ++hf) {
+                o8[4 * hf + 0] += bf16_bits_to_f32(pw[spl][hf].x & 0xffffu) * f;
+                o8[4 * hf + 1] += bf16_bits_to_f32(pw[spl][hf].x >> 16) * f;
+                o8[4 * hf + 2] += bf16_bits_to_f32(pw[spl][hf].y & 0xffffu) * f;
+                o8[4 * hf + 3] += bf16_bits_to_f32(pw[spl][hf].y >> 16) * f;
             }
         }
         const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -1124,7 +1133,7 @@ int64_t first_items(int n_seq, int n_rows, int n_heads, int splits) {
 size_t split_workspace(int n_seq, int n_rows, int n_heads, int splits) {
     if (splits <= 1) return 0;
     const int64_t items = first_items(n_seq, n_rows, n_heads, splits);
-    return (size_t)items * kQT * (kHD + 2) * sizeof(float);
+    return (size_t)items * kQT * (kHD * sizeof(uint16_t) + 2 * sizeof(float));
 }
 
 int mass_tiles(int max_kv) { return (max_kv + kKT - 1) / kKT; }
@@ -1239,8 +1248,8 @@ extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_
     a.splits = splits;
     if (splits > 1) {
         const int64_t items = first_items(n_seq, n_rows, n_heads, splits);
-        a.part_o = (float*)workspace;
-        a.part_ml = a.part_o + items * kQT * kHD;
+        a.part_o = (uint16_t*)workspace;
+        a.part_ml = (float*)(a.part_o + items * kQT * kHD);
     } else if (dt != DLLM_F32 && mass_rows > 0) {
         a.mass_tiles = mass_tiles(max_kv);
         a.mass_p = (uint16_t*)workspace;

@@ -185,7 +185,7 @@ def test_workspace_queries(lib):
     assert w(0, 2, 88, 4, 64, 128, 128, 32) == 0             # fp32 path
     assert w(1, 32, 2304, 32, 128, 2048, 2048, 129) == 0     # more window rows than a query tile: refused
     small = w(1, 1, 72, 32, 128, 512, 512, 0)                # batch 1: keys split
-    assert small > 0 and small % (128 * 130 * 4) == 0
+    assert small > 0 and small % (128 * (128 * 2 + 2 * 4)) == 0   # bf16 partial rows and (max, sum)
     assert small == w(1, 1, 72, 32, 128, 512, 512, 32)       # the split path forms the score from its partials
 
 
