@@ -683,7 +683,12 @@ __global__ __launch_bounds__(256, 1) void qkv_stream2_kernel(QkvArgs a, int n_pa
         c -= c >= n_st ? n_st : 0;
         const uint32_t base = __builtin_amdgcn_readfirstlane(ring0 + slot * kStageBytes + wave * kInst * 1024);
 #pragma unroll
-        for (int i = 0; i < kInst; ++i) copy16_to_lds(src[i] + c * KC, base + i * 1024);
+        for (int i = 0; i < kInst; ++i) {
+            // W rows are read once: non-temporal, so they do not push x (which
+            // every workgroup re-reads) out of L2
+            if (4 * (wave * kInst + i) >= MT * 16) copy16_to_lds_nt(src[i] + c * KC, base + i * 1024);
+            else copy16_to_lds(src[i] + c * KC, base + i * 1024);
+        }
     };
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s) issue(s, s);
