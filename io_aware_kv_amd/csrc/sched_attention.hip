@@ -358,8 +358,9 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     // other sequences' tiles).  Full refreshes read every key once per query
     // tile and keep the default policy, so the tiles after the first hit in L2.
     // (The choice is made once per issued tile: a branch per copy measured 3%
-    // slower on full refreshes.)
-    const bool kv_once = si.nqt == 1;
+    // slower on full refreshes.)  Split launches (few sequences, latency-bound)
+    // keep the default policy: measured 0.4 us faster at batch 1.
+    const bool kv_once = si.nqt == 1 && a.splits == 1;
     auto issue_p = [&](auto NTC, int sl, int t) __attribute__((always_inline)) {
         constexpr bool kNt = decltype(NTC)::value != 0;
         auto copy_kv = [&](const uint16_t* src, uint32_t dst) __attribute__((always_inline)) {
