@@ -82,6 +82,7 @@ struct AttnArgs {
     int splits;             // key splits per (sequence, head, query tile); 1 = fused path
     uint16_t* part_o;       // split mode: [item][kQT][kHD] unnormalised outputs, bf16
     float* part_ml;         // split mode: [item][kQT][2] running max (base 2) and sum
+    int qt_rows;            // split mode: query rows per first-launch item (64 or 128)
 };
 
 // split partial outputs, fragment-major: element offset of lane `lane`'s four
@@ -210,7 +211,6 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     static_assert(QT * 8 <= kMaskStageBytes, "layout");
     static_assert(NS * kPerStage + 4 * RT < 64, "wait counts");
     static_assert(kRing >= (4 * kMaxSeq + 1) * 4, "the schedule scan borrows the ring");
-    static_assert(QT == kQT, "the window rows of formula (2) fit the first query tile");
     // one LDS allocation: the ring (which the schedule scan borrows first), then the page tables
     __shared__ __attribute__((aligned(16))) uint8_t lds[kRing + (kMaxPages + 1) * 4 + kMaxPages / 4];
     int* s_pref = reinterpret_cast<int*>(lds);                                    // [kMaxSeq + 1], scheduling only
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     const bool want_mass = qt == 0 && a.mass_accum != nullptr && a.mass_count != nullptr;
     const int mb_in = want_mass ? a.mass_count[b] : 0;
     // unsplit: window rows whose probabilities the main pass keeps
-    const int mbp = a.splits == 1 ? max(0, min(mb_in, min(a.max_mass, min(si.rows, kQT)))) : 0;
+    const int mbp = a.splits == 1 ? max(0, min(mb_in, min(a.max_mass, min(si.rows, QT)))) : 0;
     // this (sequence, head)'s probability rows and references (wave-uniform bases)
     const int64_t mass_item0 = (int64_t)(b * a.H + h) * a.mass_tiles * a.max_mass;
     uint16_t* const mp_item = mbp > 0 ? a.mass_p + mass_item0 * kKT : nullptr;
@@ -671,7 +671,7 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     float* s_lse = reinterpret_cast<float*>(lds);                        // [kQT]
 
     if (a.splits > 1) {
-        // ---- split mode (QT == kQT): publish the unnormalised partial; attn_finish_kernel
+        // ---- split mode: publish the unnormalised partial; attn_finish_kernel
         // merges the splits and forms the column mass ----
         // fragment-major: [item][wave][rt][dt][lane][4], so every store
         // instruction writes 512 B of whole lines (row-major stores would
@@ -804,7 +804,7 @@ __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
             if (b < a.n_seq) {
                 SeqInfo s = seq_info(a, b);
                 items = a.H * ((s.rows + kMergeRows - 1) / kMergeRows + (want_mass ? (s.kv + kKT - 1) / kKT : 0));
-                first = s.nqt * a.H * a.splits;
+                first = (s.rows + a.qt_rows - 1) / a.qt_rows * a.H * a.splits;
                 s_seq[3 * b] = s.r0;
                 s_seq[3 * b + 1] = s.rows;
                 s_seq[3 * b + 2] = s.kv;
@@ -851,14 +851,16 @@ __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
     const int nch = (si.rows + kMergeRows - 1) / kMergeRows;
     // split-mode item index of (b, h, split, qt) in the first launch
     const int first_items = s_first[b];
-    auto split_item = [&](int h, int spl, int qt) { return first_items + (h * a.splits + spl) * si.nqt + qt; };
+    const int nqt1 = (si.rows + a.qt_rows - 1) / a.qt_rows;   // first-launch query tiles
+    auto split_item = [&](int h, int spl, int qt) { return first_items + (h * a.splits + spl) * nqt1 + qt; };
+    const int rt_per_wave = a.qt_rows / 64;                      // row tiles a first-launch wave held
 
     if (local < a.H * nch) {
         // ---- merge item: rows ch*16 .. ch*16+15 of head h, thread = (row, 8 columns) ----
         const int ch = local % nch, h = local / nch;
         const int row = ch * kMergeRows + (tid >> 4), c8 = tid & 15;
         if (row >= si.rows) return;
-        const int qt = row / kQT, r = row % kQT;
+        const int qt = row / a.qt_rows, r = row % a.qt_rows;
         float ms[MAXS], ls[MAXS];
         uint2 pw[MAXS][2];
 #pragma unroll
@@ -867,7 +869,7 @@ __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
             ms[spl] = a.part_ml[(it * kQT + r) * 2];
             ls[spl] = a.part_ml[(it * kQT + r) * 2 + 1];
             // columns c8*8 .. +7: tile dt = c8/2, lane groups 2 (c8 % 2) and +1
-            const int w = r >> 5, rt = (r >> 4) & 1, lr = r & 15, g0 = 2 * (c8 & 1);
+            const int w = r / (16 * rt_per_wave), rt = (r >> 4) % rt_per_wave, lr = r & 15, g0 = 2 * (c8 & 1);
             pw[spl][0] = *(const uint2*)(a.part_o + part_frag(it, w, rt, c8 >> 1, g0 * 16 + lr));
             pw[spl][1] = *(const uint2*)(a.part_o + part_frag(it, w, rt, c8 >> 1, (g0 + 1) * 16 + lr));
         }
@@ -1127,13 +1129,22 @@ int choose_splits(dllm_dtype dt, int n_seq, int n_rows, int n_heads, int max_kv)
     return s < 1 ? 1 : s;
 }
 
-int64_t first_items(int n_seq, int n_rows, int n_heads, int splits) {
-    return (int64_t)n_heads * (n_rows / kQT + n_seq) * splits;
+// Split launches without a mask and with at most 64 score rows use 64-row
+// query tiles (each wave one 16-row MFMA tile): twice the workgroups and half
+// the dependent MFMA and softmax work per wave per key tile, which is what a
+// split launch (few workgroups, latency-bound) waits on.
+constexpr int kSplitQT = 64;
+bool split_rt1(int splits, bool mask, int mass_rows) { return splits > 1 && !mask && mass_rows <= kSplitQT; }
+
+int64_t first_items(int n_seq, int n_rows, int n_heads, int splits, int qt_rows) {
+    return (int64_t)n_heads * (n_rows / qt_rows + n_seq) * splits;
 }
 
+// the workspace query does not see the mask: it sizes for 64-row tiles, the
+// larger item count
 size_t split_workspace(int n_seq, int n_rows, int n_heads, int splits) {
     if (splits <= 1) return 0;
-    const int64_t items = first_items(n_seq, n_rows, n_heads, splits);
+    const int64_t items = first_items(n_seq, n_rows, n_heads, splits, kSplitQT);
     return (size_t)items * kQT * (kHD * sizeof(uint16_t) + 2 * sizeof(float));
 }
 
@@ -1152,8 +1163,9 @@ size_t bf16_workspace(int n_seq, int n_rows, int n_heads, int max_kv, int max_ma
 }
 
 template <bool KV8>
-void launch_attn(const AttnArgs& a, dim3 grid, dim3 block, bool mask, hipStream_t stream) {
-    if (mask) hipLaunchKernelGGL((attn_bf16_kernel<2, 2, true, KV8>), grid, block, 0, stream, a);
+void launch_attn(const AttnArgs& a, dim3 grid, dim3 block, bool mask, bool rt1, hipStream_t stream) {
+    if (rt1) hipLaunchKernelGGL((attn_bf16_kernel<1, 2, false, KV8>), grid, block, 0, stream, a);
+    else if (mask) hipLaunchKernelGGL((attn_bf16_kernel<2, 2, true, KV8>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((attn_bf16_kernel<2, 2, false, KV8>), grid, block, 0, stream, a);
 }
 
@@ -1247,8 +1259,10 @@ extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_
     a.mass_overwrite = mass_overwrite != 0;
     a.o = (uint16_t*)o;
     a.splits = splits;
+    const bool rt1 = split_rt1(splits, mask_bits != nullptr, mass_rows);
+    a.qt_rows = rt1 ? kSplitQT : kQT;
     if (splits > 1) {
-        const int64_t items = first_items(n_seq, n_rows, n_heads, splits);
+        const int64_t items = first_items(n_seq, n_rows, n_heads, splits, kSplitQT);   // as the workspace
         a.part_o = (uint16_t*)workspace;
         a.part_ml = (float*)(a.part_o + items * kQT * kHD);
     } else if (dt != DLLM_F32 && mass_rows > 0) {
@@ -1257,14 +1271,15 @@ extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_
         a.mass_ref = (float*)(a.mass_p + (int64_t)n_seq * n_heads * a.mass_tiles * mass_rows * kKT);
     }
     if (dt != DLLM_F32) {
-        // 128-row query tiles: four waves of 32 rows (two 16-row MFMA tiles each)
-        const int64_t items = (int64_t)n_heads * (n_rows / kQT + n_seq) * splits;
+        // 128-row query tiles: four waves of 32 rows (two 16-row MFMA tiles
+        // each); 64-row tiles (one per wave) for the split launches above
+        const int64_t items = first_items(n_seq, n_rows, n_heads, splits, a.qt_rows);
         DLLM_CHECK_SUP(items > 0 && items < (1ll << 30));
         const dim3 grid((unsigned)items), block(kAttnThreads);
         if (dt == DLLM_BF16_E4M3KV)
-            launch_attn<true>(a, grid, block, mask_bits != nullptr, stream);
+            launch_attn<true>(a, grid, block, mask_bits != nullptr, rt1, stream);
         else
-            launch_attn<false>(a, grid, block, mask_bits != nullptr, stream);
+            launch_attn<false>(a, grid, block, mask_bits != nullptr, rt1, stream);
         if (splits > 1) {
             DLLM_CHECK_LAUNCH();
             int64_t fin = (int64_t)n_heads * (n_rows / kMergeRows + n_seq);
