@@ -112,10 +112,13 @@ def test_heavy_hitter_topk_exact(name, gpu):
 
 
 @pytest.mark.parametrize("name,splits", [("tiny_bf16", "2"), ("llada_b1", "1"), ("llada_b1", "3"),
-                                         ("verify_b4", "1"), ("verify_b4", "5")])
+                                         ("verify_b4", "1"), ("verify_b4", "5"), ("mixed_b8", "3")])
 def test_attention_split_paths(name, splits, gpu, monkeypatch):
     """Both attention paths (fused single launch, and key splits merged by a
-    second launch), including uneven splits, give the same parity."""
+    second launch), including uneven splits, give the same parity.  Unmasked
+    split launches run 64-row query tiles: mixed_b8 puts sequences of 40-72
+    rows and full refreshes of 512 and 1024 rows (8 and 16 query tiles) through
+    the merge."""
     log(f"[gpu] attention with {splits} key splits on {name}")
     monkeypatch.setenv("DLLM_ATTN_SPLITS", splits)
     c = case(name)
