@@ -571,7 +571,6 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
                     st[rt][t4][e] = p;
                     rs += p;
                 }
-            rs = wave_sum16(rs);
             if (grow) {                                   // the reference moved: rescale that row
                 const float alpha = __builtin_amdgcn_exp2f(m_run[rt] - m_new);
                 l_run[rt] *= alpha;
@@ -665,6 +664,11 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
         }
     }
     __syncthreads();                                    // every copy has been waited for above
+    // Each lane's running sum covers its own keys of the row (the four lane
+    // groups hold disjoint keys; one exponent reference per row, so one rescale
+    // serves all four): the row sums meet once, here, not every tile.
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) l_run[rt] = wave_sum16(l_run[rt]);
 
     // LDS after the main pass (the ring is free): final log-sum-exp (base 2) of
     // the tile's rows, then the score pass's factors
