@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kThr) void topk_kernel(int n_heads, int n_cap, int 
     for (int e = 0; e < kPer; ++e) sc[e] = 0.f;
     // heads in groups of kGroup: the group's loads are independent, then added
     // in ascending head order
-    constexpr int kGroup = 64 / kPer;
+    constexpr int kGroup = kPer == 1 ? 32 : 64 / kPer;     // one group covers 32 heads
     for (int h0 = 0; h0 < n_heads; h0 += kGroup) {
         float v[kGroup][kPer];
 #pragma unroll
