@@ -1133,15 +1133,20 @@ int choose_splits(dllm_dtype dt, int n_seq, int n_rows, int n_heads, int max_kv)
     return s < 1 ? 1 : s;
 }
 
-// Split launches without a mask and with at most 64 score rows use 64-row
-// query tiles (each wave one 16-row MFMA tile): twice the workgroups and half
-// the dependent MFMA and softmax work per wave per key tile, which is what a
-// split launch (few workgroups, latency-bound) waits on.
-constexpr int kSplitQT = 64;
-bool split_rt1(int splits, bool mask, int mass_rows) { return splits > 1 && !mask && mass_rows <= kSplitQT; }
-
 int64_t first_items(int n_seq, int n_rows, int n_heads, int splits, int qt_rows) {
     return (int64_t)n_heads * (n_rows / qt_rows + n_seq) * splits;
+}
+
+// Split launches without a mask, with at most 64 score rows and with fewer
+// 128-row items than compute units use 64-row query tiles (each wave one
+// 16-row MFMA tile): twice the workgroups and half the dependent MFMA and
+// softmax work per wave per key tile, which is what such a launch (latency-
+// bound) waits on.  Where the 128-row items already fill the compute units
+// the doubled grid measured slower (the verify step: 58 -> 65 us).
+constexpr int kSplitQT = 64;
+bool split_rt1(int n_seq, int n_rows, int n_heads, int splits, bool mask, int mass_rows) {
+    return splits > 1 && !mask && mass_rows <= kSplitQT &&
+           first_items(n_seq, n_rows, n_heads, splits, kQT) <= kNumCu;
 }
 
 // the workspace query does not see the mask: it sizes for 64-row tiles, the
@@ -1263,7 +1268,7 @@ extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_
     a.mass_overwrite = mass_overwrite != 0;
     a.o = (uint16_t*)o;
     a.splits = splits;
-    const bool rt1 = split_rt1(splits, mask_bits != nullptr, mass_rows);
+    const bool rt1 = split_rt1(n_seq, n_rows, n_heads, splits, mask_bits != nullptr, mass_rows);
     a.qt_rows = rt1 ? kSplitQT : kQT;
     if (splits > 1) {
         const int64_t items = first_items(n_seq, n_rows, n_heads, splits, kSplitQT);   // as the workspace
