@@ -217,6 +217,7 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     int* s_seq = s_pref + (kMaxSeq + 1);                                          // [kMaxSeq][3], scheduling only
     int* s_pages = reinterpret_cast<int*>(lds + kRing);                      // [kMaxPages]
     int* s_total = s_pages + kMaxPages;
+    // per key tile: bit q (q < 4) = page 4t + q exists and is valid, bit 4 = every key valid
     uint8_t* s_tile_full = reinterpret_cast<uint8_t*>(s_total + 1);               // [kMaxPages / 4]
     auto k_tile = [&](int sl) { return reinterpret_cast<uint16_t*>(lds + sl * kStageBytes); };
     auto v_tile = [&](int sl) { return reinterpret_cast<uint16_t*>(lds + sl * kStageBytes) + kTileH; };
@@ -313,10 +314,11 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     }
     __syncthreads();
     for (int t = tid; t < kMaxPages / 4; t += kAttnThreads) {
-        bool full = t < ntiles && (t + 1) * kKT <= si.kv;
+        uint32_t pg = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) full = full && s_pages[min(t * 4 + q, max(npages - 1, 0))] >= 0;
-        s_tile_full[t] = full ? 1 : 0;
+        for (int q = 0; q < 4; ++q) pg |= (t * 4 + q < npages && s_pages[t * 4 + q] >= 0 ? 1u : 0u) << q;
+        const bool full = t < ntiles && (t + 1) * kKT <= si.kv && pg == 15u;
+        s_tile_full[t] = (uint8_t)(pg | (full ? 16u : 0u));
     }
     __syncthreads();
 
@@ -374,7 +376,7 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
         const uint32_t dst = lds_addr(is_v ? v_tile(sl) : k_tile(sl));
         // (the masked and E4M3 kernels keep only the general path: their
         // register budget has no room for both)
-        if (!HAS_MASK && !KV8 && t < t_end && __builtin_amdgcn_readfirstlane(s_tile_full[t])) {
+        if (!HAS_MASK && !KV8 && t < t_end && (__builtin_amdgcn_readfirstlane(s_tile_full[t]) & 16)) {
             // every key valid: a wave's copies touch two pages (wave-uniform), so
             // a copy's source is a page base plus a fixed 32-bit lane offset
             const int p0 = __builtin_amdgcn_readfirstlane(s_pages[t * 4 + 2 * (wave & 1)]);
@@ -474,6 +476,7 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     auto vis_bits = [&](int t, bool rok, uint32_t w0, uint32_t w1) __attribute__((always_inline)) -> uint32_t {
         uint32_t bits = 0;
         const int kbase = t * kKT;
+        const uint32_t pg = s_tile_full[t];                  // the tile's valid pages, one read
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
@@ -481,7 +484,7 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
                 const int kk = reg_key(t4, g, e);
                 const int kg = kbase + kk;
                 const uint32_t w = (kk < 32) ? w0 : w1;
-                const bool ok = (kg < si.kv) & (s_pages[min(kg >> 4, last_page)] >= 0) &
+                const bool ok = (kg < si.kv) & (((pg >> (kk >> 4)) & 1u) != 0) &
                                 (((w >> (kk & 31)) & 1u) != 0);
                 bits |= (ok ? 1u : 0u) << (t4 * 4 + e);
             }
@@ -532,7 +535,7 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     auto attend = [&](int sl, int t) __attribute__((always_inline)) {
         f32x4 st[RT][4];
         scores(k_tile(sl), st);
-        const bool full = !HAS_MASK && s_tile_full[t];
+        const bool full = !HAS_MASK && (s_tile_full[t] & 16);
         bf16x8 pf[RT][2];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
