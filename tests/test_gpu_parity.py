@@ -115,10 +115,11 @@ def test_heavy_hitter_topk_exact(name, gpu):
                                          ("verify_b4", "1"), ("verify_b4", "5"), ("mixed_b8", "3")])
 def test_attention_split_paths(name, splits, gpu, monkeypatch):
     """Both attention paths (fused single launch, and key splits merged by a
-    second launch), including uneven splits, give the same parity.  Unmasked
-    split launches run 64-row query tiles: mixed_b8 puts sequences of 40-72
-    rows and full refreshes of 512 and 1024 rows (8 and 16 query tiles) through
-    the merge."""
+    second launch), including uneven splits, give the same parity.  Small
+    unmasked split launches run 64-row query tiles (tiny_bf16, llada_b1: 72
+    rows make a full tile and an 8-row one); mixed_b8 puts sequences of 40-72
+    rows and full refreshes of 512 and 1024 rows (4 and 8 query tiles of 128)
+    through the merge."""
     log(f"[gpu] attention with {splits} key splits on {name}")
     monkeypatch.setenv("DLLM_ATTN_SPLITS", splits)
     c = case(name)
