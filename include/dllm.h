@@ -341,6 +341,23 @@ int dllm_decode_verify(dllm_dtype dt, int n_seq, int n_rows, const int32_t* cu_r
                        int32_t* token, float* conf, uint8_t* accept, int32_t* n_accept,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Tuning override, for tests and tuning runs; correct use needs none.  Forces
+ * a kernel choice process-wide:
+ *   knob "attn_splits": value a split count ("1" .. "1024"; capped at 16 and
+ *       at the key tiles) for the bf16 dllm_sched_attention;
+ *   knob "qkv_kernel": value "tiled", "gemm" or a tile shape ("g256x256",
+ *       "g128x256", "g128x256o2", "g64x256", "g64x256o2", "g256x128",
+ *       "g256x128o2", "g128x128", "g128x128o2") for projections of more than
+ *       128 rows, where the shape allows it;
+ *   value NULL or "" restores the automatic choice.
+ * The first values come from the environment variables DLLM_ATTN_SPLITS and
+ * DLLM_QKV_KERNEL, read once per process (at the first call that needs them
+ * or at the first dllm_set_tuning).  A workspace query and the call it sizes
+ * read the same stored value: change a knob only between such pairs.
+ * Errors: INVALID_ARG for an unknown knob or value (nothing changes).
+ */
+int dllm_set_tuning(const char* knob, const char* value);
 
 #ifdef __cplusplus
 }

@@ -148,6 +148,13 @@ __device__ __forceinline__ void lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Tuning overrides (tuning.hip): the forced attention split count (0 =
+// automatic) and the forced projection kernel name (nullptr = automatic),
+// from DLLM_ATTN_SPLITS / DLLM_QKV_KERNEL read once per process, or from
+// dllm_set_tuning.
+int tuning_attn_splits();
+const char* tuning_qkv_kernel();
+
 }  // namespace dllm
 
 #define DLLM_CHECK_ARG(cond) \

@@ -922,7 +922,9 @@ struct QkvPlan {
 // alone or in pairs, at the measured time of each.  None splits K
 // across workgroups, so no workspace is needed.  Shapes the GEMM cannot take
 // fall back to the 128 x 128 LDS-tiled kernel.
-// DLLM_QKV_KERNEL=tiled|gemm|g128x256|... overrides the choice where the shape allows it.
+// The qkv_kernel tuning override (DLLM_QKV_KERNEL, read once per process, or
+// dllm_set_tuning: tiled|gemm|g128x256|...) forces the choice where the shape
+// allows it.
 QkvPlan plan_bf16(int R, int d_model, int n_out, int head_dim) {
     QkvPlan p{};
     const bool gemm_ok = head_dim == 128 && n_out % 256 == 0 && d_model % (kGBK * kGemmKB) == 0;
@@ -943,7 +945,7 @@ QkvPlan plan_bf16(int R, int d_model, int n_out, int head_dim) {
             }
         }
     }
-    if (const char* e = getenv("DLLM_QKV_KERNEL")) {
+    if (const char* e = tuning_qkv_kernel()) {
         if (!strcmp(e, "tiled")) p.kind = kTiled128;
         else if (!strcmp(e, "gemm") && gemm_ok) p.kind = kGemm, p.shape = kG256x256;
         else

@@ -1116,8 +1116,9 @@ __global__ __launch_bounds__(kF32Threads) void attn_f32_kernel(AttnArgs a, const
 // When batch x heads cannot fill the chip (one workgroup streams at most
 // ~50 GB/s), keys are split so that roughly 512 workgroups stream them, and a
 // second launch merges the splits and forms the column mass.
-// DLLM_ATTN_SPLITS overrides the split count (a tuning knob; the workspace
-// query reads it too, so the two agree).
+// The attn_splits tuning override (DLLM_ATTN_SPLITS, read once per process,
+// or dllm_set_tuning) forces the split count; the workspace query reads the
+// same stored value, so the two agree.
 int choose_splits(dllm_dtype dt, int n_seq, int n_rows, int n_heads, int max_kv) {
     if (dt != DLLM_BF16 && dt != DLLM_BF16_E4M3KV) return 1;
     const int ktiles = (max_kv + kKT - 1) / kKT;
@@ -1129,8 +1130,7 @@ int choose_splits(dllm_dtype dt, int n_seq, int n_rows, int n_heads, int max_kv)
         const int cap = ktiles / 2 > 1 ? ktiles / 2 : 1;     // at least two tiles per split
         if (s > cap) s = cap;
     }
-    const char* env = getenv("DLLM_ATTN_SPLITS");
-    if (env && atoi(env) > 0) s = atoi(env);
+    if (const int forced = tuning_attn_splits(); forced > 0) s = forced;
     if (s > kMaxSplits) s = kMaxSplits;
     if (s > ktiles) s = ktiles > 0 ? ktiles : 1;
     return s < 1 ? 1 : s;

@@ -24,7 +24,7 @@ EXPORTS = (
     "dllm_qkv_project", "dllm_rope_apply", "dllm_cache_write",
     "dllm_sched_attention_workspace", "dllm_sched_attention", "dllm_topk_tracked",
     "dllm_confidence_workspace", "dllm_confidence_argmax", "dllm_confidence_commit", "dllm_verify_accept",
-    "dllm_decode_commit", "dllm_decode_verify",
+    "dllm_decode_commit", "dllm_decode_verify", "dllm_set_tuning",
 )
 
 
@@ -77,13 +77,21 @@ def load() -> ctypes.CDLL:
                                        _vp, _sz, _vp]
     lib.dllm_decode_verify.argtypes = [_i32, _i32, _i32, _vp, _i32, _vp, _i64, _vp, _f32, _vp, _vp, _vp,
                                        _vp, _vp, _sz, _vp]
-    for name in ("dllm_build_block_table", "dllm_map_slots", "dllm_qkv_rope_cachewrite",
+    lib.dllm_set_tuning.argtypes = [ctypes.c_char_p, ctypes.c_char_p]
+    for name in ("dllm_set_tuning", "dllm_build_block_table", "dllm_map_slots", "dllm_qkv_rope_cachewrite",
                  "dllm_qkv_rope_cachewrite_paged", "dllm_qkv_project", "dllm_rope_apply", "dllm_cache_write",
                  "dllm_sched_attention", "dllm_topk_tracked", "dllm_confidence_argmax", "dllm_confidence_commit",
                  "dllm_verify_accept", "dllm_decode_commit", "dllm_decode_verify"):
         getattr(lib, name).restype = _i32
     _lib = lib
     return lib
+
+
+def set_tuning(knob: str, value: Optional[str]) -> None:
+    """Process-wide tuning override: knob "attn_splits" (a split count as
+    text) or "qkv_kernel" (a projection kernel name); None restores the
+    automatic choice."""
+    _check("dllm_set_tuning", load().dllm_set_tuning(knob.encode(), None if value is None else str(value).encode()))
 
 
 def _check(fn: str, rc: int) -> None:

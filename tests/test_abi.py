@@ -210,3 +210,23 @@ def test_pack_mask_layout():
             for j in range(v.shape[1]):
                 w = int(bits[off[b] + i * words + j // 32])
                 assert ((w >> (j % 32)) & 1) == int(v[i, j])
+
+
+def test_tuning_override(lib):
+    # unknown knobs and values are refused and change nothing; NULL / "" restore
+    # the automatic choice
+    assert lib.dllm_set_tuning(b"nonsense", b"1") == -1
+    assert lib.dllm_set_tuning(None, b"1") == -1
+    assert lib.dllm_set_tuning(b"attn_splits", b"x3") == -1
+    assert lib.dllm_set_tuning(b"attn_splits", b"-1") == -1
+    assert lib.dllm_set_tuning(b"qkv_kernel", b"g999x1") == -1
+    w = lib.dllm_sched_attention_workspace
+    auto = w(1, 1, 72, 32, 128, 512, 512, 32)
+    assert lib.dllm_set_tuning(b"attn_splits", b"2") == 0
+    forced = w(1, 1, 72, 32, 128, 512, 512, 32)
+    assert lib.dllm_set_tuning(b"attn_splits", None) == 0
+    assert w(1, 1, 72, 32, 128, 512, 512, 32) == auto
+    assert forced != auto and forced % (128 * (128 * 2 + 2 * 4)) == 0
+    for name in (b"tiled", b"gemm", b"g256x256", b"g128x256o2", b"g128x128"):
+        assert lib.dllm_set_tuning(b"qkv_kernel", name) == 0
+    assert lib.dllm_set_tuning(b"qkv_kernel", b"") == 0
