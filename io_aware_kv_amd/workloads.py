@@ -407,6 +407,17 @@ def device_activations(wl: Workload, rows: StepRows, step: int, layer: int, devi
                               ((1000 * wl.wid + 2) * 64 + step) * 4096 + layer, device)
 
 
+def device_cache_fill(wl: Workload, layer: int, which: int, device):
+    """Contents of a layer's K (which = 0) or V (which = 1) cache before a
+    step that is checked on its own, without the full refresh that would
+    otherwise fill it: every row N(0, 1) in bf16, the spread of a projected
+    K or V element of these inputs (x ~ N(0, 1), W ~ N(0, 1/d_model))."""
+    sh = wl.shape
+    n = sh.n_heads * sh.head_dim
+    return device_normal_bf16((wl.pool_pages * PAGE, n), 1.0,
+                              ((1000 * wl.wid + 9) * 4 + which) * 4096 + layer, device)
+
+
 def seeded_tracked(wl: Workload, step: int) -> List[np.ndarray]:
     """Tracked positions chosen by a seeded draw among the eligible ones (used
     where a step's row set must not depend on either side's top-k)."""

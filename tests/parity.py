@@ -28,6 +28,20 @@ def log(msg: str) -> None:
     sys.stdout.flush()
 
 
+def measure(got: np.ndarray, want: np.ndarray, atol: float, rtol: float, what: str) -> dict:
+    """The error statistics of close() without the assertion: max error,
+    max error / rms(oracle), elements beyond atol + rtol |want|, and the
+    largest ratio err / (atol + rtol |want|) (above 1 = outside the gate)."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    err = np.abs(got - want)
+    lim = atol + rtol * np.abs(want)
+    rms = float(np.sqrt(np.mean(want ** 2))) if want.size else 0.0
+    return {"what": what, "max_abs": float(err.max()) if err.size else 0.0,
+            "max_over_rms": float(err.max() / rms) if err.size and rms else 0.0,
+            "n_bad": int((err > lim).sum()), "worst_ratio": float((err / lim).max()) if err.size else 0.0}
+
+
 def close(got: np.ndarray, want: np.ndarray, atol: float, rtol: float, what: str) -> dict:
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)

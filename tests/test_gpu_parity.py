@@ -12,7 +12,7 @@ import pytest
 
 import oracle as O
 from io_aware_kv_amd import workloads as W
-from parity import (MASS_TOL, TOL, Case, check_topk, close, device_bits, device_values, log)
+from parity import (MASS_TOL, TOL, Case, check_topk, close, device_bits, device_values, log, measure)
 
 pytestmark = pytest.mark.gpu
 
@@ -108,12 +108,16 @@ def test_heavy_hitter_topk_exact(name, gpu):
     log(f"[gpu] heavy-hitter top-k {name}")
     c = case(name, heavy=True)
     g = run_gpu_step(c, 0, gpu)
+    atol, rtol = TOL[c.kind]
+    m = measure(g["o"], c.out0["o"], atol, rtol, "o at the workload gate")
+    log(f"   heavy {name} o at the workload gate: max_abs={m['max_abs']:.3e} n_bad={m['n_bad']} "
+        f"worst err/limit={m['worst_ratio']:.3f}")
     compare_step(c, g, 0, exact_topk=True, o_scale=4.0)
 
 
 @pytest.mark.parametrize("name,splits", [("tiny_bf16", "2"), ("llada_b1", "1"), ("llada_b1", "3"),
                                          ("verify_b4", "1"), ("verify_b4", "5"), ("mixed_b8", "3")])
-def test_attention_split_paths(name, splits, gpu, monkeypatch):
+def test_attention_split_paths(name, splits, gpu):
     """Both attention paths (fused single launch, and key splits merged by a
     second launch), including uneven splits, give the same parity.  Small
     unmasked split launches run 64-row query tiles (tiny_bf16, llada_b1: 72
@@ -121,9 +125,13 @@ def test_attention_split_paths(name, splits, gpu, monkeypatch):
     rows and full refreshes of 512 and 1024 rows (4 and 8 query tiles of 128)
     through the merge."""
     log(f"[gpu] attention with {splits} key splits on {name}")
-    monkeypatch.setenv("DLLM_ATTN_SPLITS", splits)
+    from io_aware_kv_amd import dllm
     c = case(name)
-    g = run_gpu_step(c, 1, gpu)
+    dllm.set_tuning("attn_splits", splits)
+    try:
+        g = run_gpu_step(c, 1, gpu)
+    finally:
+        dllm.set_tuning("attn_splits", None)
     compare_step(c, g, 1)
 
 
@@ -132,7 +140,7 @@ def test_attention_split_paths(name, splits, gpu, monkeypatch):
                                          ("mixed_b8", "g64x256"), ("llada_b1", "g64x256o2"),
                                          ("mixed_b8", "g256x128"), ("mixed_b8", "g256x128o2"),
                                          ("tiny_bf16", "g128x128"), ("mixed_b8", "g128x128o2")])
-def test_projection_kernel_paths(name, kernel, gpu, monkeypatch):
+def test_projection_kernel_paths(name, kernel, gpu):
     """The projection for more than 128 rows has the 128 x 128 LDS-tiled
     kernel and the whole-head GEMM in five tile shapes (256 x 256, 128 x 256,
     64 x 256, 256 x 128, 128 x 128), the smaller four alone on a compute unit
@@ -141,9 +149,13 @@ def test_projection_kernel_paths(name, kernel, gpu, monkeypatch):
     of 153, 25 and 25 rows at 256-, 64- and 128-row tiles; tiny_bf16 is one
     row tile by three or six column tiles over a contraction of 256)."""
     log(f"[gpu] projection kernel {kernel} on {name}")
-    monkeypatch.setenv("DLLM_QKV_KERNEL", kernel)
+    from io_aware_kv_amd import dllm
     c = case(name)
-    g = run_gpu_step(c, 0, gpu)
+    dllm.set_tuning("qkv_kernel", kernel)
+    try:
+        g = run_gpu_step(c, 0, gpu)
+    finally:
+        dllm.set_tuning("qkv_kernel", None)
     compare_step(c, g, 0)
 
 
