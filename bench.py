@@ -3,15 +3,21 @@
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 slot map -> fused QKV + RoPE + cache write -> scheduled attention with the
-formula-(2) column mass -> top-k of the tracked set.  The default workload is
-the LLaDA-8B-shaped layer (d_model 4096, 32 heads x 128, bf16) with one
-sequence of 512 tokens in the cache phase: 72 refreshed rows (32 masked
-window + 8 newly decoded + 32 tracked).
+formula-(2) column mass, layer by layer, then the top-k of the tracked set.
 
-Metric: refreshed tokens/s per layer = rows refreshed per step / step time.
-Inputs are resident in HBM before timing starts.  To keep the 256 MB
-Infinity Cache from serving the weights and caches, the timed loop rotates
-over enough independent copies (weights, caches, inputs) to span >= 1 GiB.
+Default workload (the headline): the 32-layer LLaDA-8B-shaped sweep (d_model
+4096, 32 heads x 128, bf16) at batch 32, context 2048 (prompt 1536 + gen 512),
+with denoising steps alternating between a full refresh (2048 rows per
+sequence and layer) and a cache-phase step (32 masked window + 8 new + 32
+tracked rows per sequence and layer); one top-32 per step after the last
+layer.  Timed steps alternate the two kinds.
+
+Metric: refreshed tokens/s per layer = rows refreshed per layer over the timed
+steps / (their time / layers).  Inputs are resident in HBM before timing
+starts; the batch-32 caches and weights (38 GB) are far larger than the
+256 MB Infinity Cache.  The single-layer workloads reported beside it (batch
+1, the mixed batch of 8, the batch-4 verify step) rotate over enough
+independent copies of weights, caches and inputs to span >= 1 GiB.
 
 Prints ONE JSON line on stdout; diagnostics go to stderr.
 """
@@ -28,6 +34,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "refreshed tokens/s per layer (cache-update+attention)"
+SINGLE = ("llada_b1", "mixed_b8", "verify_b4")
 
 
 def eprint(*a):
@@ -37,12 +45,13 @@ def eprint(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="llada_b1",
-                   choices=["llada_b1", "mixed_b8", "verify_b4", "llada_b32"])
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=4)
+    p.add_argument("--workload", default="llada_b32", choices=["llada_b32", *SINGLE])
     p.add_argument("--rotate-gib", type=float, default=1.0)
     p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--no-extras", action="store_true",
+                   help="only the headline workload (no other workloads, variants or decode side)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--probe", default=None,
@@ -57,17 +66,68 @@ def parse():
     return p.parse_args()
 
 
+def pct(vals):
+    import numpy as np
+    a = np.asarray(vals, dtype=np.float64)
+    return {"mean": float(a.mean()), "p10": float(np.percentile(a, 10)), "p50": float(np.percentile(a, 50)),
+            "p90": float(np.percentile(a, 90))}
+
+
+def layer_work(sh, rows, cache_el=2):
+    """Algorithmic bytes and flops of one layer of a step: the projection
+    (W_qkv once; per row x in, q out, K and V rows into the cache) and the
+    attention (per key of a sequence its K and V row; per row q in, o out;
+    4 n flops per visible (row, key) pair), each kernel's bound, their sum
+    (the step's roofline) and the stricter overlap bound."""
+    import numpy as np
+    n = sh.n_heads * sh.head_dim
+    d = sh.d_model
+    el = 2 if sh.dtype == "bf16" else 4
+    kel = cache_el if el == 2 else el
+    R = rows.n_rows
+    qkv_bytes = 3 * n * d * el + R * d * el + R * n * el + 2 * R * n * kel
+    qkv_flops = 2 * R * d * 3 * n
+    kv = rows.kv_len.astype(np.int64)
+    attn_bytes = int(kv.sum()) * 2 * n * kel + 2 * R * n * el
+    attn_flops = 0
+    for b in range(len(kv)):
+        rb = int(rows.cu_q[b + 1] - rows.cu_q[b])
+        vis = rows.visible[b].sum() if rows.visible is not None else rb * int(kv[b])
+        attn_flops += 4 * int(vis) * n
+    bw, pk = HBM_PEAK_GBS * 1e9, MFMA_BF16_PEAK_TFLOPS * 1e12
+    b_qkv = max(qkv_bytes / bw, qkv_flops / pk) * 1e6
+    b_att = max(attn_bytes / bw, attn_flops / pk) * 1e6
+    return {"qkv_bytes": qkv_bytes, "qkv_flops": qkv_flops, "attn_bytes": attn_bytes, "attn_flops": attn_flops,
+            "qkv_bound_us": b_qkv, "qkv_bound": "hbm" if qkv_bytes / bw >= qkv_flops / pk else "mfma",
+            "attn_bound_us": b_att, "attn_bound": "hbm" if attn_bytes / bw >= attn_flops / pk else "mfma",
+            "sum_of_bounds_us": b_qkv + b_att,
+            "overlap_bound_us": max((qkv_bytes + attn_bytes) / bw, (qkv_flops + attn_flops) / pk) * 1e6}
+
+
+def counter_traffic(name):
+    """Counter-measured HBM bytes per launch of a profiled kernel
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain-copy calibration), from a
+    profiles/ record; None once the kernel's source differs from the one
+    profiled."""
+    import hashlib
+    tfile = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(tfile):
+        return None
+    tj = json.load(open(tfile))
+    src = open(os.path.join(ROOT, tj["source"]), "rb").read()
+    if hashlib.sha256(src).hexdigest() != tj["source_sha256"]:
+        return None
+    return tj["bytes_per_launch"]
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
     from io_aware_kv_amd import dllm
-    from io_aware_kv_amd import workloads as W
-    from io_aware_kv_amd.runner import FlashCacheRunner
 
     dllm.load()
     dev = torch.device("cuda:0")
@@ -75,29 +135,303 @@ def main():
     if args.probe:
         return probe(args.probe, dev)
     if args.workload == "llada_b32":
-        return bench_layers(args, dev)
-    wl = W.make_workload(args.workload)
+        out = bench_layers(args, dev)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        if not args.no_extras:
+            out["other_workloads"] = {}
+            for name in SINGLE:
+                out["other_workloads"][name] = bench_single(args, dev, name, detail=name == "llada_b1")
+                torch.cuda.empty_cache()
+    else:
+        out = bench_single(args, dev, args.workload, detail=not args.no_extras)
+    if args.copy_probe_mib:
+        # optional plain copy (calibrates the HBM byte counters)
+        n = args.copy_probe_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b_ = torch.empty_like(a)
+        for _ in range(3):
+            b_.copy_(a)
+        torch.cuda.synchronize()
+        del a, b_
+    if not args.no_decode and not args.no_graph and not args.no_extras:
+        out["decode_side"] = bench_decode(args, dev)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = (cpu_baseline_b32() if args.workload == "llada_b32"
+                               else cpu_baseline(args.workload, args.cpu_seconds))
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# the headline: 32 layers, batch 32
+# ---------------------------------------------------------------------------
+
+def bench_layers(args, dev):
+    """32-layer batch-32 sweep.  Timed: K denoising steps alternating full
+    refresh (2048 rows per sequence per layer) and cache phase (72 rows per
+    sequence per layer), each with per-layer HIP events around the projection
+    and the attention on the launch stream, plus the step's top-k.  Variants
+    (score from the middle layers only, E4M3 caches, block-freeze row sets,
+    the unfused arm) are timed after it on the same layers."""
+    import numpy as np
+    import torch
+    from io_aware_kv_amd import workloads as W
+    from io_aware_kv_amd.runner import FlashCacheRunner
+    wl = W.make_workload("llada_b32")
+    sh = wl.shape
+    L = sh.layers
+    run = FlashCacheRunner(wl, device=dev)
+    Ws = [W.device_weights(wl, l, dev) for l in range(L)]
+    rows = {"full": W.full_refresh_rows(wl)}
+    sts = {"full": run.upload_step(rows["full"])}
+    xs = {"full": [W.device_activations(wl, rows["full"], 0, l, dev) for l in range(L)]}
+    stream = torch.cuda.current_stream()
+
+    def step(kind, ev=None, unfused=False):
+        st = sts[kind]
+        mass = kind in ("full", "cache", "cache_mid")    # block-cache steps have no formula-(2) rows
+        run.map_slots(st)
+        for l in range(L):
+            if ev is not None:
+                ev[l][0].record(stream)
+            if unfused:
+                run.cache_update_unfused(st, xs[kind][l], Ws[l], l)
+            else:
+                run.cache_update(st, xs[kind][l], Ws[l], l)
+            if ev is not None:
+                ev[l][1].record(stream)
+            # cache_mid: the score only from the middle layers 5..20 (1-based); the
+            # first scoring layer stores its term, the others add theirs
+            first = 4 if kind == "cache_mid" else 0
+            run.attention(st, l, with_mass=mass and (kind != "cache_mid" or 5 <= l + 1 <= 20),
+                          mass_overwrite=l == first)
+            if ev is not None:
+                ev[l][2].record(stream)
+        if mass:
+            run.topk(clear_mass=False)
+        if ev is not None:
+            ev[L][0].record(stream)
+
+    step("full")
+    idx = run.top_idx.cpu().numpy()
+    rows["cache"] = W.config_step_rows(wl, [idx[b][idx[b] >= 0] for b in range(wl.n_seq)])
+    sts["cache"] = run.upload_step(rows["cache"])
+    xs["cache"] = [W.device_activations(wl, rows["cache"], 1, l, dev) for l in range(L)]
+    kinds = ("full", "cache")
+    for i in range(max(2, args.warmup)):
+        step(kinds[i % 2])
+    torch.cuda.synchronize()
+
+    # ---- the timed region: K steps alternating full refresh and cache phase ----
+    K = max(2, args.steps)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    evs = [[[ev() for _ in range(3)] for _ in range(L + 1)] for _ in range(K)]
+    t_step = [(ev(), ev()) for _ in range(K)]
+    t0, t1 = ev(), ev()
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(K):
+        t_step[i][0].record(stream)
+        step(kinds[i % 2], evs[i])
+        t_step[i][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    res = {}
+    for k, kind in enumerate(kinds):
+        its = range(k, K, 2)
+        qkv = [evs[i][l][0].elapsed_time(evs[i][l][1]) * 1e3 for i in its for l in range(L)]
+        att = [evs[i][l][1].elapsed_time(evs[i][l][2]) * 1e3 for i in its for l in range(L)]
+        tk = [evs[i][L - 1][2].elapsed_time(evs[i][L][0]) * 1e3 for i in its]
+        stp = [t_step[i][0].elapsed_time(t_step[i][1]) for i in its]
+        wk = layer_work(sh, rows[kind])
+        ms = float(np.mean(stp))
+        q, a = pct(qkv), pct(att)
+        res[kind] = {"rows_per_layer": rows[kind].n_rows, "steps_timed": len(stp),
+                     "ms_per_step": ms, "ms_per_step_pct": pct(stp), "us_per_layer": ms * 1e3 / L,
+                     "tokens_per_s_per_layer": rows[kind].n_rows / (ms * 1e-3 / L),
+                     "qkv_us": q["mean"], "qkv_us_pct": q, "qkv_bound_us": wk["qkv_bound_us"],
+                     "qkv_bound": wk["qkv_bound"], "qkv_frac": wk["qkv_bound_us"] / q["mean"],
+                     "attn_us": a["mean"], "attn_us_pct": a, "attn_bound_us": wk["attn_bound_us"],
+                     "attn_bound": wk["attn_bound"], "attn_frac": wk["attn_bound_us"] / a["mean"],
+                     "topk_us": float(np.mean(tk)), "topk_us_per_layer": float(np.mean(tk)) / L,
+                     "layer_sum_of_bounds_us": wk["sum_of_bounds_us"],
+                     "layer_overlap_bound_us": wk["overlap_bound_us"],
+                     "layer_roofline_frac": wk["sum_of_bounds_us"] / (ms * 1e3 / L),
+                     "layer_overlap_frac": wk["overlap_bound_us"] / (ms * 1e3 / L),
+                     "alg_bytes_per_layer": wk["qkv_bytes"] + wk["attn_bytes"],
+                     "alg_flops_per_layer": wk["qkv_flops"] + wk["attn_flops"]}
+        eprint(f"[bench] llada_b32 {kind}: {ms:.2f} ms/step, {ms * 1e3 / L:.1f} us/layer "
+               f"(projection {q['mean']:.1f} us = {res[kind]['qkv_frac']:.3f} of its bound, "
+               f"attention {a['mean']:.1f} us = {res[kind]['attn_frac']:.3f})")
+    tot_rows = sum(rows[kinds[i % 2]].n_rows for i in range(K))
+    value = tot_rows / (total_ms * 1e-3 / L)
+    dom = res["full"]
+    dom_work = layer_work(sh, rows["full"])
+    achieved = dom_work["qkv_flops"] / (dom["qkv_us"] * 1e-6) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": total_ms / K, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "LLaDA-8B-shaped 32-layer sweep (d_model 4096, 32x128 heads, bf16), batch 32, "
+                               "context 2048 (prompt 1536 + gen 512); denoising steps alternating full refresh "
+                               "(2048 rows/seq/layer) and cache phase (72 rows/seq/layer: 32 window + 8 new + "
+                               "32 tracked), top-32 once per step",
+                   "layers": L, "batch": wl.n_seq, "d_model": sh.d_model, "heads": sh.n_heads,
+                   "head_dim": sh.head_dim, "parallelism": "single GPU", "timing": "stream launches",
+                   "steps_alternate": list(kinds)},
+        "steps_detail": res,
+        "step_roofline_frac": sum(res[k]["layer_sum_of_bounds_us"] * res[k]["steps_timed"] for k in kinds) * L
+                              / (total_ms * 1e3),
+        "step_overlap_frac": sum(res[k]["layer_overlap_bound_us"] * res[k]["steps_timed"] for k in kinds) * L
+                             / (total_ms * 1e3),
+        "roofline": {"bound": "mfma", "kernel": "qkv_rope_cachewrite (full refresh, 65536 rows per layer)",
+                     "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": counter_traffic("qkv_rope_cachewrite_llada_b32_full_traffic.json"),
+                     "alg_flops_per_launch": dom_work["qkv_flops"],
+                     "alg_bytes_per_launch": dom_work["qkv_bytes"]},
+    }
+    if args.no_extras:
+        return out
+
+    # ---- variants on the same layers ----
+    rows["cache_mid"], sts["cache_mid"], xs["cache_mid"] = rows["cache"], sts["cache"], xs["cache"]
+    for mode in W.BLOCK_CACHE_MODES:
+        rows[mode] = W.block_cache_rows(wl, mode)
+        sts[mode] = run.upload_step(rows[mode])
+        xs[mode] = [W.device_activations(wl, rows[mode], 2, l, dev) for l in range(L)]
+    run8 = FlashCacheRunner(wl, device=dev, kv_format="e4m3")
+    st8 = {"full": run8.upload_step(rows["full"]), "cache": run8.upload_step(rows["cache"])}
+
+    def step8(kind, ev=None):
+        st = st8[kind]
+        run8.map_slots(st)
+        for l in range(L):
+            if ev is not None:
+                ev[l][0].record(stream)
+            run8.cache_update(st, xs[kind][l], Ws[l], l)
+            if ev is not None:
+                ev[l][1].record(stream)
+            run8.attention(st, l, mass_overwrite=l == 0)
+            if ev is not None:
+                ev[l][2].record(stream)
+        run8.topk(clear_mass=False)
+
+    step8("full")
+    step8("cache")
+    torch.cuda.synchronize()
+    KV = max(2, min(5, K // 2))
+    var = {}
+    for kind in ("cache_mid", "cache_e4m3", "cache_unfused") + W.BLOCK_CACHE_MODES:
+        vevs = [[[ev() for _ in range(3)] for _ in range(L + 1)] for _ in range(KV)]
+        a0, a1 = ev(), ev()
+        a0.record(stream)
+        for i in range(KV):
+            if kind == "cache_e4m3":
+                step8("cache", vevs[i])
+            elif kind == "cache_unfused":
+                step("cache", vevs[i], unfused=True)
+            else:
+                step(kind, vevs[i])
+        a1.record(stream)
+        torch.cuda.synchronize()
+        ms = a0.elapsed_time(a1) / KV
+        rk = rows["cache"] if kind in ("cache_e4m3", "cache_unfused") else rows[kind]
+        wk = layer_work(sh, rk, cache_el=1 if kind == "cache_e4m3" else 2)
+        qkv_us = float(np.mean([vevs[i][l][0].elapsed_time(vevs[i][l][1]) for i in range(KV) for l in range(L)])) * 1e3
+        att_us = float(np.mean([vevs[i][l][1].elapsed_time(vevs[i][l][2]) for i in range(KV) for l in range(L)])) * 1e3
+        var[kind] = {"rows_per_layer": rk.n_rows, "ms_per_step": ms, "us_per_layer": ms * 1e3 / L,
+                     "tokens_per_s_per_layer": rk.n_rows / (ms * 1e-3 / L),
+                     "qkv_us": qkv_us, "qkv_bound_us": wk["qkv_bound_us"], "qkv_frac": wk["qkv_bound_us"] / qkv_us,
+                     "qkv_bound": wk["qkv_bound"],
+                     "attn_us": att_us, "attn_bound_us": wk["attn_bound_us"], "attn_frac": wk["attn_bound_us"] / att_us,
+                     "attn_bound": wk["attn_bound"],
+                     "layer_roofline_frac": wk["sum_of_bounds_us"] / (ms * 1e3 / L)}
+        eprint(f"[bench] llada_b32 {kind}: {var[kind]}")
+    var["cache_unfused"]["fused_speedup_per_layer"] = var["cache_unfused"]["ms_per_step"] / res["cache"]["ms_per_step"]
+    var["cache_unfused"]["fused_update_speedup"] = var["cache_unfused"]["qkv_us"] / res["cache"]["qkv_us"]
+    out["block_cache_steps"] = {k: var.pop(k) for k in W.BLOCK_CACHE_MODES}
+    out["cache_phase_middle_layer_score"] = var.pop("cache_mid")
+    out["cache_phase_e4m3_cache"] = var.pop("cache_e4m3")
+    out["unfused_arm_cache_phase"] = var.pop("cache_unfused")
+    del run8, st8, xs, sts, Ws, run
+    return out
+
+
+# ---------------------------------------------------------------------------
+# single-layer workloads (batch 1, mixed batch 8, verify batch 4)
+# ---------------------------------------------------------------------------
+
+def describe(name):
+    return {
+        "llada_b1": "LLaDA-8B-shaped layer (d_model 4096, 32x128 heads, bf16), batch 1, context 512 "
+                    "(prompt 256 + gen 256), cache-phase step: 32 window + 8 new + 32 tracked rows",
+        "mixed_b8": "LLaDA-8B-shaped layer, batch 8 mixed: 6 cache-phase sequences (40-72 rows, context "
+                    "512-1024) + 2 full refreshes (512, 1024 rows)",
+        "verify_b4": "LLaDA-8B-shaped layer, batch 4, context 1024 + 32 view slots, verify step with "
+                     "16 draft + 16 mask views + 40 ordinary rows per sequence under the verify mask",
+    }[name]
+
+
+def _graph_time(fn, copies, K, warmup, stream):
+    """Per-call time of fn(copy) replayed from one captured graph per copy."""
+    import torch
+    graphs = []
+    cs = torch.cuda.Stream()
+    cs.wait_stream(stream)
+    with torch.cuda.stream(cs):
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cs):
+                fn(c)
+            graphs.append(g)
+    stream.wait_stream(cs)
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        graphs[i % copies].replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for i in range(K):
+        graphs[i % copies].replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    return g0.elapsed_time(g1) / K
+
+
+def bench_single(args, dev, name, detail=False):
+    """One single-layer workload: step 0 (full refresh) on the GPU fills the
+    cache and picks the tracked rows; its own step is then timed as plain
+    launches (HIP events around every kernel) and as hipGraph replays over
+    rotated copies (>= 1 GiB).  detail: also the unfused arm, the full
+    refresh, the E4M3 cache and the block-freeze row sets on the same layer."""
+    import numpy as np
+    import torch
+    from io_aware_kv_amd import dllm
+    from io_aware_kv_amd import workloads as W
+    from io_aware_kv_amd.runner import FlashCacheRunner
+    wl = W.make_workload(name)
     sh = wl.shape
     n_out = sh.n_heads * sh.head_dim
 
-    # ---- step 0 (full refresh) on the GPU fills the cache and picks the tracked rows ----
     run = FlashCacheRunner(wl, device=dev, layers=1)
-    w_raw = W.weights(wl, 0)
-    w0 = run.to_device_array(w_raw)
+    w0 = run.to_device_array(W.weights(wl, 0))
     rows0 = W.full_refresh_rows(wl)
     st0 = run.upload_step(rows0)
     x0 = run.to_device_array(W.activations(wl, rows0, 0))
     run.layer_step(st0, x0, w0, 0)
     run.topk(clear_mass=True)
     idx = run.top_idx.cpu().numpy()
-    tracked = [idx[b][idx[b] >= 0] for b in range(wl.n_seq)]
-    rows1 = W.config_step_rows(wl, tracked)
+    rows1 = W.config_step_rows(wl, [idx[b][idx[b] >= 0] for b in range(wl.n_seq)])
     R = rows1.n_rows
     st = run.upload_step(rows1)
     x1 = run.to_device_array(W.activations(wl, rows1, 1))
     del st0, x0
 
-    # ---- buffer rotation over independent copies ----
     per_copy = (w0.numel() * w0.element_size() + 2 * run.k_cache[0].numel() * run.k_cache[0].element_size()
                 + x1.numel() * x1.element_size())
     copies = max(1, int(np.ceil(args.rotate_gib * (1 << 30) / per_copy)))
@@ -106,59 +440,42 @@ def main():
         Ws.append(w0.clone()); Ks.append(run.k_cache[0].clone())
         Vs.append(run.v_cache[0].clone()); Xs.append(x1.clone())
     torch.cuda.synchronize()
-    eprint(f"[bench] {args.workload}: R={R} rows/step, {copies} copies x {per_copy / 2**20:.1f} MiB "
+    eprint(f"[bench] {name}: R={R} rows/step, {copies} copies x {per_copy / 2**20:.1f} MiB "
            f"= {copies * per_copy / 2**30:.2f} GiB rotated")
 
-    def step(i):
-        c = i % copies
-        dllm.qkv_rope_cachewrite_paged(Xs[c], Ws[c], st.pos, st.cu_q, st.logical, run.page_table,
-                                       wl.max_pages, st.slot, st.q, Ks[c], Vs[c], sh.n_heads,
-                                       sh.head_dim, sh.rope_base, st.ws_qkv)
-        dllm.sched_attention(st.q, st.cu_q, Ks[c], Vs[c], run.page_table, wl.max_pages, st.kv_len, st.o,
-                             st.ws_attn, sh.n_heads, sh.head_dim, st.max_kv, mask_bits=st.mask_bits,
-                             mask_off=st.mask_off, mass_count=st.mass_count, max_mass_rows=st.max_mass,
-                             mass_accum=run.mass, n_cap=run.n_cap, mass_overwrite=True)
-        run.topk(clear_mass=False)
+    def qkv(c, s=st, X=Xs):
+        dllm.qkv_rope_cachewrite_paged(X[c], Ws[c], s.pos, s.cu_q, s.logical, run.page_table, wl.max_pages,
+                                       s.slot, s.q, Ks[c], Vs[c], sh.n_heads, sh.head_dim, sh.rope_base, s.ws_qkv)
 
-    # the unfused comparison arm of the same step: slot mapping, projection to
-    # memory, rotary, cache write as launches of their own, then attention, top-k
-    qkv_raw = torch.empty(R, 3 * n_out, dtype=st.q.dtype, device=dev)
+    def attn(c, s=st, mass=True):
+        dllm.sched_attention(s.q, s.cu_q, Ks[c], Vs[c], run.page_table, wl.max_pages, s.kv_len, s.o,
+                             s.ws_attn, sh.n_heads, sh.head_dim, s.max_kv, mask_bits=s.mask_bits,
+                             mask_off=s.mask_off, mass_count=s.mass_count if mass else None,
+                             max_mass_rows=s.max_mass if mass else 0, mass_accum=run.mass if mass else None,
+                             n_cap=run.n_cap, mass_overwrite=mass)
 
-    def step_unfused(i):
-        c = i % copies
-        run.map_slots(st)
-        dllm.qkv_project(Xs[c], Ws[c], qkv_raw, sh.n_heads, sh.head_dim, st.ws_qkv)
-        dllm.rope_apply(qkv_raw, st.pos, st.q, sh.n_heads, sh.head_dim, sh.rope_base)
-        dllm.cache_write(qkv_raw, st.slot, Ks[c], Vs[c], sh.n_heads, sh.head_dim)
-        dllm.sched_attention(st.q, st.cu_q, Ks[c], Vs[c], run.page_table, wl.max_pages, st.kv_len, st.o,
-                             st.ws_attn, sh.n_heads, sh.head_dim, st.max_kv, mask_bits=st.mask_bits,
-                             mask_off=st.mask_off, mass_count=st.mass_count, max_mass_rows=st.max_mass,
-                             mass_accum=run.mass, n_cap=run.n_cap, mass_overwrite=True)
+    def step(c):
+        qkv(c)
+        attn(c)
         run.topk(clear_mass=False)
 
     stream = torch.cuda.current_stream()
     for i in range(args.warmup):
-        step(i)
+        step(i % copies)
     torch.cuda.synchronize()
 
     # ---- plain stream launches, HIP events around every kernel ----
-    K = args.steps
+    K = max(20, args.steps * 10)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(K):
         c = i % copies
         e = evs[i]
         e[0].record(stream)
-        dllm.qkv_rope_cachewrite_paged(Xs[c], Ws[c], st.pos, st.cu_q, st.logical, run.page_table,
-                                       wl.max_pages, st.slot, st.q, Ks[c], Vs[c], sh.n_heads,
-                                       sh.head_dim, sh.rope_base, st.ws_qkv)
+        qkv(c)
         e[1].record(stream)
-        dllm.sched_attention(st.q, st.cu_q, Ks[c], Vs[c], run.page_table, wl.max_pages, st.kv_len, st.o,
-                             st.ws_attn, sh.n_heads, sh.head_dim, st.max_kv, mask_bits=st.mask_bits,
-                             mask_off=st.mask_off, mass_count=st.mass_count, max_mass_rows=st.max_mass,
-                             mass_accum=run.mass, n_cap=run.n_cap, mass_overwrite=True)
+        attn(c)
         e[2].record(stream)
         run.topk(clear_mass=False)
         e[3].record(stream)
@@ -166,151 +483,96 @@ def main():
     torch.cuda.synchronize()
     plain_ms = t_start.elapsed_time(t_end) / K
     names = ["qkv_rope_cachewrite", "sched_attention", "topk_tracked"]
-    per = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)])) * 1e3
-           for j, n in enumerate(names)}
-    per_p50 = {n: float(np.median([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)])) * 1e3
-               for j, n in enumerate(names)}
+    per = {n: pct([evs[i][j].elapsed_time(evs[i][j + 1]) * 1e3 for i in range(K)]) for j, n in enumerate(names)}
 
-    # ---- captured hipGraph replay (one graph per copy) ----
-    graph_ms = None
+    graph_ms = None if args.no_graph else _graph_time(step, copies, K, args.warmup, stream)
+    step_ms = graph_ms if graph_ms is not None else plain_ms
+    wk = layer_work(sh, rows1)
+    # the dominant kernel alone: back-to-back launches (one per copy) in one
+    # graph, so its per-launch time is the kernel plus the dispatch gap only
+    qkv_us = per["qkv_rope_cachewrite"]["mean"]
     if not args.no_graph:
-        graphs = []
-        cs = torch.cuda.Stream()
-        cs.wait_stream(stream)
-        with torch.cuda.stream(cs):
-            for c in range(copies):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=cs):
-                    step(c)
-                graphs.append(g)
-        stream.wait_stream(cs)
-        torch.cuda.synchronize()
-        for i in range(args.warmup):
-            graphs[i % copies].replay()
-        torch.cuda.synchronize()
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        g0.record(stream)
-        for i in range(K):
-            graphs[i % copies].replay()
-        g1.record(stream)
-        torch.cuda.synchronize()
-        graph_ms = g0.elapsed_time(g1) / K
+        qkv_us = _graph_time(lambda _c: [qkv(c) for c in range(copies)], 1, max(1, K // copies), 1,
+                             stream) * 1e3 / copies
+    kernels = {
+        "qkv_rope_cachewrite": {"us": qkv_us, "us_events_pct": per["qkv_rope_cachewrite"],
+                                "alg_bytes": wk["qkv_bytes"], "alg_flops": wk["qkv_flops"],
+                                "bound": wk["qkv_bound"], "frac": wk["qkv_bound_us"] / qkv_us},
+        "sched_attention": {"us": per["sched_attention"]["mean"], "us_pct": per["sched_attention"],
+                            "alg_bytes": wk["attn_bytes"], "alg_flops": wk["attn_flops"],
+                            "bound": wk["attn_bound"], "frac": wk["attn_bound_us"] / per["sched_attention"]["mean"]},
+        "topk_tracked": {"us": per["topk_tracked"]["mean"], "us_pct": per["topk_tracked"]},
+    }
+    hbm = wk["qkv_bound"] == "hbm"
+    out = {
+        "metric": METRIC, "value": R / (step_ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": step_ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": sh.dtype, "data": "synthetic",
+        "config": {"workload": describe(name), "rows_per_step": R, "layers": 1, "batch": wl.n_seq,
+                   "d_model": sh.d_model, "heads": sh.n_heads, "head_dim": sh.head_dim,
+                   "kv_len": [int(k) for k in rows1.kv_len], "parallelism": "single GPU",
+                   "rotated_copies": copies, "timing": "hipGraph replay" if graph_ms else "stream launches"},
+        "plain_launch_ms_per_step": plain_ms, "graph_ms_per_step": graph_ms,
+        "step_sum_of_bounds_us": wk["sum_of_bounds_us"], "step_overlap_bound_us": wk["overlap_bound_us"],
+        "step_roofline_frac": wk["sum_of_bounds_us"] / (step_ms * 1e3),
+        "step_overlap_frac": wk["overlap_bound_us"] / (step_ms * 1e3),
+        "kernels": kernels,
+        "roofline": {"bound": wk["qkv_bound"], "kernel": "qkv_rope_cachewrite",
+                     "achieved": (wk["qkv_bytes"] / 1e9 if hbm else wk["qkv_flops"] / 1e12) / (qkv_us * 1e-6),
+                     "peak": HBM_PEAK_GBS if hbm else MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "GB/s" if hbm else "TFLOP/s",
+                     "frac": wk["qkv_bound_us"] / qkv_us,
+                     "traffic": counter_traffic(f"qkv_rope_cachewrite_{name}_traffic.json")},
+    }
+    eprint(f"[bench] {name}: {step_ms * 1e3:.1f} us/step ({out['step_roofline_frac']:.3f} of the step bound), "
+           f"kernels {({k: round(v['us'], 1) for k, v in kernels.items()})}")
+    if not detail or args.no_graph:
+        return out
 
-    # ---- the dominant kernel alone: back-to-back launches (one per copy) in a
-    # graph, so the per-launch time is the kernel plus the dispatch gap only ----
-    qkv_graph_us = None
-    if not args.no_graph:
-        qg = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(cs):
-            with torch.cuda.graph(qg, stream=cs):
-                for c in range(copies):
-                    dllm.qkv_rope_cachewrite_paged(Xs[c], Ws[c], st.pos, st.cu_q, st.logical, run.page_table,
-                                                   wl.max_pages, st.slot, st.q, Ks[c], Vs[c], sh.n_heads,
-                                                   sh.head_dim, sh.rope_base, st.ws_qkv)
-        stream.wait_stream(cs)
-        torch.cuda.synchronize()
-        reps = max(1, K // copies)
-        qg.replay()
-        torch.cuda.synchronize()
-        q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        q0.record(stream)
-        for _ in range(reps):
-            qg.replay()
-        q1.record(stream)
-        torch.cuda.synchronize()
-        qkv_graph_us = q0.elapsed_time(q1) / (reps * copies) * 1e3
+    # ---- the unfused arm of the same step ----
+    qkv_raw = torch.empty(R, 3 * n_out, dtype=st.q.dtype, device=dev)
 
-    # ---- the unfused arm, same replay scheme ----
-    unfused_ms = None
-    if not args.no_graph and sh.dtype == "bf16":
-        ugraphs = []
-        with torch.cuda.stream(cs):
-            for c in range(copies):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=cs):
-                    step_unfused(c)
-                ugraphs.append(g)
-        stream.wait_stream(cs)
-        torch.cuda.synchronize()
-        for i in range(args.warmup):
-            ugraphs[i % copies].replay()
-        torch.cuda.synchronize()
-        u0, u1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        u0.record(stream)
-        for i in range(K):
-            ugraphs[i % copies].replay()
-        u1.record(stream)
-        torch.cuda.synchronize()
-        unfused_ms = u0.elapsed_time(u1) / K
+    def step_unfused(c):
+        run.map_slots(st)
+        dllm.qkv_project(Xs[c], Ws[c], qkv_raw, sh.n_heads, sh.head_dim, st.ws_qkv)
+        dllm.rope_apply(qkv_raw, st.pos, st.q, sh.n_heads, sh.head_dim, sh.rope_base)
+        dllm.cache_write(qkv_raw, st.slot, Ks[c], Vs[c], sh.n_heads, sh.head_dim)
+        attn(c)
+        run.topk(clear_mass=False)
+    if sh.dtype == "bf16":
+        ums = _graph_time(step_unfused, copies, K, args.warmup, stream)
+        out["unfused_arm"] = {"ms_per_step": ums, "fused_speedup": ums / step_ms,
+                              "note": "slot mapping, projection to memory, rotary, cache write as separate "
+                                      "launches; same attention and top-k"}
 
-    # ---- block-granular caching steps over the same layer, caches and kernels:
-    # DualCache (the current block only) and the active window of PrefixCache /
-    # FreeCache (the current block and every later block) ----
-    block = None
-    full = None
-    if not args.no_graph:
-        block = {}
-        for mode in W.BLOCK_CACHE_MODES + ("full",):
-            rws = W.block_cache_rows(wl, mode) if mode != "full" else rows0
-            stm = run.upload_step(rws)
-            xm = run.to_device_array(W.activations(wl, rws, 2))
-            Xm = [xm] + [xm.clone() for _ in range(copies - 1)]
-            mass = mode == "full"     # the full refresh forms the score and runs the top-k
+    # ---- the full refresh and the block-granular caching steps on the same layer ----
+    block = {}
+    for mode in W.BLOCK_CACHE_MODES + ("full",):
+        rws = W.block_cache_rows(wl, mode) if mode != "full" else rows0
+        stm = run.upload_step(rws)
+        xm = run.to_device_array(W.activations(wl, rws, 2))
+        Xm = [xm] + [xm.clone() for _ in range(copies - 1)]
+        mass = mode == "full"     # the full refresh forms the score and runs the top-k
 
-            def mstep(c, stm=stm, Xm=Xm, mass=mass):
-                dllm.qkv_rope_cachewrite_paged(Xm[c], Ws[c], stm.pos, stm.cu_q, stm.logical, run.page_table,
-                                               wl.max_pages, stm.slot, stm.q, Ks[c], Vs[c], sh.n_heads,
-                                               sh.head_dim, sh.rope_base, stm.ws_qkv)
-                dllm.sched_attention(stm.q, stm.cu_q, Ks[c], Vs[c], run.page_table, wl.max_pages, stm.kv_len,
-                                     stm.o, stm.ws_attn, sh.n_heads, sh.head_dim, stm.max_kv,
-                                     mass_count=stm.mass_count if mass else None,
-                                     max_mass_rows=stm.max_mass if mass else 0,
-                                     mass_accum=run.mass if mass else None, n_cap=run.n_cap,
-                                     mass_overwrite=mass)
-                if mass:
-                    run.topk(clear_mass=False)
-            mg = []
-            with torch.cuda.stream(cs):
-                for c in range(copies):
-                    g = torch.cuda.CUDAGraph()
-                    with torch.cuda.graph(g, stream=cs):
-                        mstep(c)
-                    mg.append(g)
-            stream.wait_stream(cs)
-            torch.cuda.synchronize()
-            for i in range(args.warmup):
-                mg[i % copies].replay()
-            torch.cuda.synchronize()
-            m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            m0.record(stream)
-            for i in range(K):
-                mg[i % copies].replay()
-            m1.record(stream)
-            torch.cuda.synchronize()
-            mms = m0.elapsed_time(m1) / K
-            rec = {"rows": rws.n_rows, "kv_len": [int(k) for k in rws.kv_len], "us_per_step": mms * 1e3,
-                   "tokens_per_s": rws.n_rows / (mms * 1e-3)}
-            if mode == "full":
-                # step bound: projection max(W bytes, MFMA) + attention max(K/V bytes, MFMA), bf16 peaks
-                Rf = rws.n_rows
-                pb = max((3 * n_out * sh.d_model + 4 * Rf * n_out) * 2 / (HBM_PEAK_GBS * 1e9),
-                         2 * Rf * sh.d_model * 3 * n_out / (MFMA_BF16_PEAK_TFLOPS * 1e12))
-                kv = rws.kv_len.astype(np.int64)
-                cu = rws.cu_q.astype(np.int64)
-                af = sum(4 * int(cu[b + 1] - cu[b]) * int(kv[b]) * n_out for b in range(wl.n_seq))
-                ab = max((int(kv.sum()) * 2 + 2 * Rf) * n_out * 2 / (HBM_PEAK_GBS * 1e9),
-                         af / (MFMA_BF16_PEAK_TFLOPS * 1e12))
-                rec["step_roofline_us"] = (pb + ab) * 1e6
-                rec["step_roofline_frac"] = (pb + ab) * 1e6 / rec["us_per_step"]
-                full = rec
-            else:
-                block[mode] = rec
-            del mg, Xm, xm, stm
-        torch.cuda.synchronize()
+        def mstep(c, stm=stm, Xm=Xm, mass=mass):
+            qkv(c, stm, Xm)
+            attn(c, stm, mass)
+            if mass:
+                run.topk(clear_mass=False)
+        mms = _graph_time(mstep, copies, K, args.warmup, stream)
+        wm = layer_work(sh, rws)
+        rec = {"rows": rws.n_rows, "kv_len": [int(k) for k in rws.kv_len], "us_per_step": mms * 1e3,
+               "tokens_per_s": rws.n_rows / (mms * 1e-3), "step_sum_of_bounds_us": wm["sum_of_bounds_us"],
+               "step_roofline_frac": wm["sum_of_bounds_us"] / (mms * 1e3)}
+        if mode == "full":
+            out["full_refresh_step"] = rec
+        else:
+            block[mode] = rec
+        del Xm, xm, stm
+    out["block_cache_steps"] = block
 
     # ---- the same step over one-byte E4M3 caches (filled by a full refresh in that format) ----
-    lowbit = None
-    if not args.no_graph and sh.dtype == "bf16":
+    if sh.dtype == "bf16":
         run8 = FlashCacheRunner(wl, device=dev, layers=1, kv_format="e4m3")
         st8_0 = run8.upload_step(rows0)
         run8.layer_step(st8_0, run8.to_device_array(W.activations(wl, rows0, 0)), w0, 0)
@@ -329,128 +591,11 @@ def main():
                                  max_mass_rows=st8.max_mass, mass_accum=run8.mass, n_cap=run8.n_cap,
                                  mass_overwrite=True)
             run8.topk(clear_mass=False)
-        g8 = []
-        with torch.cuda.stream(cs):
-            for c in range(copies):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=cs):
-                    step8(c)
-                g8.append(g)
-        stream.wait_stream(cs)
-        torch.cuda.synchronize()
-        for i in range(args.warmup):
-            g8[i % copies].replay()
-        torch.cuda.synchronize()
-        l0, l1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        l0.record(stream)
-        for i in range(K):
-            g8[i % copies].replay()
-        l1.record(stream)
-        torch.cuda.synchronize()
-        lms = l0.elapsed_time(l1) / K
-        lowbit = {"cache_format": "E4M3 (one byte per K/V element)", "us_per_step": lms * 1e3,
-                  "tokens_per_s": R / (lms * 1e-3), "vs_bf16_cache": graph_ms / lms if graph_ms else None}
-        del g8, K8, V8
-
-    step_ms = graph_ms if graph_ms is not None else plain_ms
-    value = R / (step_ms * 1e-3)
-
-    # ---- roofline of the dominant kernel (the weight-streaming projection) ----
-    d = sh.d_model
-    el = 2 if sh.dtype == "bf16" else 4
-    qkv_bytes = 3 * n_out * d * el + R * d * el + R * n_out * el + 2 * R * n_out * el
-    # launch duration of the dominant kernel: back-to-back graph launches when
-    # timed (closest to the kernel trace), else the events around each launch
-    qkv_us = qkv_graph_us if qkv_graph_us is not None else per["qkv_rope_cachewrite"]
-    achieved = qkv_bytes / (qkv_us * 1e-6) / 1e9
-    kv_keys = int(rows1.kv_len.sum())
-    attn_bytes = kv_keys * 2 * n_out * el + 2 * R * n_out * el
-    attn_flops = 0
-    for b in range(wl.n_seq):
-        rb = int(rows1.cu_q[b + 1] - rows1.cu_q[b])
-        vis = rows1.visible[b].sum() if rows1.visible is not None else rb * int(rows1.kv_len[b])
-        attn_flops += 4 * int(vis) * n_out
-    qkv_flops = 2 * R * d * 3 * n_out
-    b_qkv = max(qkv_bytes / (HBM_PEAK_GBS * 1e9), qkv_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
-    b_att = max(attn_bytes / (HBM_PEAK_GBS * 1e9), attn_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
-    step_bound_us = (b_qkv + b_att) * 1e6
-    kernels = {
-        "qkv_rope_cachewrite": {"us": qkv_us, "us_events": per["qkv_rope_cachewrite"],
-                                "us_events_p50": per_p50["qkv_rope_cachewrite"],
-                                "alg_bytes": qkv_bytes, "alg_flops": qkv_flops,
-                                "bound": "hbm" if qkv_bytes / 8e12 >= qkv_flops / 2.5e15 else "mfma",
-                                "frac": b_qkv * 1e6 / qkv_us},
-        "sched_attention": {"us": per["sched_attention"], "us_p50": per_p50["sched_attention"],
-                            "alg_bytes": attn_bytes, "alg_flops": attn_flops,
-                            "bound": "hbm" if attn_bytes / 8e12 >= attn_flops / 2.5e15 else "mfma",
-                            "frac": b_att * 1e6 / per["sched_attention"]},
-        "topk_tracked": {"us": per["topk_tracked"]},
-    }
-    traffic = None
-    tfile = os.path.join(ROOT, "profiles", "qkv_rope_cachewrite_llada_b1_traffic.json")
-    if args.workload == "llada_b1" and os.path.exists(tfile):
-        # counter-measured HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by
-        # a plain-copy calibration); only valid for the kernel source profiled
-        import hashlib
-        tj = json.load(open(tfile))
-        src = open(os.path.join(ROOT, tj["source"]), "rb").read()
-        if hashlib.sha256(src).hexdigest() == tj["source_sha256"]:
-            traffic = tj["bytes_per_launch"]
-
-    # ---- optional plain copy (calibrates the HBM byte counters) ----
-    if args.copy_probe_mib:
-        n = args.copy_probe_mib << 20
-        a = torch.empty(n, dtype=torch.uint8, device=dev)
-        b_ = torch.empty_like(a)
-        for _ in range(3):
-            b_.copy_(a)
-        torch.cuda.synchronize()
-
-    # ---- decode side (after the model head), timed on its own ----
-    decode = None
-    if not args.no_decode and not args.no_graph:
-        decode = bench_decode(args, dev)
-
-    # ---- CPU baseline: the oracle on host cores, bounded sample ----
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, rows1, args.cpu_seconds)
-
-    out = {
-        "metric": "refreshed tokens/s per layer (cache-update+attention)",
-        "value": value,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": step_ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": sh.dtype,
-        "data": "synthetic",
-        "config": {"workload": describe(args.workload), "rows_per_step": R, "layers": 1,
-                   "batch": wl.n_seq, "d_model": sh.d_model, "heads": sh.n_heads, "head_dim": sh.head_dim,
-                   "kv_len": [int(k) for k in rows1.kv_len], "parallelism": "single GPU",
-                   "rotated_copies": copies, "timing": "hipGraph replay" if graph_ms else "stream launches"},
-        "plain_launch_ms_per_step": plain_ms,
-        "graph_ms_per_step": graph_ms,
-        "step_roofline_us": step_bound_us,
-        "step_roofline_frac": step_bound_us / (step_ms * 1e3),
-        "kernels": kernels,
-        "roofline": {"bound": "hbm", "kernel": "qkv_rope_cachewrite", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic},
-        "unfused_arm": None if unfused_ms is None else {
-            "ms_per_step": unfused_ms, "fused_speedup": unfused_ms / step_ms,
-            "note": "slot mapping, projection to memory, rotary, cache write as separate launches; same attention and top-k"},
-        "full_refresh_step": full,
-        "e4m3_cache_step": lowbit,
-        "block_cache_steps": block,
-        "decode_side": decode,
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(out), flush=True)
+        lms = _graph_time(step8, copies, K, args.warmup, stream)
+        out["e4m3_cache_step"] = {"cache_format": "E4M3 (one byte per K/V element)", "us_per_step": lms * 1e3,
+                                  "tokens_per_s": R / (lms * 1e-3), "vs_bf16_cache": step_ms / lms}
+        del K8, V8, run8
+    return out
 
 
 def probe(what, dev, launches=3):
@@ -473,7 +618,7 @@ def probe(what, dev, launches=3):
         parts = what.split(":")
         R = int(parts[1])
         if len(parts) > 2:
-            os.environ["DLLM_QKV_KERNEL"] = parts[2]
+            dllm.set_tuning("qkv_kernel", parts[2])
         H, D, d = 32, 128, 4096
         w = torch.randn(3 * H * D, d, device=dev).mul_(d ** -0.5).to(torch.bfloat16)
         x = torch.randn(R, d, device=dev).to(torch.bfloat16)
@@ -524,25 +669,8 @@ def bench_decode(args, dev):
                     dllm.decode_verify(L[c], cu, draft, 0.8, tok, conf, flag, cnt, ws)
             call(0)
             torch.cuda.synchronize()
-            cs = torch.cuda.Stream()
-            cs.wait_stream(stream)
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.stream(cs):
-                with torch.cuda.graph(g, stream=cs):
-                    for c in range(copies):
-                        call(c)
-            stream.wait_stream(cs)
-            torch.cuda.synchronize()
-            g.replay()
-            torch.cuda.synchronize()
-            reps = max(2, min(50, args.steps * 4 // copies))
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(reps):
-                g.replay()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) / (reps * copies) * 1e3
+            reps = max(2, min(50, args.steps * 40 // copies))
+            us = _graph_time(lambda _c: [call(c) for c in range(copies)], 1, reps, 1, stream) * 1e3 / copies
             alg = per + R * (4 + 4 + 1) + len(lens) * 4 + (R * 4 if kind == "verify" else 0)
             gbs = alg / (us * 1e-6) / 1e9
             res[kind] = {"us_per_call": us, "alg_bytes": alg, "achieved_GBs": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
@@ -553,225 +681,93 @@ def bench_decode(args, dev):
     return out
 
 
-def bench_layers(args, dev):
-    """32-layer batch-32 sweep: alternating full-refresh steps (2048 rows per
-    sequence per layer) and cache-phase steps (72 rows per sequence per layer),
-    one top-k per step after the last layer."""
-    import numpy as np
-    import torch
-    from io_aware_kv_amd import dllm
-    from io_aware_kv_amd import workloads as W
-    from io_aware_kv_amd.runner import FlashCacheRunner
-    wl = W.make_workload("llada_b32")
-    sh = wl.shape
-    L, n = sh.layers, sh.n_heads * sh.head_dim
-    run = FlashCacheRunner(wl, device=dev)
-    Ws = [W.device_weights(wl, l, dev) for l in range(L)]
-    rows = {"full": W.full_refresh_rows(wl)}
-    sts = {"full": run.upload_step(rows["full"])}
-    xs = {"full": [W.device_activations(wl, rows["full"], 0, l, dev) for l in range(L)]}
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, untouched, on this host's cores
+# ---------------------------------------------------------------------------
 
-    def step(kind, ev=None, unfused=False):
-        st = sts[kind]
-        mass = kind in ("full", "cache", "cache_mid")    # block-cache steps have no formula-(2) rows
-        run.map_slots(st)
-        for l in range(L):
-            if ev is not None:
-                ev[l][0].record()
-            if unfused:
-                run.cache_update_unfused(st, xs[kind][l], Ws[l], l)
-            else:
-                run.cache_update(st, xs[kind][l], Ws[l], l)
-            if ev is not None:
-                ev[l][1].record()
-            # cache_mid: the score only from the middle layers 5..20 (1-based); the
-            # first scoring layer stores its term, the others add theirs
-            first = 4 if kind == "cache_mid" else 0
-            run.attention(st, l, with_mass=mass and (kind != "cache_mid" or 5 <= l + 1 <= 20),
-                          mass_overwrite=l == first)
-            if ev is not None:
-                ev[l][2].record()
-        if mass:
-            run.topk(clear_mass=False)
-
-    step("full")
-    idx = run.top_idx.cpu().numpy()
-    rows["cache"] = W.config_step_rows(wl, [idx[b][idx[b] >= 0] for b in range(wl.n_seq)])
-    sts["cache"] = run.upload_step(rows["cache"])
-    xs["cache"] = [W.device_activations(wl, rows["cache"], 1, l, dev) for l in range(L)]
-    rows["cache_mid"], sts["cache_mid"], xs["cache_mid"] = rows["cache"], sts["cache"], xs["cache"]
-    for mode in W.BLOCK_CACHE_MODES:
-        rows[mode] = W.block_cache_rows(wl, mode)
-        sts[mode] = run.upload_step(rows[mode])
-        xs[mode] = [W.device_activations(wl, rows[mode], 2, l, dev) for l in range(L)]
-    # the same cache-phase step over one-byte E4M3 caches (a second set of
-    # caches, filled by a full refresh in that format)
-    run8 = FlashCacheRunner(wl, device=dev, kv_format="e4m3")
-    st8 = {"full": run8.upload_step(rows["full"]), "cache": run8.upload_step(rows["cache"])}
-
-    def step8(kind, ev=None):
-        st = st8[kind]
-        run8.map_slots(st)
-        for l in range(L):
-            if ev is not None:
-                ev[l][0].record()
-            run8.cache_update(st, xs[kind][l], Ws[l], l)
-            if ev is not None:
-                ev[l][1].record()
-            run8.attention(st, l, mass_overwrite=l == 0)
-            if ev is not None:
-                ev[l][2].record()
-        run8.topk(clear_mass=False)
-
-    step8("full")
-    for _ in range(max(1, args.warmup // 10)):
-        step("cache")
-        step("full")
-        step8("cache")
-    torch.cuda.synchronize()
-    K = max(2, min(args.steps, 10))
-    res = {}
-    for kind in ("full", "cache", "cache_mid", "cache_e4m3") + W.BLOCK_CACHE_MODES:
-        evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(L)] for _ in range(K)]
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for i in range(K):
-            if kind == "cache_e4m3":
-                step8("cache", evs[i])
-            else:
-                step(kind, evs[i])
-        t1.record()
-        torch.cuda.synchronize()
-        ms = t0.elapsed_time(t1) / K
-        qkv_us = float(np.mean([evs[i][l][0].elapsed_time(evs[i][l][1]) for i in range(K) for l in range(L)])) * 1e3
-        att_us = float(np.mean([evs[i][l][1].elapsed_time(evs[i][l][2]) for i in range(K) for l in range(L)])) * 1e3
-        rk = rows["cache"] if kind == "cache_e4m3" else rows[kind]
-        R = rk.n_rows
-        kv = rk.kv_len.astype(np.int64)
-        cu = rk.cu_q.astype(np.int64)
-        cache_el = 1 if kind == "cache_e4m3" else 2        # bytes per cached K/V element
-        qkv_flops = 2 * R * sh.d_model * 3 * n
-        qkv_bytes = 3 * n * sh.d_model * 2 + R * (16 + 8 * cache_el) * 1024
-        att_flops = int(sum(4 * (cu[b + 1] - cu[b]) * kv[b] * n for b in range(wl.n_seq)))
-        att_bytes = int(kv.sum()) * 2 * n * cache_el + 2 * R * n * 2
-        b_qkv = max(qkv_bytes / (HBM_PEAK_GBS * 1e9), qkv_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
-        b_att = max(att_bytes / (HBM_PEAK_GBS * 1e9), att_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
-        res[kind] = {"rows_per_layer": R, "ms_per_step": ms, "us_per_layer": ms * 1e3 / L,
-                     "tokens_per_s_per_layer": R / (ms * 1e-3 / L),
-                     "qkv_us": qkv_us, "qkv_bound_us": b_qkv, "qkv_frac": b_qkv / qkv_us,
-                     "qkv_bound": "mfma" if qkv_flops / 2.5e15 > qkv_bytes / 8e12 else "hbm",
-                     "attn_us": att_us, "attn_bound_us": b_att, "attn_frac": b_att / att_us,
-                     "attn_bound": "mfma" if att_flops / 2.5e15 > att_bytes / 8e12 else "hbm",
-                     "layer_roofline_frac": (b_qkv + b_att) / (ms * 1e3 / L)}
-        eprint(f"[bench] llada_b32 {kind}: {res[kind]}")
-    # the unfused comparison arm on the cache-phase step (per-layer projection,
-    # rotary and cache write as three launches with q|k|v in memory)
-    step("cache", unfused=True)
-    torch.cuda.synchronize()
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(L)] for _ in range(K)]
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(K):
-        step("cache", evs[i], unfused=True)
-    t1.record()
-    torch.cuda.synchronize()
-    ums = t0.elapsed_time(t1) / K
-    unfused = {"us_per_layer": ums * 1e3 / L,
-               "update_us": float(np.mean([evs[i][l][0].elapsed_time(evs[i][l][1]) for i in range(K) for l in range(L)])) * 1e3,
-               "fused_speedup_per_layer": ums / res["cache"]["ms_per_step"],
-               "fused_update_speedup": float(np.mean([evs[i][l][0].elapsed_time(evs[i][l][1]) for i in range(K) for l in range(L)])) * 1e3 / res["cache"]["qkv_us"]}
-    eprint(f"[bench] llada_b32 cache, unfused arm: {unfused}")
-    tot_rows = sum(res[k]["rows_per_layer"] for k in ("full", "cache"))
-    tot_ms = sum(res[k]["ms_per_step"] for k in ("full", "cache"))
-    block = {k: res.pop(k) for k in W.BLOCK_CACHE_MODES}
-    mid = res.pop("cache_mid")
-    e4m3 = res.pop("cache_e4m3")
-    value = tot_rows / (tot_ms * 1e-3 / L)
-    dom = res["full"]
-    out = {
-        "metric": "refreshed tokens/s per layer (cache-update+attention)",
-        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": 2 * K, "warmup": args.warmup,
-        "ms_per_step": tot_ms / 2, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "LLaDA-8B-shaped 32-layer sweep (d_model 4096, 32x128 heads, bf16), batch 32, "
-                               "context 2048 (prompt 1536 + gen 512); alternating full-refresh (2048 rows/seq) and "
-                               "cache-phase (72 rows/seq) steps, top-32 once per step",
-                   "layers": L, "batch": wl.n_seq, "parallelism": "single GPU", "timing": "stream launches"},
-        "steps_detail": res,
-        "block_cache_steps": block,
-        "cache_phase_middle_layer_score": mid,
-        "cache_phase_e4m3_cache": e4m3,
-        "unfused_arm_cache_phase": unfused,
-        "roofline": {"bound": "mfma", "kernel": "qkv_rope_cachewrite (full refresh)",
-                     "achieved": 2 * dom["rows_per_layer"] * sh.d_model * 3 * n / (dom["qkv_us"] * 1e-6) / 1e12,
-                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": dom["qkv_frac"], "traffic": None},
-        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_b32(wl, rows["cache"], args.cpu_seconds),
-    }
-    print(json.dumps(out), flush=True)
+def host_setup():
+    """Set the BLAS pool to every core this process may run on (capped at the
+    thread share the environment grants, OMP_NUM_THREADS, where set) and
+    describe the host: cores, CPU model, BLAS library."""
+    visible = len(os.sched_getaffinity(0))
+    share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    cores = min(visible, share) if share > 0 else visible
+    limiter = None
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(limits=cores, user_api="blas")
+        blas = [f"{i.get('internal_api')} {i.get('version')} ({os.path.basename(i.get('filepath', ''))}, "
+                f"{i.get('num_threads')} threads)" for i in threadpool_info() if i.get("user_api") == "blas"]
+    except Exception as e:       # threadpoolctl missing
+        blas = [f"unknown ({e.__class__.__name__})"]
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return limiter, {"cores": cores, "cores_visible": visible, "cpu_model": model, "blas": blas}
 
 
-def cpu_baseline_b32(wl, rows, seconds):
-    """The oracle on one sequence's cache-phase rows of one layer (72 rows over
-    2048 keys), repeated for about `seconds`; tokens/s scales linearly with
-    rows, sequences and layers, so this is the batch figure too."""
+def cpu_baseline_b32():
+    """The oracle on a bounded sample of the headline workload: one layer,
+    two sequences of each step type (full refresh: 2048 rows over 2048 keys;
+    cache phase: 72 rows over 2048 keys), each sequence a separate oracle
+    call.  The oracle treats sequences and layers independently, so its
+    refreshed tokens/s per layer for the whole batch follows by scaling the
+    time linearly by sequences (32 / 2); labelled extrapolated."""
     import numpy as np
     import oracle as O
     from io_aware_kv_amd import workloads as W
+    limiter, host = host_setup()
+    wl = W.make_workload("llada_b32")
     sh = wl.shape
     n = sh.n_heads * sh.head_dim
-    r0, r1 = int(rows.cu_q[0]), int(rows.cu_q[1])
-    kv = int(rows.kv_len[0])
     rng = np.random.default_rng(0)
     w = rng.standard_normal((3 * n, sh.d_model)) / np.sqrt(sh.d_model)
-    x = rng.standard_normal((r1 - r0, sh.d_model))
-    pages = (kv + W.PAGE - 1) // W.PAGE
+    pages = wl.max_pages
     table = O.build_block_table([pages], list(range(pages)), pages, pages)
     kc = np.zeros((pages * W.PAGE, n))
     vc = np.zeros_like(kc)
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        O.layer_step(x, w, rows.pos[r0:r1], rows.logical[r0:r1], [0, r1 - r0], [kv], [int(rows.mass_count[0])],
-                     kc, vc, table, sh.n_heads, sh.head_dim, sh.rope_base, W.PAGE)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": (r1 - r0) * reps / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} oracle layer steps of one sequence's cache-phase rows ({r1 - r0} rows, {kv} keys, "
-                      f"fp64 NumPy) in {el:.1f} s; extrapolated linearly to the batch"}
+    full = W.full_refresh_rows(wl)
+    cache = W.config_step_rows(wl, W.seeded_tracked(wl, 1))
+    t, meas, rows_sampled = {}, {}, {}
+    for kind, rws in (("full", full), ("cache", cache)):
+        el = 0.0
+        nr = 0
+        for b in (0, 1):
+            r0, r1 = int(rws.cu_q[b]), int(rws.cu_q[b + 1])
+            x = rng.standard_normal((r1 - r0, sh.d_model))
+            t0 = time.perf_counter()
+            O.layer_step(x, w, rws.pos[r0:r1], rws.logical[r0:r1], [0, r1 - r0], [int(rws.kv_len[b])],
+                         [int(rws.mass_count[b])], kc, vc, table, sh.n_heads, sh.head_dim, sh.rope_base, W.PAGE)
+            el += time.perf_counter() - t0
+            nr += r1 - r0
+        meas[kind] = el
+        t[kind] = el * wl.n_seq / 2          # per layer for the batch, extrapolated
+        rows_sampled[kind] = nr
+    value = (full.n_rows + cache.n_rows) / (t["full"] + t["cache"])
+    del limiter
+    return {"value": value, "unit": "tokens/s", **host, "kind": "oracle",
+            "sample": f"extrapolated: one layer, 2 of the 32 sequences of each step type (full refresh "
+                      f"{rows_sampled['full']} rows, cache phase {rows_sampled['cache']} rows, 2048 keys each), "
+                      f"fp64 NumPy, measured {meas['full']:.1f} s + {meas['cache']:.1f} s and scaled by 16 to the "
+                      f"batch; the same alternating mix of step types as the GPU figure"}
 
 
-def describe(name):
-    return {
-        "llada_b1": "LLaDA-8B-shaped layer (d_model 4096, 32x128 heads, bf16), batch 1, context 512 "
-                    "(prompt 256 + gen 256), cache-phase step: 32 window + 8 new + 32 tracked rows",
-        "mixed_b8": "LLaDA-8B-shaped layer, batch 8 mixed: 6 cache-phase sequences (40-72 rows, context "
-                    "512-1024) + 2 full refreshes (512, 1024 rows)",
-        "verify_b4": "LLaDA-8B-shaped layer, batch 4, context 1024 + 32 view slots, verify step with "
-                     "16 draft + 16 mask views + 40 ordinary rows per sequence under the verify mask",
-    }[name]
-
-
-def cpu_baseline(wl, rows, seconds):
-    """The oracle, untouched, on this host's cores: the same step (projection,
-    RoPE, scatter, attention, formula-(2) term, top-k) on the same rows,
-    repeated for about `seconds`."""
+def cpu_baseline(name, seconds):
+    """The oracle on the same single-layer step (projection, RoPE, scatter,
+    attention, formula-(2) term, top-k), repeated for about `seconds`."""
     import numpy as np
     import oracle as O
     from io_aware_kv_amd import workloads as W
+    limiter, host = host_setup()
+    wl = W.make_workload(name)
     sh = wl.shape
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    rows = W.config_step_rows(wl, W.seeded_tracked(wl, 1))
     table = O.build_block_table(wl.seq_pages, wl.pool_perm, wl.pool_pages, wl.max_pages)
     w = W.as_f64(wl, W.weights(wl, 0))
     x = W.as_f64(wl, W.activations(wl, rows, 1))
@@ -789,7 +785,8 @@ def cpu_baseline(wl, rows, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return {"value": rows.n_rows * reps / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    del limiter
+    return {"value": rows.n_rows * reps / el, "unit": "tokens/s", **host, "kind": "oracle",
             "sample": f"{reps} oracle steps of the same workload ({rows.n_rows} rows each, fp64 NumPy) "
                       f"in {el:.1f} s"}
 
