@@ -17,6 +17,7 @@ from .flashcache import (  # noqa: F401
     row_slots,
     project,
     rope,
+    round_bf16,
     scatter,
     attention,
     column_mass,

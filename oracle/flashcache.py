@@ -134,6 +134,18 @@ def rope(t: np.ndarray, pos: Sequence[int], base: float) -> np.ndarray:
     return out
 
 
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """Round to the nearest bf16 value, ties to even: 8 significant bits
+    (the bfloat16 format keeps float32's 8-bit exponent and 7 stored fraction
+    bits), spacing 2^(e-8) for |a| in [2^(e-1), 2^e), and 2^-133 below the
+    smallest normal 2^-126.  Models a buffer of the path that stores bf16 (q,
+    and the K/V cache rows, written once per step)."""
+    a = np.asarray(a, dtype=np.float64)
+    _, e = np.frexp(a)                      # a = m 2^e with 1/2 <= |m| < 1 (e = 0 at 0)
+    e = np.maximum(e, -125)
+    return np.ldexp(np.rint(np.ldexp(a, 8 - e)), e - 8)
+
+
 def scatter(cache: np.ndarray, slots: Sequence[int], rows: np.ndarray) -> np.ndarray:
     """Write rows into the flat cache at the given slots; nothing else changes
     ([FD] 核心方法: K/V go straight into the preallocated flat layout)."""
@@ -245,19 +257,26 @@ def topk(mass: np.ndarray, eligible: np.ndarray, k: int) -> Tuple[np.ndarray, np
 
 def layer_step(x, w, pos, logical, cu_q, kv_len, mass_count, k_cache, v_cache, page_table,
                n_heads: int, head_dim: int, rope_base: float, page_size: int,
-               visible=None, kv_format: str = "plain"):
+               visible=None, kv_format: str = "plain", store: str = "exact"):
     """Steps a1..a5 of one layer in the method's order: project, rotate q and
     k, write K/V rows into the cache, attend over the updated cache, and form
     this layer's formula-(2) term.  Returns a dict of float64 arrays.
 
     kv_format "e4m3": the rows are stored in the low-bit cache format of
     oracle/lowbit.py, so the cache (and "k", "v" of the result) hold the
-    stored values, which the attention reads."""
+    stored values, which the attention reads.
+    store "bf16": q, K and V are rounded once to bf16 where the step stores
+    them (q between the cache update and the attention, K/V in a bf16 cache),
+    so the attention reads the stored values; "exact" keeps them in float64."""
     n = n_heads * head_dim
     q, k, v = project(x, w, n)
     R = q.shape[0]
     q = rope(q.reshape(R, n_heads, head_dim), pos, rope_base).reshape(R, n)
     k = rope(k.reshape(R, n_heads, head_dim), pos, rope_base).reshape(R, n)
+    if store == "bf16":
+        q, k, v = round_bf16(q), round_bf16(k), round_bf16(v)
+    elif store != "exact":
+        raise OracleError(f"unknown store precision {store}")
     if kv_format == "e4m3":
         k, v = e4m3_round(k), e4m3_round(v)
     elif kv_format != "plain":

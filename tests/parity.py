@@ -84,6 +84,15 @@ class Case:
                                  self.rows0.cu_q, self.rows0.kv_len, self.rows0.mass_count, kc, vc,
                                  self.table, sh.n_heads, sh.head_dim, sh.rope_base, W.PAGE)
         self.top0 = O.topk(self.out0["mass"], wl.eligible().astype(bool), sh.top_k)
+        # the same step with the path's bf16 stores of q, K and V modelled (the
+        # attention reads the stored values): the reference for o where the
+        # planted rows' large scores magnify the storage rounding
+        self.out0_store = None
+        if heavy and self.kind == "bf16":
+            self.out0_store = O.layer_step(W.as_f64(wl, self.x0_raw), w64, self.rows0.pos, self.rows0.logical,
+                                           self.rows0.cu_q, self.rows0.kv_len, self.rows0.mass_count, kc, vc,
+                                           self.table, sh.n_heads, sh.head_dim, sh.rope_base, W.PAGE,
+                                           store="bf16")
         # step 1 starts from the step-0 cache rounded to the path dtype
         rnd = bf16_round if self.kind == "bf16" else (lambda a: np.asarray(a, np.float32).astype(np.float64))
         self.k1_in = rnd(self.out0["k_cache"])

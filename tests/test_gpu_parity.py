@@ -66,7 +66,8 @@ def run_gpu_step(c: Case, step: int, gpu, fused_slots: bool = True, unfused: boo
             "cnt": run.top_cnt.cpu().numpy(), "mass_after": run.mass.cpu().numpy()}
 
 
-def compare_step(c: Case, g: dict, step: int, exact_topk: bool = False, o_scale: float = 1.0):
+def compare_step(c: Case, g: dict, step: int, exact_topk: bool = False, o_ref=None):
+    """o_ref: the oracle o to gate o against (default: the step's own)."""
     out = c.out0 if step == 0 else c.out1
     atol, rtol = TOL[c.kind]
     # integer outputs, bit-exact
@@ -79,7 +80,7 @@ def compare_step(c: Case, g: dict, step: int, exact_topk: bool = False, o_scale:
     infos = [close(g["q"], out["q"], atol, rtol, "q_out"),
              close(g["k_cache"][out["slots"]], out["k"], atol, rtol, "K rows"),
              close(g["v_cache"][out["slots"]], out["v"], atol, rtol, "V rows"),
-             close(g["o"], out["o"], atol * o_scale, rtol * o_scale, "o")]
+             close(g["o"], out["o"] if o_ref is None else o_ref, atol, rtol, "o")]
     ma, mr = MASS_TOL[c.kind]
     infos.append(close(g["mass"], out["mass"], ma, mr, "mass"))
     assert not g["mass_after"].any(), "top-k did not clear the score"
@@ -101,18 +102,22 @@ def test_workload_step_parity(name, step, gpu):
 @pytest.mark.parametrize("name", ["llada_b1", "verify_b4"])
 def test_heavy_hitter_topk_exact(name, gpu):
     """Planted heavy hitters (step-0 x rows scaled by 2) separate the top-k,
-    so the GPU's set must equal the oracle's exactly.  Scaling x by 2 scales q
-    and k of those rows by 2 and their scores by 4, and the bf16 storage of q
-    and k moves a score in proportion to its size, so the o gate of this
-    variant is 4x the workload tolerance; every other output keeps its gate."""
+    so the GPU's set must equal the oracle's exactly.  Every output keeps the
+    workload gate.  Scaling x by 2 scales q and k of those rows by 2 and their
+    scores by 4, and the bf16 stores of q and of the cached K move a score in
+    proportion to its size: o is gated against the oracle with those stores
+    modelled (q, K, V rounded once to bf16 before the attention); its distance
+    from the float64-stored oracle is logged."""
     log(f"[gpu] heavy-hitter top-k {name}")
     c = case(name, heavy=True)
     g = run_gpu_step(c, 0, gpu)
     atol, rtol = TOL[c.kind]
-    m = measure(g["o"], c.out0["o"], atol, rtol, "o at the workload gate")
-    log(f"   heavy {name} o at the workload gate: max_abs={m['max_abs']:.3e} n_bad={m['n_bad']} "
+    m = measure(g["o"], c.out0["o"], atol, rtol, "o against the float64-stored oracle")
+    log(f"   heavy {name} o against the float64-stored oracle: max_abs={m['max_abs']:.3e} n_bad={m['n_bad']} "
         f"worst err/limit={m['worst_ratio']:.3f}")
-    compare_step(c, g, 0, exact_topk=True, o_scale=4.0)
+    m = measure(c.out0_store["o"], c.out0["o"], atol, rtol, "bf16-stored oracle vs float64-stored oracle")
+    log(f"   heavy {name} oracle with bf16 stores vs without: max_abs={m['max_abs']:.3e} n_bad={m['n_bad']}")
+    compare_step(c, g, 0, exact_topk=True, o_ref=c.out0_store["o"])
 
 
 @pytest.mark.parametrize("name,splits", [("tiny_bf16", "2"), ("llada_b1", "1"), ("llada_b1", "3"),

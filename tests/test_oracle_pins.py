@@ -498,3 +498,74 @@ def test_layer_range_score_sums_only_its_layers():
     for bad in ((0, 3), (5, 33), (7, 6)):
         with pytest.raises(O.OracleError):
             O.layer_range_score(terms, *bad)
+
+
+# ---------------------------------------------------------------------------
+# bf16 store rounding (round_bf16)
+# ---------------------------------------------------------------------------
+
+def _bf16_values(bits):
+    """bf16 bit patterns -> their values (the upper half of a float32)."""
+    with np.errstate(invalid="ignore"):            # NaN patterns
+        return (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def test_round_bf16_fixes_every_bf16_value():
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    v = _bf16_values(bits)
+    fin = np.isfinite(v)
+    got = O.round_bf16(v[fin])
+    assert np.array_equal(got, v[fin])
+    assert np.array_equal(np.signbit(got), np.signbit(v[fin]))
+
+
+def test_round_bf16_ties_to_even_and_nearest():
+    # consecutive positive finite bf16 values (normals and subnormals) and the
+    # exact midpoints between them: ties go to the even bit pattern, and a
+    # hair either side of a tie goes to the nearer neighbour
+    bits = np.arange(0, 0x7f7f, dtype=np.uint32)
+    lo, hi = _bf16_values(bits), _bf16_values(bits + 1)
+    mid = (lo + hi) / 2                      # exact in float64
+    even = np.where(bits % 2 == 0, lo, hi)
+    assert np.array_equal(O.round_bf16(mid), even)
+    assert np.array_equal(O.round_bf16(-mid), -even)
+    gap = hi - lo
+    assert np.array_equal(O.round_bf16(mid - gap / 64), lo)
+    assert np.array_equal(O.round_bf16(mid + gap / 64), hi)
+    assert O.round_bf16(1.0 + 2.0 ** -8) == 1.0                  # tie at 1: to the even 1.0
+    assert O.round_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6  # tie above 1 + 2^-7: to the even one
+
+
+def test_round_bf16_matches_float32_bit_rounding():
+    # an independent route for float32 inputs: add 0x7fff plus the lowest kept
+    # bit to the float32 pattern and drop the low half
+    rng = np.random.default_rng(11)
+    f = (rng.standard_normal(200000) * np.exp(rng.uniform(-30, 30, 200000))).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7fff + ((u >> 16) & 1)) >> 16).astype(np.uint32)
+    assert np.array_equal(O.round_bf16(f.astype(np.float64)), _bf16_values(r))
+
+
+def test_layer_step_bf16_store_reads_the_rounded_rows():
+    # with store="bf16" the step's q, K and V are the rounded ones, the cache
+    # holds them, and the attention equals the exact oracle run on those values
+    rng = np.random.default_rng(3)
+    H, D, d = 2, 8, 16
+    kv = 24
+    table = O.build_block_table([2], [1, 0], 2, 2)
+    x = rng.standard_normal((5, d))
+    w = rng.standard_normal((3 * H * D, d)) / 4
+    logical = np.array([3, 7, 11, 20, 23])
+    kc = rng.standard_normal((32, H * D))
+    vc = rng.standard_normal((32, H * D))
+    a = O.layer_step(x, w, logical, logical, [0, 5], [kv], [2], kc, vc, table, H, D, 1e4, 16, store="bf16")
+    b = O.layer_step(x, w, logical, logical, [0, 5], [kv], [2], kc, vc, table, H, D, 1e4, 16)
+    for key in ("q", "k", "v"):
+        assert np.array_equal(a[key], O.round_bf16(b[key]))
+        assert not np.array_equal(a[key], b[key])
+    slots = a["slots"]
+    assert np.array_equal(a["k_cache"][slots], a["k"]) and np.array_equal(a["v_cache"][slots], a["v"])
+    o, _ = O.attention(a["q"], a["k_cache"], a["v_cache"], table, [0, 5], [kv], H, D, 16)
+    assert np.array_equal(o, a["o"])
+    with pytest.raises(O.OracleError):
+        O.layer_step(x, w, logical, logical, [0, 5], [kv], [2], kc, vc, table, H, D, 1e4, 16, store="fp16")
