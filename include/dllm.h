@@ -258,6 +258,33 @@ int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_heads, int 
                          size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * dllm_sched_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops and harnesses that forbid
+ * allocation): no workspace argument.  The scratch memory that
+ * dllm_sched_attention takes from its workspace (split partials, the score's
+ * window-row probabilities) comes from a static device array of
+ * DLLM_NOALLOC_SCRATCH_BYTES (64 MiB), one per GPU, held from the library's
+ * first use on that GPU until the process ends.  Arguments, results and
+ * errors as dllm_sched_attention; a call whose workspace query
+ * (dllm_sched_attention_workspace with the same sizes) exceeds the array
+ * returns DLLM_ERR_UNSUPPORTED before any work is enqueued (for example a
+ * batch of 32 sequences of 2048 keys with 32 score rows each needs 132 MiB),
+ * and DLLM_ERR_HIP if the array's device address cannot be obtained.  The
+ * call allocates nothing.  Every call on one GPU shares that GPU's array,
+ * which keeps the last call's contents (no call needs it cleared): calls
+ * that overlap on one GPU (other streams, other host threads) race on it and
+ * must be serialised by the caller.
+ */
+#define DLLM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int dllm_sched_attention_noalloc(dllm_dtype dt, int n_seq, int n_rows, int n_heads, int head_dim,
+                                 int page_size, int max_kv, const void* q, const int32_t* cu_q,
+                                 const void* k_cache, const void* v_cache, int64_t cache_rows,
+                                 const int32_t* page_table, int max_pages, const int32_t* kv_len,
+                                 const uint32_t* mask_bits, const int64_t* mask_off, int64_t mask_words,
+                                 const int32_t* mass_count, int max_mass_rows, float* mass_accum,
+                                 int mass_overwrite, int n_cap, void* o, hipStream_t stream);
+
+/*
  * a6: per-sequence top-k of the accumulated score over eligible positions.
  * [FD] 方法步骤详情 step 4: the top-k decoded tokens by formula (2), with the
  * newly decoded tokens, form the next tracked set (the caller adds the new

@@ -38,6 +38,8 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "common.h"
 
 namespace {
@@ -1216,15 +1218,20 @@ extern "C" size_t dllm_sched_attention_workspace(dllm_dtype dt, int n_seq, int n
                           choose_splits(dt, n_seq, n_rows, n_heads, max_kv));
 }
 
-extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_heads,
-                                    int head_dim, int page_size, int max_kv, const void* q,
-                                    const int32_t* cu_q, const void* k_cache, const void* v_cache,
-                                    int64_t cache_rows, const int32_t* page_table, int max_pages,
-                                    const int32_t* kv_len, const uint32_t* mask_bits,
-                                    const int64_t* mask_off, int64_t mask_words,
-                                    const int32_t* mass_count, int max_mass_rows,
-                                    float* mass_accum, int mass_overwrite, int n_cap, void* o, void* workspace,
-                                    size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// Both attention entry points: argument checks, then the launches.  The
+// workspace is either the caller's (dllm_sched_attention) or the static
+// scratch array (dllm_sched_attention_noalloc): get_ws(ws_need, &ptr, &bytes)
+// supplies it once the size is known, after every host-side check, or
+// returns an error before anything is enqueued.
+template <typename GetWs>
+int attention_call(dllm_dtype dt, int n_seq, int n_rows, int n_heads, int head_dim, int page_size,
+                   int max_kv, const void* q, const int32_t* cu_q, const void* k_cache,
+                   const void* v_cache, int64_t cache_rows, const int32_t* page_table, int max_pages,
+                   const int32_t* kv_len, const uint32_t* mask_bits, const int64_t* mask_off,
+                   int64_t mask_words, const int32_t* mass_count, int max_mass_rows, float* mass_accum,
+                   int mass_overwrite, int n_cap, void* o, GetWs get_ws, hipStream_t stream) {
     int st = check_attn(dt, n_seq, n_rows, n_heads, head_dim, page_size, max_kv, n_cap);
     if (st != DLLM_OK) return st;
     DLLM_CHECK_ARG(max_pages > 0 && cache_rows >= 16);
@@ -1243,7 +1250,9 @@ extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_
     const int splits = choose_splits(dt, n_seq, n_rows, n_heads, max_kv);
     const int mass_rows = want_mass ? max_mass_rows : 0;
     const size_t ws_need = dt == DLLM_F32 ? 0 : bf16_workspace(n_seq, n_rows, n_heads, max_kv, mass_rows, splits);
-    DLLM_CHECK_ARG(workspace_bytes >= ws_need && (ws_need == 0 || workspace != nullptr));
+    void* workspace = nullptr;
+    st = get_ws(ws_need, &workspace);
+    if (st != DLLM_OK) return st;
 
     AttnArgs a{};
     a.n_seq = n_seq;
@@ -1309,4 +1318,76 @@ extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_
     }
     DLLM_CHECK_LAUNCH();
     return DLLM_OK;
+}
+
+}  // namespace
+
+// Scratch memory of the allocation-free entry point, at file scope: one copy
+// per device (each GPU that loads the library holds it until the process
+// ends).  In host code `scratch` names a host-side stand-in; kernels get the
+// device address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[DLLM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = DLLM_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the current device's copy of `scratch` (its address as host code must pass
+// it), looked up with that device current on its first use
+int scratch_for_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return DLLM_ERR_HIP;
+    if (dev >= kMaxDevices) return DLLM_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DLLM_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DLLM_OK;
+}
+
+}  // namespace
+
+extern "C" int dllm_sched_attention(dllm_dtype dt, int n_seq, int n_rows, int n_heads,
+                                    int head_dim, int page_size, int max_kv, const void* q,
+                                    const int32_t* cu_q, const void* k_cache, const void* v_cache,
+                                    int64_t cache_rows, const int32_t* page_table, int max_pages,
+                                    const int32_t* kv_len, const uint32_t* mask_bits,
+                                    const int64_t* mask_off, int64_t mask_words,
+                                    const int32_t* mass_count, int max_mass_rows,
+                                    float* mass_accum, int mass_overwrite, int n_cap, void* o, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+    auto caller_ws = [&](size_t need, void** ws) -> int {
+        DLLM_CHECK_ARG(workspace_bytes >= need && (need == 0 || workspace != nullptr));
+        *ws = workspace;
+        return DLLM_OK;
+    };
+    return attention_call(dt, n_seq, n_rows, n_heads, head_dim, page_size, max_kv, q, cu_q, k_cache, v_cache,
+                          cache_rows, page_table, max_pages, kv_len, mask_bits, mask_off, mask_words,
+                          mass_count, max_mass_rows, mass_accum, mass_overwrite, n_cap, o, caller_ws, stream);
+}
+
+extern "C" int dllm_sched_attention_noalloc(dllm_dtype dt, int n_seq, int n_rows, int n_heads,
+                                            int head_dim, int page_size, int max_kv, const void* q,
+                                            const int32_t* cu_q, const void* k_cache, const void* v_cache,
+                                            int64_t cache_rows, const int32_t* page_table, int max_pages,
+                                            const int32_t* kv_len, const uint32_t* mask_bits,
+                                            const int64_t* mask_off, int64_t mask_words,
+                                            const int32_t* mass_count, int max_mass_rows,
+                                            float* mass_accum, int mass_overwrite, int n_cap, void* o,
+                                            hipStream_t stream) {
+    auto static_ws = [](size_t need, void** ws) -> int {
+        *ws = nullptr;
+        if (need == 0) return DLLM_OK;
+        DLLM_CHECK_SUP(need <= kNoAllocScratchBytes);
+        return scratch_for_current_device(ws);
+    };
+    return attention_call(dt, n_seq, n_rows, n_heads, head_dim, page_size, max_kv, q, cu_q, k_cache, v_cache,
+                          cache_rows, page_table, max_pages, kv_len, mask_bits, mask_off, mask_words,
+                          mass_count, max_mass_rows, mass_accum, mass_overwrite, n_cap, o, static_ws, stream);
 }

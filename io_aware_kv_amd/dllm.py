@@ -24,8 +24,9 @@ EXPORTS = (
     "dllm_qkv_project", "dllm_rope_apply", "dllm_cache_write",
     "dllm_sched_attention_workspace", "dllm_sched_attention", "dllm_topk_tracked",
     "dllm_confidence_workspace", "dllm_confidence_argmax", "dllm_confidence_commit", "dllm_verify_accept",
-    "dllm_decode_commit", "dllm_decode_verify", "dllm_set_tuning",
+    "dllm_decode_commit", "dllm_decode_verify", "dllm_set_tuning", "dllm_sched_attention_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 64 << 20     # DLLM_NOALLOC_SCRATCH_BYTES
 
 
 class DllmError(RuntimeError):
@@ -78,7 +79,10 @@ def load() -> ctypes.CDLL:
     lib.dllm_decode_verify.argtypes = [_i32, _i32, _i32, _vp, _i32, _vp, _i64, _vp, _f32, _vp, _vp, _vp,
                                        _vp, _vp, _sz, _vp]
     lib.dllm_set_tuning.argtypes = [ctypes.c_char_p, ctypes.c_char_p]
-    for name in ("dllm_set_tuning", "dllm_build_block_table", "dllm_map_slots", "dllm_qkv_rope_cachewrite",
+    lib.dllm_sched_attention_noalloc.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
+                                                 _i64, _vp, _i32, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _i32,
+                                                 _i32, _vp, _vp]
+    for name in ("dllm_set_tuning", "dllm_sched_attention_noalloc", "dllm_build_block_table", "dllm_map_slots", "dllm_qkv_rope_cachewrite",
                  "dllm_qkv_rope_cachewrite_paged", "dllm_qkv_project", "dllm_rope_apply", "dllm_cache_write",
                  "dllm_sched_attention", "dllm_topk_tracked", "dllm_confidence_argmax", "dllm_confidence_commit",
                  "dllm_verify_accept", "dllm_decode_commit", "dllm_decode_verify"):
@@ -234,6 +238,21 @@ def sched_attention(q, cu_q, k_cache, v_cache, page_table, max_pages: int, kv_le
         _ptr(k_cache), _ptr(v_cache), k_cache.shape[0], _ptr(page_table), max_pages, _ptr(kv_len),
         _ptr(mask_bits), _ptr(mask_off), mask_words, _ptr(mass_count), max_mass_rows,
         _ptr(mass_accum), int(bool(mass_overwrite)), n_cap, _ptr(o), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def sched_attention_noalloc(q, cu_q, k_cache, v_cache, page_table, max_pages: int, kv_len, o,
+                            n_heads: int, head_dim: int, max_kv: int, mask_bits=None, mask_off=None,
+                            mass_count=None, max_mass_rows: int = 0, mass_accum=None, n_cap: int = 0,
+                            page_size: int = PAGE, mass_overwrite: bool = False, stream=None) -> None:
+    """sched_attention with the library's static scratch array in place of a
+    workspace (no device allocation by the call)."""
+    dt = cache_dtype_code(q, k_cache)
+    mask_words = 0 if mask_bits is None else mask_bits.numel()
+    _check("dllm_sched_attention_noalloc", load().dllm_sched_attention_noalloc(
+        dt, cu_q.numel() - 1, q.shape[0], n_heads, head_dim, page_size, max_kv, _ptr(q), _ptr(cu_q),
+        _ptr(k_cache), _ptr(v_cache), k_cache.shape[0], _ptr(page_table), max_pages, _ptr(kv_len),
+        _ptr(mask_bits), _ptr(mask_off), mask_words, _ptr(mass_count), max_mass_rows,
+        _ptr(mass_accum), int(bool(mass_overwrite)), n_cap, _ptr(o), _stream(stream)))
 
 
 def topk_tracked(mass, eligible, k: int, idx, val, count, clear_mass: bool = False, stream=None) -> None:

@@ -230,3 +230,17 @@ def test_tuning_override(lib):
     for name in (b"tiled", b"gemm", b"g256x256", b"g128x256o2", b"g128x128"):
         assert lib.dllm_set_tuning(b"qkv_kernel", name) == 0
     assert lib.dllm_set_tuning(b"qkv_kernel", b"") == 0
+
+
+def test_noalloc_refuses_before_touching_the_device(lib):
+    # the batch-32, 2048-key score needs more scratch than the static array:
+    # refused with UNSUPPORTED before any HIP call (none is possible here)
+    need = lib.dllm_sched_attention_workspace(1, 32, 2304, 32, 128, 2048, 2048, 32)
+    assert need > dllm.NOALLOC_SCRATCH_BYTES
+    fake = ctypes.c_void_p(0x1000)
+    rc = lib.dllm_sched_attention_noalloc(1, 32, 2304, 32, 128, 16, 2048, fake, fake, fake, fake, 65536, fake,
+                                          128, fake, None, None, 0, fake, 32, fake, 1, 2048, fake, None)
+    assert rc == -2
+    # argument errors as the workspace-taking call
+    assert lib.dllm_sched_attention_noalloc(1, 1, 72, 32, 128, 16, 512, None, fake, fake, fake, 512, fake,
+                                            32, fake, None, None, 0, None, 0, None, 0, 0, fake, None) == -1
