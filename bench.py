@@ -133,7 +133,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.probe:
-        return probe(args.probe, dev)
+        probe(args.probe, dev)
+        if args.copy_probe_mib:
+            copy_probe(args.copy_probe_mib, dev)
+        return
     if args.workload == "llada_b32":
         out = bench_layers(args, dev)
         torch.cuda.synchronize()
@@ -146,14 +149,7 @@ def main():
     else:
         out = bench_single(args, dev, args.workload, detail=not args.no_extras)
     if args.copy_probe_mib:
-        # optional plain copy (calibrates the HBM byte counters)
-        n = args.copy_probe_mib << 20
-        a = torch.empty(n, dtype=torch.uint8, device=dev)
-        b_ = torch.empty_like(a)
-        for _ in range(3):
-            b_.copy_(a)
-        torch.cuda.synchronize()
-        del a, b_
+        copy_probe(args.copy_probe_mib, dev)
     if not args.no_decode and not args.no_graph and not args.no_extras:
         out["decode_side"] = bench_decode(args, dev)
     if not args.no_cpu_baseline:
@@ -596,6 +592,19 @@ def bench_single(args, dev, name, detail=False):
                                   "tokens_per_s": R / (lms * 1e-3), "vs_bf16_cache": step_ms / lms}
         del K8, V8, run8
     return out
+
+
+def copy_probe(mib, dev):
+    """A plain device copy of `mib` MiB, three times: what the HBM byte
+    counters read for known bytes (their calibration)."""
+    import torch
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b_ = torch.empty_like(a)
+    for _ in range(3):
+        b_.copy_(a)
+    torch.cuda.synchronize()
+    eprint(f"[probe] device copy of {mib} MiB, 3 times")
 
 
 def probe(what, dev, launches=3):
