@@ -615,7 +615,7 @@ __global__ __launch_bounds__(256, 1) void qkv_stream2_kernel(QkvArgs a, int n_pa
     constexpr int kStageBytes = C::kStageBytes;
     static_assert(NS >= 2 && (NS - 1) * kInst < 64, "ring depth / wait count");
     static_assert(C::kSmem <= kStream2Lds, "LDS budget");
-    static_assert(kStageBytes >= (kMaxSeqPaged + 1) * 4, "cu_q fits a ring slot");
+    static_assert(kStageBytes >= (kMaxSeqPaged + 1 + kStreamMaxRows) * 4, "cu_q and positions fit a ring slot");
     constexpr int kPieces = kPP / 8;                       // 8-pair output pieces per row
     constexpr int kItems = (kStreamMaxRows * kPieces + 255) / 256;   // epilogue items per thread
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::kSmem];
@@ -628,17 +628,18 @@ __global__ __launch_bounds__(256, 1) void qkv_stream2_kernel(QkvArgs a, int n_pa
 
     // epilogue items (row, 8-pair piece) of this thread: idx = tid + 256 k;
     // their positions and slots are first used after the ring has drained.
-    // Paged mode: the rows' logical positions and cu_q are loaded here, ahead
-    // of every copy; the slot lookups follow once the ring is running.
+    // Paged mode: cu_q and the rows' logical positions are copied straight
+    // into the ring's last slot (which no copy fills before the first barrier
+    // of the main loop), ahead of every other copy; the slot lookups follow
+    // once the ring is running.
     int it_pos[kItems], it_slot[kItems], it_log[kItems];
-    int cuq[kMaxSeqPaged / 256 + 1];
 #pragma unroll
     for (int k = 0; k < kItems; ++k) {
         const int idx = tid + 256 * k;
         const int r = min(idx / kPieces, a.R - 1);
+        it_log[k] = 0;
         if constexpr (PAGED) {
             it_pos[k] = a.pos[r];
-            it_log[k] = load_untracked(a.logical + r);
         } else if (!a.raw_out) {
             it_pos[k] = a.pos[r];
             it_slot[k] = a.slot[r];
@@ -647,19 +648,28 @@ __global__ __launch_bounds__(256, 1) void qkv_stream2_kernel(QkvArgs a, int n_pa
             it_slot[k] = -1;
         }
     }
+    // [0, kMaxSeqPaged] cu_q, then [kMaxSeqPaged + 1, + kStreamMaxRows) logical positions
+    constexpr int kMetaCopies = (kMaxSeqPaged + 1 + kStreamMaxRows + 255) / 256;   // 4-byte copies per wave
+    const uint32_t meta0 = lds_addr(smem + (NS - 1) * kStageBytes);
     if constexpr (PAGED) {
 #pragma unroll
-        for (int i = 0; i <= kMaxSeqPaged / 256; ++i) cuq[i] = load_untracked(a.cu_q + min(tid + 256 * i, a.n_seq));
+        for (int i = 0; i < kMetaCopies; ++i) {
+            const int e = 256 * i + 64 * wave + lane;
+            const int32_t* src = e <= kMaxSeqPaged ? a.cu_q + min(e, a.n_seq)
+                                                   : a.logical + min(e - (kMaxSeqPaged + 1), a.R - 1);
+            copy4_to_lds(src, __builtin_amdgcn_readfirstlane(meta0 + (uint32_t)(256 * i + 64 * wave) * 4));
+        }
     }
 
-    // copy sources: copy i of this wave covers staged rows 4 (wave kInst + i) ..
-    // +3, lane -> row + lane / 16 and the 16-byte slot lane % 16 of its place;
-    // the logical slot stored there is XOR-swizzled by the row, so the 16 rows
-    // a fragment read touches sit in 16 distinct bank groups
+    // copy sources: copy i of this wave covers staged rows 4 (4 i + wave) ..
+    // +3 (so copy i of the four waves is one 16-row tile: x for i < MT, W
+    // rows after), lane -> row + lane / 16 and the 16-byte slot lane % 16 of
+    // its place; the logical slot stored there is XOR-swizzled by the row, so
+    // the 16 rows a fragment read touches sit in 16 distinct bank groups
     const uint16_t* src[kInst];
 #pragma unroll
     for (int i = 0; i < kInst; ++i) {
-        const int r = 4 * (wave * kInst + i) + (lane >> 4);
+        const int r = 4 * (4 * i + wave) + (lane >> 4);
         const int ls = (lane & 15) ^ (r & 15);
         const uint16_t* row_ptr;
         if (r < MT * 16) {
@@ -681,31 +691,25 @@ __global__ __launch_bounds__(256, 1) void qkv_stream2_kernel(QkvArgs a, int n_pa
     auto issue = [&](int slot, int j) __attribute__((always_inline)) {
         int c = min(j, n_st - 1) + k_off;                  // past the end: re-read the last stage
         c -= c >= n_st ? n_st : 0;
-        const uint32_t base = __builtin_amdgcn_readfirstlane(ring0 + slot * kStageBytes + wave * kInst * 1024);
+        const uint32_t base = __builtin_amdgcn_readfirstlane(ring0 + slot * kStageBytes + wave * 1024);
 #pragma unroll
         for (int i = 0; i < kInst; ++i) {
             // W rows are read once: non-temporal, so they do not push x (which
-            // every workgroup re-reads) out of L2
-            if (4 * (wave * kInst + i) >= MT * 16) copy16_to_lds_nt(src[i] + c * KC, base + i * 1024);
-            else copy16_to_lds(src[i] + c * KC, base + i * 1024);
+            // every workgroup re-reads) out of L2 (the choice is per copy index,
+            // the same for every wave: no branch)
+            if (i >= MT) copy16_to_lds_nt(src[i] + c * KC, base + i * 4096);
+            else copy16_to_lds(src[i] + c * KC, base + i * 4096);
         }
     };
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s) issue(s, s);
 
     if constexpr (PAGED) {
-        // sequence of each item row from cu_q (staged in the ring's last slot,
-        // which the first copy into it follows a barrier), then its page entry
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 1) * kInst, 15));   // the metadata, not the copies
-#pragma unroll
-        for (int i = 0; i <= kMaxSeqPaged / 256; ++i) cuq[i] = fence_value(cuq[i]);
-#pragma unroll
-        for (int k = 0; k < kItems; ++k) it_log[k] = fence_value(it_log[k]);
-        int* s_cuq = reinterpret_cast<int*>(smem + (NS - 1) * kStageBytes);
-#pragma unroll
-        for (int i = 0; i <= kMaxSeqPaged / 256; ++i)
-            if (tid + 256 * i <= a.n_seq) s_cuq[tid + 256 * i] = cuq[i];
-        lds_sync();
+        // sequence of each item row from cu_q, then its page entry
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 1) * kInst, 15));   // the metadata, not the stages
+        lds_sync();                                        // every wave's metadata copies
+        const int* s_cuq = reinterpret_cast<const int*>(smem + (NS - 1) * kStageBytes);
+        const int* s_log = s_cuq + kMaxSeqPaged + 1;
 #pragma unroll
         for (int k = 0; k < kItems; ++k) {
             const int r = min((tid + 256 * k) / kPieces, a.R - 1);
@@ -714,7 +718,8 @@ __global__ __launch_bounds__(256, 1) void qkv_stream2_kernel(QkvArgs a, int n_pa
                 const int mid = (lo + hi + 1) >> 1;
                 if (s_cuq[mid] <= r) lo = mid; else hi = mid - 1;
             }
-            const int l = it_log[k];
+            const int l = s_log[r];
+            it_log[k] = l;
             const bool in_seq = r >= s_cuq[lo] && r < s_cuq[lo + 1];
             const int j = l >= 0 ? l / a.page_size : -1;
             const bool ok = in_seq && j >= 0 && j < a.max_pages;
