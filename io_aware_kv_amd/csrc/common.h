@@ -111,18 +111,13 @@ __device__ __forceinline__ void copy4_to_lds(const void* gptr, uint32_t base) {
                  :: "v"(gptr), "s"(base) : "memory", "m0");
 }
 
-// A 4-byte load the compiler does not track (so it adds no wait for it, and
+// A 16-byte load the compiler does not track (so it adds no wait for it, and
 // counts none of it in the waits it adds): the caller waits with an explicit
 // s_waitcnt and then passes the value through fence_value() before using it.
 // Nothing stops the register allocator from copying the destination before
-// the wait, so a value that stays live across a loop is safer loaded with an
-// ordinary load (a copy of that kind once staged stale attention codes); the
-// remaining uses were checked in the generated assembly.
-__device__ __forceinline__ int load_untracked(const int32_t* p) {
-    int v;
-    asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p) : "memory");
-    return v;
-}
+// that wait; a build-time walk over the generated assembly checks, on every
+// control-flow path, that no instruction touches the destination registers
+// before a wait that covers the load.
 __device__ __forceinline__ u32x4 load_untracked_x4(const void* p) {
     u32x4 v;
     asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
@@ -130,10 +125,6 @@ __device__ __forceinline__ u32x4 load_untracked_x4(const void* p) {
 }
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // Keeps later uses of v from being scheduled above the preceding wait.
-__device__ __forceinline__ int fence_value(int v) {
-    asm volatile("" : "+v"(v));
-    return v;
-}
 __device__ __forceinline__ u32x4 fence_value(u32x4 v) {
     asm volatile("" : "+v"(v));
     return v;

@@ -365,8 +365,9 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     // slower on full refreshes.)  Split launches (few sequences, latency-bound)
     // keep the default policy: measured 0.4 us faster at batch 1.
     const bool kv_once = si.nqt == 1 && a.splits == 1;
-    auto issue_p = [&](auto NTC, int sl, int t) __attribute__((always_inline)) {
+    auto issue_p = [&](auto NTC, auto FULLC, int sl, int t) __attribute__((always_inline)) {
         constexpr bool kNt = decltype(NTC)::value != 0;
+        constexpr bool kFullPath = decltype(FULLC)::value != 0;
         auto copy_kv = [&](const uint16_t* src, uint32_t dst) __attribute__((always_inline)) {
             if constexpr (kNt) copy16_to_lds_nt(src, dst);
             else copy16_to_lds(src, dst);
@@ -378,7 +379,7 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
         const uint32_t dst = lds_addr(is_v ? v_tile(sl) : k_tile(sl));
         // (the masked and E4M3 kernels keep only the general path: their
         // register budget has no room for both)
-        if (!HAS_MASK && !KV8 && t < t_end && (__builtin_amdgcn_readfirstlane(s_tile_full[t]) & 16)) {
+        if (kFullPath && !HAS_MASK && !KV8 && t < t_end && (__builtin_amdgcn_readfirstlane(s_tile_full[t]) & 16)) {
             // every key valid: a wave's copies touch two pages (wave-uniform), so
             // a copy's source is a page base plus a fixed 32-bit lane offset
             const int p0 = __builtin_amdgcn_readfirstlane(s_pages[t * 4 + 2 * (wave & 1)]);
@@ -423,8 +424,14 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
         }
     };
     auto issue = [&](int sl, int t) __attribute__((always_inline)) {
-        if (kv_once) issue_p(Ic<1>{}, sl, t);
-        else issue_p(Ic<0>{}, sl, t);
+        if (kv_once) issue_p(Ic<1>{}, Ic<1>{}, sl, t);
+        else issue_p(Ic<0>{}, Ic<1>{}, sl, t);
+    };
+    // the ring's first fill: one straight-line form (the general path, cached
+    // copies) so that every path through it issues the same copies, which the
+    // query fragments' wait counts; the streaming hint is lost on these NS tiles
+    auto issue_first = [&](int sl, int t) __attribute__((always_inline)) {
+        issue_p(Ic<0>{}, Ic<0>{}, sl, t);
     };
 
     // KV8: decode the codes loaded by issue() (their wait is the caller's) into
@@ -457,14 +464,19 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
             qraw[rt][ks] = load_untracked_x4(a.q + (int64_t)qrow * a.n_out + h * kHD + ks * 32 + g * 8);
     }
     const int n_main = t_end - t_begin;
-    const int n_pro = KV8 ? min(1, n_main) : min(NS, n_main);   // the ring's first fill: real tiles only
-    for (int s = 0; s < NS; ++s)
-        if (s < n_pro) issue(s, t_begin + s);
     if constexpr (KV8) {
+        // tile 0 always (an item without tiles loads rows it would read, and
+        // never reads the stage back), so the wait is unconditional
+        issue_first(0, t_begin);
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));   // the query fragments and tile 0's codes
-        if (n_pro > 0) commit8(0);
+        commit8(0);
     } else {
-        wait_stages<NS, kPerStage>(n_pro);               // the query fragments (older than every copy)
+        // the whole ring, always (a stage past the item's last tile copies rows
+        // it reads anyway and is never read back), so one constant wait covers
+        // the query fragments: they are older than every copy
+#pragma unroll
+        for (int s = 0; s < NS; ++s) issue_first(s, t_begin + s);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(NS * kPerStage, 15));
     }
     bf16x8 qf[RT][4];
 #pragma unroll
@@ -659,7 +671,8 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
         }
     } else {
         for (int i = 0; i < n_main; ++i) {
-            const int issued = min(n_main, NS + max(i - 1, 0));   // tiles issued before this step
+            // stages issued before this step: the prologue's NS, then one per step
+            const int issued = NS + max(0, min(n_main - NS, i - 1));
             wait_stages<NS, kPerStage>(issued - 1 - i);            // ... younger than tile i
             lds_sync();
             __builtin_amdgcn_sched_barrier(0);
