@@ -221,7 +221,12 @@ int dllm_cache_write(dllm_dtype dt, int n_rows, int n_heads, int head_dim, const
  *              (0-based within sequence b) sees key j iff bit j%32 of word
  *              mask_off[b] + i*ceil(kv_len[b]/32) + j/32 is 1; mask_off int64[B]
  *   mass_count int32[B] or NULL    the first mass_count[b] (<= max_mass_rows <= 128)
- *              rows of sequence b are the masked-window rows of formula (2)
+ *              rows of sequence b are the masked-window rows of formula (2):
+ *              the caller orders each sequence's rows with its window rows
+ *              first (the order is otherwise free; the rows after them do not
+ *              enter the score).  A count outside 0..min(max_mass_rows, rows
+ *              of b) is taken as the nearest end of that range; a sequence
+ *              with no score rows forms no term
  *   mass_accum float[B*H*n_cap]    per-head running score: for each head h,
  *              mass_accum[(b*H + h)*n_cap + i] += (1/(H*m_b)) * sum over the
  *              window rows of head h's probability of key i (m_b =
