@@ -118,11 +118,19 @@ __device__ __forceinline__ SeqInfo seq_info(const AttnArgs& a, int b) {
 // gfx950 lane swaps: a swap of a value with itself leaves each lane holding its
 // own value in one result and its partner's in the other, so combining the
 // two results reduces without selecting (and without an LDS round trip).
+// A plain v_max_f32: fmaxf on values the compiler cannot prove canonical
+// (a lane swap's results) first quiets each operand with an extra maximum;
+// the scores are never NaN, so that step is dropped.
+__device__ __forceinline__ float max_raw(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
 __device__ __forceinline__ float wave_max16(float v) {
     auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+    v = max_raw(__uint_as_float(t[0]), __uint_as_float(t[1]));
     t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+    return max_raw(__uint_as_float(t[0]), __uint_as_float(t[1]));
 }
 __device__ __forceinline__ float wave_sum16(float v) {
     auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -516,16 +524,32 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
         }
     };
 
+    // Row sums of the probabilities come from the matrix cores: a tile of
+    // ones in place of V^T gives, in every element of a lane's accumulator,
+    // the sum over the tile's keys of that lane's query row (of the bf16
+    // probabilities the P.V product uses, so numerator and denominator see
+    // the same values); two more MFMAs per row tile replace 16 adds per lane.
+    // The masked kernel keeps the adds (its visibility code needs the
+    // registers): each lane sums its own keys, the lane groups meet at the end.
+    constexpr bool kMfmaSum = !HAS_MASK;
     float m_run[RT], l_run[RT];
-    f32x4 acc[RT][8];
+    f32x4 acc[RT][8], acc_l[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         m_run[rt] = kNegBig;
-        l_run[rt] = 0.f;
+        acc_l[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) acc[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 
+    // Every row tile of the wave is computed, also one past the item's last
+    // row (its rows repeat the last query row and are never stored): the loop
+    // is straight-line code with no per-row-tile tests, which the compiler
+    // schedules far better; the extra tiles occur only in an item's last
+    // query tile and run on other SIMDs in parallel.  The masked kernels keep
+    // the tests (their visibility code needs the registers).
+    constexpr bool kSkipIdle = HAS_MASK;
     // S^T for the active row tiles (K fragments shared across them)
     auto scores = [&](const uint16_t* kt_lds, f32x4 (&st)[RT][4]) __attribute__((always_inline)) {
 #pragma unroll
@@ -538,7 +562,7 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
                 st[rt][t4] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (!rt_active[rt]) continue;             // uniform per wave
+                if (kSkipIdle && !rt_active[rt]) continue;   // uniform per wave
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks)
                     st[rt][t4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[rt][ks], st[rt][t4], 0, 0, 0);
@@ -553,9 +577,13 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
         bf16x8 pf[RT][2];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            if (!rt_active[rt]) continue;
+            if (kSkipIdle && !rt_active[rt]) continue;
             // raw scores; the scale is folded into the exponent (c > 0 keeps the order)
             if (!full) {
+                // a side effect the compiler may not speculate: keeps this a
+                // branch (flattened into selects it costs every full tile ~100
+                // vector instructions)
+                asm volatile("");
                 uint32_t w0, w1;
                 mask_pair(sl, wrow + rt * 16 + ln, t, w0, w1);
                 const uint32_t vis = vis_bits(t, row_ok[rt], w0, w1);
@@ -579,22 +607,23 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
             const float mt = mx * a.scale_log2;
             const bool grow = mt > m_run[rt] + kRescaleSlack;
             const float m_new = grow ? mt : m_run[rt];
-            float rs = 0.f;
+            float rs = 0.f;                               // the masked kernel's per-lane row sum
 #pragma unroll
             for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float p = __builtin_amdgcn_exp2f(fmaf(st[rt][t4][e], a.scale_log2, -m_new));
                     st[rt][t4][e] = p;
-                    rs += p;
+                    if constexpr (!kMfmaSum) rs += p;
                 }
             if (grow) {                                   // the reference moved: rescale that row
                 const float alpha = __builtin_amdgcn_exp2f(m_run[rt] - m_new);
-                l_run[rt] *= alpha;
+                if constexpr (kMfmaSum) acc_l[rt] *= alpha;
+                else acc_l[rt][0] *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < 8; ++dt) acc[rt][dt] *= alpha;
             }
-            l_run[rt] += rs;
+            if constexpr (!kMfmaSum) acc_l[rt][0] += rs;  // after the rescale: p is relative to m_new
             m_run[rt] = m_new;
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
@@ -642,10 +671,12 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
             }
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-                if (!rt_active[rt]) continue;
+                if (kSkipIdle && !rt_active[rt]) continue;
 #pragma unroll
                 for (int dt = 0; dt < 8; ++dt)
                     acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf[rt][c], acc[rt][dt], 0, 0, 0);
+                if constexpr (kMfmaSum)
+                    acc_l[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[rt][c], acc_l[rt], 0, 0, 0);
             }
         }
     };
@@ -656,37 +687,38 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     // A step waits until its own tile has landed (the stages issued after it
     // may stay in flight), then an LDS-only barrier publishes it
     // (__syncthreads would also wait for the younger stages).
-    if constexpr (KV8) {
-        // tile i's codes were loaded in step i - 1; its stage was last read in step i - 2
-        for (int i = 0; i < n_main; ++i) {
-            if (i > 0) {
-                __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
-                commit8(i % NS);
+    {
+        if constexpr (KV8) {
+            // tile i's codes were loaded in step i - 1; its stage was last read in step i - 2
+            for (int i = 0; i < n_main; ++i) {
+                if (i > 0) {
+                    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+                    commit8(i % NS);
+                }
+                lds_sync();
+                __builtin_amdgcn_sched_barrier(0);
+                if (i + 1 < n_main) issue((i + 1) % NS, t_begin + i + 1);
+                __builtin_amdgcn_sched_barrier(0);
+                attend(i % NS, t_begin + i);
             }
-            lds_sync();
-            __builtin_amdgcn_sched_barrier(0);
-            if (i + 1 < n_main) issue((i + 1) % NS, t_begin + i + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            attend(i % NS, t_begin + i);
-        }
-    } else {
-        for (int i = 0; i < n_main; ++i) {
-            // stages issued before this step: the prologue's NS, then one per step
-            const int issued = NS + max(0, min(n_main - NS, i - 1));
-            wait_stages<NS, kPerStage>(issued - 1 - i);            // ... younger than tile i
-            lds_sync();
-            __builtin_amdgcn_sched_barrier(0);
-            if (i > 0 && i - 1 + NS < n_main) issue((i - 1) % NS, t_begin + i - 1 + NS);
-            __builtin_amdgcn_sched_barrier(0);
-            attend(i % NS, t_begin + i);
+        } else {
+            for (int i = 0; i < n_main; ++i) {
+                // stages issued before this step: the prologue's NS, then one per step
+                const int issued = NS + max(0, min(n_main - NS, i - 1));
+                wait_stages<NS, kPerStage>(issued - 1 - i);            // ... younger than tile i
+                lds_sync();
+                __builtin_amdgcn_sched_barrier(0);
+                if (i > 0 && i - 1 + NS < n_main) issue((i - 1) % NS, t_begin + i - 1 + NS);
+                __builtin_amdgcn_sched_barrier(0);
+                attend(i % NS, t_begin + i);
+            }
         }
     }
     __syncthreads();                                    // every copy has been waited for above
-    // Each lane's running sum covers its own keys of the row (the four lane
-    // groups hold disjoint keys; one exponent reference per row, so one rescale
-    // serves all four): the row sums meet once, here, not every tile.
+    // the MFMA row sums already cover every key of the row (all four lane
+    // groups); the per-lane sums of the masked kernel meet here
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) l_run[rt] = wave_sum16(l_run[rt]);
+    for (int rt = 0; rt < RT; ++rt) l_run[rt] = kMfmaSum ? acc_l[rt][0] : wave_sum16(acc_l[rt][0]);
 
     // LDS after the main pass (the ring is free): final log-sum-exp (base 2) of
     // the tile's rows, then the score pass's factors
