@@ -333,6 +333,21 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     __syncthreads();
 
     const int last_page = max(npages - 1, 0);
+    // Items whose key tiles are all full (every key valid, no mask) and number
+    // at most 64 take their copy bases from registers: lane 2j + e of vpg<k>
+    // holds page 4(t_begin + 32k + j) + 2(wave & 1) + e, the page of half e of
+    // this wave's keys in the item's tile 32k + j, read once here; then no
+    // step of the main pass waits on an LDS read of a page entry or a tile
+    // flag (those round trips cost 6% of a full-refresh launch).
+    // (two named registers, not an array: a select between array elements
+    // became an indexed scratch array that the compiler placed in LDS)
+    bool fast = !HAS_MASK && !KV8 && t_end - t_begin <= 64;
+    auto page_lane = [&](int k) __attribute__((always_inline)) {
+        const int t = t_begin + 32 * k + (lane >> 1);
+        fast &= __builtin_amdgcn_ballot_w64(t < t_end && !(s_tile_full[min(t, kMaxPages / 4 - 1)] & 16)) == 0;
+        return s_pages[min(4 * t + 2 * (wave & 1) + (lane & 1), kMaxPages - 1)];
+    };
+    const int vpg0 = page_lane(0), vpg1 = page_lane(1);
     // keys past kv_len or on a bad page read the sequence's key 0 (a row the
     // item reads anyway); the visibility bits zero them
     const int key0_page = npages > 0 ? s_pages[0] : -1;
@@ -387,11 +402,21 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
         const uint32_t dst = lds_addr(is_v ? v_tile(sl) : k_tile(sl));
         // (the masked and E4M3 kernels keep only the general path: their
         // register budget has no room for both)
-        if (kFullPath && !HAS_MASK && !KV8 && t < t_end && (__builtin_amdgcn_readfirstlane(s_tile_full[t]) & 16)) {
+        if (kFullPath && !HAS_MASK && !KV8 && t < t_end &&
+            (fast || (__builtin_amdgcn_readfirstlane(s_tile_full[t]) & 16))) {
             // every key valid: a wave's copies touch two pages (wave-uniform), so
             // a copy's source is a page base plus a fixed 32-bit lane offset
-            const int p0 = __builtin_amdgcn_readfirstlane(s_pages[t * 4 + 2 * (wave & 1)]);
-            const int p1 = __builtin_amdgcn_readfirstlane(s_pages[t * 4 + 2 * (wave & 1) + 1]);
+            int p0, p1;
+            if (fast) {
+                const int j = t - t_begin, l0 = 2 * (j & 31);
+                const int a0 = __builtin_amdgcn_readlane(vpg0, l0), a1 = __builtin_amdgcn_readlane(vpg0, l0 + 1);
+                const int c0 = __builtin_amdgcn_readlane(vpg1, l0), c1 = __builtin_amdgcn_readlane(vpg1, l0 + 1);
+                p0 = (j & 32) ? c0 : a0;
+                p1 = (j & 32) ? c1 : a1;
+            } else {
+                p0 = __builtin_amdgcn_readfirstlane(s_pages[t * 4 + 2 * (wave & 1)]);
+                p1 = __builtin_amdgcn_readfirstlane(s_pages[t * 4 + 2 * (wave & 1) + 1]);
+            }
             const int64_t b0 = (int64_t)p0 * 16 * a.n_out, b1 = (int64_t)p1 * 16 * a.n_out;
 #pragma unroll
             for (int i = 0; i < kDmaPerWave; ++i) {
@@ -573,17 +598,19 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     auto attend = [&](int sl, int t) __attribute__((always_inline)) {
         f32x4 st[RT][4];
         scores(k_tile(sl), st);
-        const bool full = !HAS_MASK && (s_tile_full[t] & 16);
-        bf16x8 pf[RT][2];
+        bool full = !HAS_MASK;
+        if (!HAS_MASK && !fast) full = (s_tile_full[t] & 16) != 0;
+        // raw scores; the scale is folded into the exponent (c > 0 keeps the order).
+        // Keys a row may not see get -inf: one branch for every row tile, with
+        // a side effect the compiler may not speculate, so that a full tile
+        // runs none of it (flattened into selects, or with its key indices
+        // hoisted above the branch, it cost every full tile up to ~100 vector
+        // instructions)
+        if (!full) {
+            asm volatile("");
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            if (kSkipIdle && !rt_active[rt]) continue;
-            // raw scores; the scale is folded into the exponent (c > 0 keeps the order)
-            if (!full) {
-                // a side effect the compiler may not speculate: keeps this a
-                // branch (flattened into selects it costs every full tile ~100
-                // vector instructions)
-                asm volatile("");
+            for (int rt = 0; rt < RT; ++rt) {
+                if (kSkipIdle && !rt_active[rt]) continue;
                 uint32_t w0, w1;
                 mask_pair(sl, wrow + rt * 16 + ln, t, w0, w1);
                 const uint32_t vis = vis_bits(t, row_ok[rt], w0, w1);
@@ -593,6 +620,11 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
                     for (int e = 0; e < 4; ++e)
                         st[rt][t4][e] = ((vis >> (t4 * 4 + e)) & 1u) ? st[rt][t4][e] : -INFINITY;
             }
+        }
+        bf16x8 pf[RT][2];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            if (kSkipIdle && !rt_active[rt]) continue;
             float mx = -INFINITY;
 #pragma unroll
             for (int t4 = 0; t4 < 4; ++t4)
