@@ -501,3 +501,41 @@ def decode_logits_device(seed: int, rows: DecodeRows, vocab: int, device):
         t[twi, torch.from_numpy(rows.twin_tok[tw].astype(np.int64)).to(device)] = \
             torch.from_numpy(rows.peak_val[tw]).to(device).to(torch.bfloat16)
     return t
+
+
+# ---------------------------------------------------------------------------
+# Long contexts for the attention alone: sequences whose keys span more key
+# tiles than the workloads above (up to the bf16 kernel's 16384-key page
+# table), on a shuffled page pool, with seeded q and cache contents.
+# ---------------------------------------------------------------------------
+
+@dataclass
+class LongContext:
+    kv: np.ndarray            # keys per sequence
+    rows: np.ndarray          # query rows per sequence
+    mass_count: np.ndarray    # score rows per sequence (the first rows)
+    seq_pages: np.ndarray     # pages per sequence (ceil(kv / 16))
+    pool_pages: int
+    pool_perm: np.ndarray     # the pool's page order (sequence b takes the next seq_pages[b])
+    max_pages: int
+    seed: int
+
+
+def long_context(kv, rows, mass_count, seed: int) -> LongContext:
+    kv = np.asarray(kv, dtype=np.int32)
+    seq_pages = (kv + PAGE - 1) // PAGE
+    pool = int(seq_pages.sum()) + 8                  # a few spare pages
+    perm = np.random.default_rng([7300, seed]).permutation(pool).astype(np.int32)
+    return LongContext(kv=kv, rows=np.asarray(rows, dtype=np.int32),
+                       mass_count=np.asarray(mass_count, dtype=np.int32), seq_pages=seq_pages,
+                       pool_pages=pool, pool_perm=perm, max_pages=int(seq_pages.max()), seed=seed)
+
+
+def long_context_tensors(lc: LongContext, n_out: int, device):
+    """q [sum(rows), n_out] and the K, V caches [pool_pages * 16, n_out],
+    N(0, 1) in bf16."""
+    R = int(lc.rows.sum())
+    base = (7400 + lc.seed) * 16
+    return (device_normal_bf16((R, n_out), 1.0, base, device),
+            device_normal_bf16((lc.pool_pages * PAGE, n_out), 1.0, base + 1, device),
+            device_normal_bf16((lc.pool_pages * PAGE, n_out), 1.0, base + 2, device))
