@@ -152,6 +152,8 @@ def main():
         copy_probe(args.copy_probe_mib, dev)
     if not args.no_decode and not args.no_graph and not args.no_extras:
         out["decode_side"] = bench_decode(args, dev)
+    if not args.no_extras:
+        out["achievable"] = achievable_probes(dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = (cpu_baseline_b32() if args.workload == "llada_b32"
                                else cpu_baseline(args.workload, args.cpu_seconds))
@@ -592,6 +594,51 @@ def bench_single(args, dev, name, detail=False):
                                   "tokens_per_s": R / (lms * 1e-3), "vs_bf16_cache": step_ms / lms}
         del K8, V8, run8
     return out
+
+
+def achievable_probes(dev):
+    """What this machine reaches on the two resources the roofline prices,
+    measured beside the line (context for its fractions, not part of the
+    path): a plain 1 GiB device copy (HBM read + write bytes per second), and
+    torch's bf16 GEMM (hipBLASLt) on the full-refresh projection's shape,
+    65536 x 4096 @ 4096 x 12288 (no rotary, no cache write)."""
+    import torch
+    res = {}
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    b_ = torch.empty_like(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(2):
+        b_.copy_(a)
+    e0.record()
+    for _ in range(5):
+        b_.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    res["device_copy_GBs"] = 2 * (1 << 30) * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b_
+    x = torch.randn(65536, 4096, device=dev).to(torch.bfloat16)
+    w = torch.randn(12288, 4096, device=dev).mul_(4096 ** -0.5).to(torch.bfloat16)
+    wt = w.t().contiguous()
+    y = torch.empty(65536, 12288, dtype=torch.bfloat16, device=dev)
+    best = None
+    # W as stored (out x in: the Linear layer's 2-D product) and W^T laid out (a plain 2-D product)
+    for gemm in (lambda: torch.nn.functional.linear(x, w), lambda: torch.matmul(x, wt, out=y)):
+        for _ in range(2):
+            gemm()
+        e0.record()
+        for _ in range(5):
+            gemm()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        best = ms if best is None else min(best, ms)
+    res["library_gemm_TFLOPs"] = 2 * 65536 * 4096 * 12288 / (best * 1e-3) / 1e12
+    res["library_gemm_frac"] = res["library_gemm_TFLOPs"] / 2500.0
+    res["note"] = ("torch's plain bf16 GEMM and device copy on this GPU, for context; the path's own kernels "
+                   "are measured above")
+    del x, w, wt, y
+    torch.cuda.empty_cache()
+    return res
 
 
 def copy_probe(mib, dev):
