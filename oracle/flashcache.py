@@ -191,7 +191,7 @@ def attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, page_tabl
             if vis is not None:
                 s = np.where(vis, s, -np.inf)
             seen = np.isfinite(s).any(axis=1)              # rows with a visible key
-            top = np.where(seen, np.max(np.where(np.isfinite(s), s, -np.inf), axis=1), 0.0)
+            top = np.where(seen, np.max(np.where(np.isfinite(s), s, -np.inf), axis=1, initial=-np.inf), 0.0)
             e = np.where(np.isfinite(s), np.exp(s - top[:, None]), 0.0)
             tot = e.sum(axis=1)
             pb[h] = np.where(seen[:, None], e / np.where(seen, tot, 1.0)[:, None], 0.0)

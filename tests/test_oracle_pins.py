@@ -263,6 +263,26 @@ def test_attention_zero_query_is_mean_and_dark_row_is_zero():
     assert not o[1].any() and not probs[0][:, 1].any()
 
 
+def test_attention_empty_key_and_row_sets():
+    # a sequence with no keys: each of its rows sees no key (o = 0, no
+    # probabilities); a sequence with no rows contributes nothing; the other
+    # sequences of the batch are unaffected
+    rng = np.random.default_rng(8)
+    H, D = 2, 8
+    table = np.array([[0, -1], [1, 2], [-1, -1]], dtype=np.int32)
+    K = rng.standard_normal((3 * P, H * D))
+    V = rng.standard_normal((3 * P, H * D))
+    q = rng.standard_normal((5, H * D))
+    cu, kv = [0, 0, 3, 5], [16, 20, 0]                     # no rows / three rows / two rows, no keys
+    o, probs = O.attention(q, K, V, table, cu, kv, H, D, P)
+    assert [p.shape for p in probs] == [(H, 0, 16), (H, 3, 20), (H, 2, 0)]
+    assert not o[3:].any()
+    o1, _ = O.attention(q[:3], K, V, table[1:2], [0, 3], [20], H, D, P)
+    assert np.array_equal(o[:3], o1)
+    m = O.column_mass(probs, [0, 3, 0], 20)
+    assert not m[0].any() and not m[2].any() and abs(m[1].sum() - 1.0) < 1e-12
+
+
 def _tiled_online_softmax(q, K, V, tile):
     """Test-local flash-style recurrence: running max, running sum, rescaled
     accumulator, over key tiles.  Must equal the dense oracle."""
