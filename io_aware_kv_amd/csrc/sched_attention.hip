@@ -719,31 +719,29 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     // A step waits until its own tile has landed (the stages issued after it
     // may stay in flight), then an LDS-only barrier publishes it
     // (__syncthreads would also wait for the younger stages).
-    {
-        if constexpr (KV8) {
-            // tile i's codes were loaded in step i - 1; its stage was last read in step i - 2
-            for (int i = 0; i < n_main; ++i) {
-                if (i > 0) {
-                    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
-                    commit8(i % NS);
-                }
-                lds_sync();
-                __builtin_amdgcn_sched_barrier(0);
-                if (i + 1 < n_main) issue((i + 1) % NS, t_begin + i + 1);
-                __builtin_amdgcn_sched_barrier(0);
-                attend(i % NS, t_begin + i);
+    if constexpr (KV8) {
+        // tile i's codes were loaded in step i - 1; its stage was last read in step i - 2
+        for (int i = 0; i < n_main; ++i) {
+            if (i > 0) {
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+                commit8(i % NS);
             }
-        } else {
-            for (int i = 0; i < n_main; ++i) {
-                // stages issued before this step: the prologue's NS, then one per step
-                const int issued = NS + max(0, min(n_main - NS, i - 1));
-                wait_stages<NS, kPerStage>(issued - 1 - i);            // ... younger than tile i
-                lds_sync();
-                __builtin_amdgcn_sched_barrier(0);
-                if (i > 0 && i - 1 + NS < n_main) issue((i - 1) % NS, t_begin + i - 1 + NS);
-                __builtin_amdgcn_sched_barrier(0);
-                attend(i % NS, t_begin + i);
-            }
+            lds_sync();
+            __builtin_amdgcn_sched_barrier(0);
+            if (i + 1 < n_main) issue((i + 1) % NS, t_begin + i + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            attend(i % NS, t_begin + i);
+        }
+    } else {
+        for (int i = 0; i < n_main; ++i) {
+            // stages issued before this step: the prologue's NS, then one per step
+            const int issued = NS + max(0, min(n_main - NS, i - 1));
+            wait_stages<NS, kPerStage>(issued - 1 - i);            // ... younger than tile i
+            lds_sync();
+            __builtin_amdgcn_sched_barrier(0);
+            if (i > 0 && i - 1 + NS < n_main) issue((i - 1) % NS, t_begin + i - 1 + NS);
+            __builtin_amdgcn_sched_barrier(0);
+            attend(i % NS, t_begin + i);
         }
     }
     __syncthreads();                                    // every copy has been waited for above

@@ -1,4 +1,4 @@
-"""Attention over long contexts: sequences whose keys span many more key
+"""Attention over long contexts and degenerate batches: sequences whose keys span many more key
 tiles than the workloads' (4100 keys with a partial last tile, 8704 keys — the
 most a score is formed for — and 16384, the bf16 kernel's page-table limit),
 on a shuffled page pool, through both attention paths (key splits merged by
@@ -35,6 +35,11 @@ def _cols(t, heads):
     ((4100, 8704), (72, 200), (32, 32), "1"),
     ((16384,), (64,), None, None),
     ((16384,), (64,), None, "1"),
+    # degenerate batches: an inactive sequence (no rows, no keys), one not
+    # refreshed this step (keys, no rows), a single key and row, a partial
+    # key tile, two query tiles over a partial key tile
+    ((0, 100, 1, 40, 200), (0, 0, 1, 17, 130), (0, 0, 1, 5, 32), None),
+    ((0, 100, 1, 40, 200), (0, 0, 1, 17, 130), (0, 0, 1, 5, 32), "1"),
 ])
 def test_long_context_attention(kv, rows, mass, splits, gpu):
     import torch
@@ -53,6 +58,7 @@ def test_long_context_attention(kv, rows, mass, splits, gpu):
     with_mass = mass is not None
     n_cap = max_kv
     max_mass = int(lc.mass_count.max()) if with_mass else 0
+    assert R > 0
     o = torch.empty(R, n_out, dtype=torch.bfloat16, device=gpu)
     score = torch.zeros(n_seq, H, n_cap, dtype=torch.float32, device=gpu)
     dllm.set_tuning("attn_splits", splits)
@@ -77,5 +83,7 @@ def test_long_context_attention(kv, rows, mass, splits, gpu):
             want = O.column_mass([pb[j:j + 1] for pb in probs], lc.mass_count, n_cap) / H
             for b in range(n_seq):
                 k = int(lc.kv[b])
+                if lc.mass_count[b] == 0:
+                    continue                              # no score rows: the term is not formed
                 info = close(got[b, h, :k], want[b, :k], *MASS_TOL["bf16"], f"score term head {h} seq {b}")
         log(f"   score terms of heads {HEADS}: last max_abs={info['max_abs']:.3e}")
