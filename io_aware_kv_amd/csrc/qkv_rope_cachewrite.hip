@@ -625,6 +625,15 @@ __global__ __launch_bounds__(256, 1) void qkv_stream2_kernel(QkvArgs a, int n_pa
     const int D = a.head_dim, half = D >> 1, H = a.n_out / D;
     const int p0 = blockIdx.x * kPP;
     const int n_st = a.d_model / KC;
+    // rotation frequency of this thread's pair (threads < kPP), formed before
+    // the main loop so the fp64 pow's latency is hidden behind it (at the end
+    // of the kernel it cost ~1 us of the batch-1 launch); staged to LDS in
+    // the epilogue
+    double theta_own = 0.0;
+    if (tid < kPP) {
+        const int p = min(p0 + tid, n_pairs - 1);
+        theta_own = pow((double)a.rope_base, -2.0 * (p % half) / D);
+    }
 
     // epilogue items (row, 8-pair piece) of this thread: idx = tid + 256 k;
     // their positions and slots are first used after the ring has drained.
@@ -781,12 +790,8 @@ __global__ __launch_bounds__(256, 1) void qkv_stream2_kernel(QkvArgs a, int n_pa
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 Cs[(wave * kRowsPad + m * 16 + g * 4 + e) * kLdc + t * 16 + ln] = acc[m][t][e];
-    // rotation frequency of each pair: one pow per pair, in parallel
     double* s_theta = reinterpret_cast<double*>(Cs + 4 * kRowsPad * kLdc);
-    if (tid < kPP) {
-        const int p = min(p0 + tid, n_pairs - 1);
-        s_theta[tid] = pow((double)a.rope_base, -2.0 * (p % half) / D);
-    }
+    if (tid < kPP) s_theta[tid] = theta_own;
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < kItems; ++k) {
