@@ -283,7 +283,7 @@ struct GemmCfg {
     static_assert(NS >= 2 * KB && NS >= 3, "two iterations of stages in the ring");
     static_assert(OCC == 1 || NS * kStage * 2 + 8 * BM + 512 <= kGemmLdsPair, "two workgroups per compute unit");
     static_assert(!kBig || OCC == 1, "one 256 x 256 workgroup per compute unit");
-    static_assert((NS - KB) * kInst < 64, "wait counts");
+    static_assert((NS - KB) * kInst < 64 && (NS - 1) * kInst < 64, "wait counts");
 };
 
 // Physical 16-byte slot of logical slot 0 in a 64-byte staged row: any 16
@@ -395,20 +395,26 @@ __global__ __launch_bounds__(256, OCC) void qkv_gemm_kernel(QkvArgs a, int n_mti
 #pragma unroll
         for (int t = 0; t < 8; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-        if (s < n_kt)
-#pragma unroll
-            for (int i = 0; i < kInst; ++i) issue_one(s, s, i);
     bf16x8 cx[WMF], cw[8];
     if constexpr (KB == 1) {
-        // one stage per barrier: the copies for stage kt + NS go out during
-        // stage kt, into the buffer stage kt was read from before the barrier
-        auto stage_barrier1 = [&](int next) __attribute__((always_inline)) {
-            wait_stages_ahead<kInst, NS - 2>(min(NS - 2, n_kt - 1 - next));
+        // One stage per barrier: the copies for stage kt + NS go out during
+        // stage kt, into the buffer stage kt was read from before the barrier.
+        // Every iteration (and the prologue) issues one whole stage: past the
+        // last stage, a re-read of the last one into the buffer just freed,
+        // never read.  So each wait is one constant count and no branch
+        // surrounds a copy.
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int i = 0; i < kInst; ++i) issue_one(s, min(s, n_kt - 1), i);
+        // stage `next` has landed; the NS - 2 stages issued after it may
+        // still be in flight; this wave's fragment reads have returned
+        auto stage_barrier1 = [&]() __attribute__((always_inline)) {
+            __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * kInst, 0));
             __builtin_amdgcn_s_barrier();
         };
-        stage_barrier1(0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 1) * kInst, 0));   // stage 0
+        __builtin_amdgcn_s_barrier();
 #pragma unroll
         for (int t = 0; t < 8; ++t) cw[t] = read_w(0, t);
 #pragma unroll
@@ -416,8 +422,8 @@ __global__ __launch_bounds__(256, OCC) void qkv_gemm_kernel(QkvArgs a, int n_mti
         for (int kt = 0; kt < n_kt; ++kt) {
             // After the last stage the reads below are of a stale buffer and go
             // unused: kept unconditional so the fragment registers need no merge.
-            stage_barrier1(kt + 1);
-            const bool more = kt + NS < n_kt;
+            stage_barrier1();                           // stage kt + 1
+            const int kc = min(kt + NS, n_kt - 1);
             bf16x8 nx[WMF], nw[8];
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -427,8 +433,8 @@ __global__ __launch_bounds__(256, OCC) void qkv_gemm_kernel(QkvArgs a, int n_mti
                     acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cw[t], cx[i], acc[i][t], 0, 0, 0);
 #pragma unroll
                 for (int c = 0; c < C::kCopyPerGroup; ++c)
-                    if (more && i * C::kCopyPerGroup + c < kInst)
-                        issue_one(kt % NS, kt + NS, i * C::kCopyPerGroup + c);
+                    if (i * C::kCopyPerGroup + c < kInst)
+                        issue_one(kt % NS, kc, i * C::kCopyPerGroup + c);
                 // the next step's W fragments early (its first group needs all
                 // eight), x fragment i once this group has used its register
 #pragma unroll
@@ -442,7 +448,15 @@ __global__ __launch_bounds__(256, OCC) void qkv_gemm_kernel(QkvArgs a, int n_mti
 #pragma unroll
             for (int t = 0; t < 8; ++t) cw[t] = nw[t];
         }
+        // the re-read copies of the last iterations land before the
+        // epilogue reuses the ring
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
     } else {
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+        if (s < n_kt)
+#pragma unroll
+            for (int i = 0; i < kInst; ++i) issue_one(s, s, i);
     wait_stages_ahead<kInst, NS - KB>(min(NS - KB, n_kt - 1));   // stage 0 (and maybe more) landed
     __builtin_amdgcn_s_barrier();
 #pragma unroll
