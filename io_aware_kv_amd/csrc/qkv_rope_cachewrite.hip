@@ -331,7 +331,8 @@ __global__ __launch_bounds__(256, OCC) void qkv_gemm_kernel(QkvArgs a, int n_mti
     const int local = item % per_group;
     const int mt = first_m + local % gm_sz, nt = local / gm_sz;
     const int row0 = mt * BM, col0 = nt * C::BN;
-    if (tid < a.head_dim / 2) s_theta[tid] = pow((double)a.rope_base, -2.0 * tid / a.head_dim);
+    // rotation frequencies in revolutions per position (theta / 2 pi)
+    if (tid < a.head_dim / 2) s_theta[tid] = pow((double)a.rope_base, -2.0 * tid / a.head_dim) * (1.0 / kTwoPi);
     if (!RAW && tid < BM) {
         const int grow = min(row0 + tid, a.R - 1);
         s_pos[tid] = a.pos[grow];
@@ -508,15 +509,15 @@ __global__ __launch_bounds__(256, OCC) void qkv_gemm_kernel(QkvArgs a, int n_mti
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const double th = s_theta[t * 16 + g * 4 + e];
+                const double fr = s_theta[t * 16 + g * 4 + e];
 #pragma unroll
                 for (int i = 0; i < WMF; ++i) {
-                    double ang = (double)s_pos[wm * WM + i * 16 + ln] * th;
-                    ang -= rint(ang * (1.0 / kTwoPi)) * kTwoPi;
-                    // hardware sin/cos take revolutions; |rev| <= 1/2 after the fp64
-                    // reduction (library sincosf here would push the accumulators
-                    // out of registers)
-                    const float rev = (float)(ang * (1.0 / kTwoPi));
+                    // the angle in revolutions, reduced in fp64 to |rev| <= 1/2;
+                    // hardware sin/cos take revolutions (library sincosf here
+                    // would push the accumulators out of registers)
+                    double rv = (double)s_pos[wm * WM + i * 16 + ln] * fr;
+                    rv -= rint(rv);
+                    const float rev = (float)rv;
                     const float sn = __builtin_amdgcn_sinf(rev), cs = __builtin_amdgcn_cosf(rev);
                     const float x0 = acc[i][t][e], x1 = acc[i][t + 4][e];
                     acc[i][t][e] = x0 * cs - x1 * sn;
@@ -646,7 +647,7 @@ __global__ __launch_bounds__(256, 1) void qkv_stream2_kernel(QkvArgs a, int n_pa
     double theta_own = 0.0;
     if (tid < kPP) {
         const int p = min(p0 + tid, n_pairs - 1);
-        theta_own = pow((double)a.rope_base, -2.0 * (p % half) / D);
+        theta_own = pow((double)a.rope_base, -2.0 * (p % half) / D) * (1.0 / kTwoPi);   // revolutions per position
     }
 
     // epilogue items (row, 8-pair piece) of this thread: idx = tid + 256 k;
@@ -842,10 +843,11 @@ __global__ __launch_bounds__(256, 1) void qkv_stream2_kernel(QkvArgs a, int n_pa
         if (part < 2 && (PAGED || !a.raw_out)) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                double ang = (double)it_pos[k] * s_theta[q * 8 + e];
-                ang -= rint(ang * (1.0 / kTwoPi)) * kTwoPi;
-                // hardware sin/cos take revolutions; |rev| <= 1/2 after the fp64 reduction
-                const float rev = (float)(ang * (1.0 / kTwoPi));
+                // the angle in revolutions, reduced in fp64 to |rev| <= 1/2 (the
+                // hardware sin/cos take revolutions)
+                double rv = (double)it_pos[k] * s_theta[q * 8 + e];
+                rv -= rint(rv);
+                const float rev = (float)rv;
                 const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
                 const float x0 = lo[e], x1 = hi[e];
                 lo[e] = x0 * cs - x1 * sn;
