@@ -401,8 +401,8 @@ __global__ __launch_bounds__(256, OCC) void qkv_gemm_kernel(QkvArgs a, int n_mti
         // One stage per barrier: the copies for stage kt + NS go out during
         // stage kt, into the buffer stage kt was read from before the barrier.
         // Every iteration (and the prologue) issues one whole stage: past the
-        // last stage, a re-read of the last one into the buffer just freed,
-        // never read.  So each wait is one constant count and no branch
+        // last stage, copies of one cached 16-byte line into the buffer just
+        // freed, never read.  So each wait is one constant count and no branch
         // surrounds a copy.
 #pragma unroll
         for (int s = 0; s < NS; ++s)
@@ -424,7 +424,8 @@ __global__ __launch_bounds__(256, OCC) void qkv_gemm_kernel(QkvArgs a, int n_mti
             // After the last stage the reads below are of a stale buffer and go
             // unused: kept unconditional so the fragment registers need no merge.
             stage_barrier1();                           // stage kt + 1
-            const int kc = min(kt + NS, n_kt - 1);
+            const bool more = kt + NS < n_kt;
+            const int kc = more ? kt + NS : 0;
             bf16x8 nx[WMF], nw[8];
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -434,8 +435,14 @@ __global__ __launch_bounds__(256, OCC) void qkv_gemm_kernel(QkvArgs a, int n_mti
                     acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cw[t], cx[i], acc[i][t], 0, 0, 0);
 #pragma unroll
                 for (int c = 0; c < C::kCopyPerGroup; ++c)
-                    if (i * C::kCopyPerGroup + c < kInst)
-                        issue_one(kt % NS, kc, i * C::kCopyPerGroup + c);
+                    if (i * C::kCopyPerGroup + c < kInst) {
+                        const int ci = i * C::kCopyPerGroup + c;
+                        const int j = wave * kInst + ci;
+                        // past the last stage every lane re-reads the operand's
+                        // first 16 bytes (one cached line) into the freed buffer
+                        copy16_to_lds(more ? src[ci] + kc * BK : (const uint16_t*)a.w,
+                                      lds0 + (uint32_t)((kt % NS) * kStage + j * 512) * 2u);
+                    }
                 // the next step's W fragments early (its first group needs all
                 // eight), x fragment i once this group has used its register
 #pragma unroll
