@@ -11,7 +11,9 @@ positions over the whole int32 range (0, 1, 2^16, 2^20 + 7, 2^24 - 1,
 most 128 rows), the GEMM in two tile shapes, the LDS-tiled kernel and the
 fp32 kernel, and compare q and the K/V rows written to their (shuffled) cache
 slots with the oracle's projection and rotation of the same inputs.  Cache
-rows no slot names must stay untouched.
+rows no slot names must stay untouched.  A contraction of 64 (two 32-deep
+stages, fewer than the GEMM's ring holds) runs the GEMM's ring with every
+refill past the last stage.
 """
 import numpy as np
 import pytest
@@ -21,18 +23,20 @@ from parity import TOL, close, log
 
 pytestmark = pytest.mark.gpu
 
-H, D, DM = 4, 128, 512
+H, D = 4, 128
 N_OUT = H * D
 BASE = 5e5
 SPECIAL = (0, 1, 1 << 16, (1 << 20) + 7, (1 << 24) - 1, (1 << 30) + 123, (1 << 31) - 1)
 
 
-@pytest.mark.parametrize("rows,kernel,dt", [(100, None, "bf16"), (300, "gemm", "bf16"), (300, "g64x256", "bf16"),
-                                            (300, "tiled", "bf16"), (77, None, "f32")])
-def test_rope_at_large_positions(rows, kernel, dt, gpu):
+@pytest.mark.parametrize("rows,kernel,dt,DM", [(100, None, "bf16", 512), (300, "gemm", "bf16", 512),
+                                               (300, "g64x256", "bf16", 512), (300, "tiled", "bf16", 512),
+                                               (77, None, "f32", 512), (300, "gemm", "bf16", 64),
+                                               (300, "g128x256o2", "bf16", 64)])
+def test_rope_at_large_positions(rows, kernel, dt, DM, gpu):
     import torch
     from io_aware_kv_amd import dllm
-    log(f"[gpu] rotation at large positions: {rows} rows, {dt}, kernel {kernel or 'planner'}")
+    log(f"[gpu] rotation at large positions: {rows} rows, d_model {DM}, {dt}, kernel {kernel or 'planner'}")
     rng = np.random.default_rng(9100 + rows)
     tdt = torch.bfloat16 if dt == "bf16" else torch.float32
     x = torch.from_numpy(rng.standard_normal((rows, DM)).astype(np.float32)).to(tdt).to(gpu)
