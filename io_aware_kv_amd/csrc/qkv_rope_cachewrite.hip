@@ -438,8 +438,8 @@ __global__ __launch_bounds__(256, OCC) void qkv_gemm_kernel(QkvArgs a, int n_mti
                     if (i * C::kCopyPerGroup + c < kInst) {
                         const int ci = i * C::kCopyPerGroup + c;
                         const int j = wave * kInst + ci;
-                        // past the last stage every lane re-reads the operand's
-                        // first 16 bytes (one cached line) into the freed buffer
+                        // past the last stage every lane reads W's first 16
+                        // bytes (one cached line) into the freed buffer
                         copy16_to_lds(more ? src[ci] + kc * BK : (const uint16_t*)a.w,
                                       lds0 + (uint32_t)((kt % NS) * kStage + j * 512) * 2u);
                     }
@@ -456,8 +456,8 @@ __global__ __launch_bounds__(256, OCC) void qkv_gemm_kernel(QkvArgs a, int n_mti
 #pragma unroll
             for (int t = 0; t < 8; ++t) cw[t] = nw[t];
         }
-        // the re-read copies of the last iterations land before the
-        // epilogue reuses the ring
+        // the copies of the last iterations land before the epilogue reuses
+        // the ring
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
     } else {
 #pragma unroll
