@@ -11,7 +11,9 @@ partial page), and o and the score terms of three heads are compared with the
 oracle run on the same table with those keys marked invisible (the oracle
 reads any real row for them, which the zero probability then drops), on both
 attention paths (keys split and merged by the second launch, and the single
-launch that keeps the window rows' probabilities).
+launch that keeps the window rows' probabilities), with bf16 caches and with
+one-byte E4M3 caches (seeded codes of moderate magnitude; the oracle reads
+their decoded values).
 """
 import numpy as np
 import pytest
@@ -32,15 +34,25 @@ def _cols(t, heads):
     return t.index_select(1, idx).to(torch.float64).cpu().numpy()
 
 
-@pytest.mark.parametrize("splits", [None, "1", "3"])
-def test_out_of_range_pages_hide_their_keys(splits, gpu):
+def _codes(shape, salt):
+    """Seeded E4M3 codes with exponent fields 4..8 (magnitudes 1/8 .. 3.75) and random signs."""
+    r = np.random.default_rng(9500 + salt)
+    mag = r.integers(0x20, 0x48, size=shape)
+    return (mag | (r.integers(0, 2, size=shape) << 7)).astype(np.uint8)
+
+
+@pytest.mark.parametrize("splits,fmt", [(None, "bf16"), ("1", "bf16"), ("3", "bf16"), (None, "e4m3"), ("3", "e4m3")])
+def test_out_of_range_pages_hide_their_keys(splits, fmt, gpu):
     import torch
     from io_aware_kv_amd import dllm
-    log(f"[gpu] out-of-range page entries, splits {splits or 'auto'}")
+    log(f"[gpu] out-of-range page entries, splits {splits or 'auto'}, {fmt} cache")
     kv, rows, mass = (1000, 700, 2100), (72, 40, 130), (32, 16, 32)
     lc = W.long_context(kv, rows, mass, seed=61 + (0 if splits is None else int(splits)))
     n_seq, n_out = len(kv), H * D
     q, kc, vc = W.long_context_tensors(lc, n_out, gpu)
+    if fmt == "e4m3":
+        kc8, vc8 = _codes(tuple(kc.shape), 1), _codes(tuple(vc.shape), 2)
+        kc, vc = torch.from_numpy(kc8).to(gpu), torch.from_numpy(vc8).to(gpu)
     table = O.build_block_table(lc.seq_pages, lc.pool_perm, lc.pool_pages, lc.max_pages).astype(np.int64)
     P = lc.pool_pages
     bad = {(0, 3): -1, (0, 10): P, (1, 0): -(1 << 31), (1, 20): P + 100, (2, 0): (1 << 31) - 1,
@@ -59,7 +71,8 @@ def test_out_of_range_pages_hide_their_keys(splits, gpu):
     score = torch.full((n_seq, H, n_cap), 7.0, dtype=torch.float32, device=gpu)
     dllm.set_tuning("attn_splits", splits)
     try:
-        ws_b = dllm.sched_attention_workspace(dllm.BF16, n_seq, R, H, D, max_kv, n_cap, max_mass)
+        code = dllm.BF16 if fmt == "bf16" else dllm.BF16_E4M3KV
+        ws_b = dllm.sched_attention_workspace(code, n_seq, R, H, D, max_kv, n_cap, max_mass)
         ws = torch.zeros(max(ws_b, 256), dtype=torch.uint8, device=gpu)
         dllm.sched_attention(q, cu_d, kc, vc, table_dev, lc.max_pages, kv_d, o, ws, H, D, max_kv,
                              mass_count=i32(lc.mass_count), max_mass_rows=max_mass, mass_accum=score,
@@ -76,7 +89,12 @@ def test_out_of_range_pages_hide_their_keys(splits, gpu):
         page_ok = (table[b, k // W.PAGE] >= 0) & (table[b, k // W.PAGE] < P)
         assert not page_ok.all()
         visible.append(np.broadcast_to(page_ok, (int(lc.rows[b]), len(k))))
-    o_want, probs = O.attention(_cols(q, HEADS), _cols(kc, HEADS), _cols(vc, HEADS), ok_table, cu, lc.kv,
+    if fmt == "e4m3":
+        idx = np.concatenate([np.arange(h * D, (h + 1) * D) for h in HEADS])
+        k_or, v_or = O.e4m3_decode(kc8[:, idx]), O.e4m3_decode(vc8[:, idx])
+    else:
+        k_or, v_or = _cols(kc, HEADS), _cols(vc, HEADS)
+    o_want, probs = O.attention(_cols(q, HEADS), k_or, v_or, ok_table, cu, lc.kv,
                                 len(HEADS), D, W.PAGE, visible=visible)
     info = close(_cols(o, HEADS), o_want, *TOL["bf16"], "o with hidden pages")
     got = score.cpu().numpy()
