@@ -208,14 +208,16 @@ def column_mass(probs: List[np.ndarray], mass_count: Sequence[int], n_cap: int) 
     """One layer's term of the tracked-set score ([FD] 方法步骤详情 step 4,
     formula (2)): for key i, the attention it receives from the masked-window
     query rows, averaged over those rows and over the heads.  Summing these
-    terms over the layers gives a_i."""
+    terms over the layers gives a_i.  The score has n_cap entries per
+    sequence: keys at or past n_cap are not recorded."""
     out = np.zeros((len(probs), n_cap), dtype=np.float64)
     for b, pb in enumerate(probs):
         H, _, kv = pb.shape
         m = int(mass_count[b])
         if m == 0:
             continue
-        out[b, :kv] = pb[:, :m, :].sum(axis=(0, 1)) / (H * m)
+        k = min(kv, n_cap)
+        out[b, :k] = (pb[:, :m, :].sum(axis=(0, 1)) / (H * m))[:k]
     return out
 
 

@@ -30,21 +30,26 @@ def _cols(t, heads):
     return t.index_select(1, idx).to(torch.float64).cpu().numpy()
 
 
-@pytest.mark.parametrize("kv,rows,mass,splits", [
-    ((4100, 8704), (72, 200), (32, 32), None),
-    ((4100, 8704), (72, 200), (32, 32), "1"),
-    ((16384,), (64,), None, None),
-    ((16384,), (64,), None, "1"),
+@pytest.mark.parametrize("kv,rows,mass,splits,cap", [
+    ((4100, 8704), (72, 200), (32, 32), None, None),
+    ((4100, 8704), (72, 200), (32, 32), "1", None),
+    ((16384,), (64,), None, None, None),
+    ((16384,), (64,), None, "1", None),
     # degenerate batches: an inactive sequence (no rows, no keys), one not
     # refreshed this step (keys, no rows), a single key and row, a partial
     # key tile, two query tiles over a partial key tile
-    ((0, 100, 1, 40, 200), (0, 0, 1, 17, 130), (0, 0, 1, 5, 32), None),
-    ((0, 100, 1, 40, 200), (0, 0, 1, 17, 130), (0, 0, 1, 5, 32), "1"),
+    ((0, 100, 1, 40, 200), (0, 0, 1, 17, 130), (0, 0, 1, 5, 32), None, None),
+    ((0, 100, 1, 40, 200), (0, 0, 1, 17, 130), (0, 0, 1, 5, 32), "1", None),
+    # a score narrower than the longest sequence: keys at or past n_cap are not
+    # recorded (n_cap not a multiple of the 64-key tile)
+    ((4100, 8704), (72, 200), (32, 32), None, 5000),
+    ((4100, 8704), (72, 200), (32, 32), "1", 5000),
 ])
-def test_long_context_attention(kv, rows, mass, splits, gpu):
+def test_long_context_attention(kv, rows, mass, splits, cap, gpu):
     import torch
     from io_aware_kv_amd import dllm
-    log(f"[gpu] long-context attention kv={kv} rows={rows} score={mass is not None} splits={splits or 'auto'}")
+    log(f"[gpu] long-context attention kv={kv} rows={rows} score={mass is not None} splits={splits or 'auto'} "
+        f"n_cap={cap or 'max kv'}")
     lc = W.long_context(kv, rows, mass if mass is not None else [0] * len(kv), seed=len(kv) * 10 + (1 if splits else 0))
     n_seq, n_out = len(kv), H * D
     q, kc, vc = W.long_context_tensors(lc, n_out, gpu)
@@ -56,7 +61,7 @@ def test_long_context_attention(kv, rows, mass, splits, gpu):
     cu_d, kv_d = i32(cu), i32(lc.kv)
     max_kv = int(lc.kv.max())
     with_mass = mass is not None
-    n_cap = max_kv
+    n_cap = cap or max_kv
     max_mass = int(lc.mass_count.max()) if with_mass else 0
     assert R > 0
     o = torch.empty(R, n_out, dtype=torch.bfloat16, device=gpu)
@@ -82,7 +87,7 @@ def test_long_context_attention(kv, rows, mass, splits, gpu):
         for j, h in enumerate(HEADS):
             want = O.column_mass([pb[j:j + 1] for pb in probs], lc.mass_count, n_cap) / H
             for b in range(n_seq):
-                k = int(lc.kv[b])
+                k = min(int(lc.kv[b]), n_cap)
                 if lc.mass_count[b] == 0:
                     continue                              # no score rows: the term is not formed
                 info = close(got[b, h, :k], want[b, :k], *MASS_TOL["bf16"], f"score term head {h} seq {b}")

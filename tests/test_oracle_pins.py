@@ -356,6 +356,8 @@ def test_column_mass_hand_computed():
     want = (p[0, 0] + p[0, 1] + p[1, 0] + p[1, 1]) / 4
     assert np.allclose(m2[:3], want, rtol=1e-14) and m2[3] == 0
     assert not O.column_mass([p], [0], 4).any()
+    # a score narrower than the keys keeps the first n_cap entries (hand values)
+    assert np.allclose(O.column_mass([p], [1], 2)[0], [1 / 6, 1 / 2], rtol=1e-14)
 
 
 def test_column_mass_sums_to_one_and_uniform_for_zero_queries():
