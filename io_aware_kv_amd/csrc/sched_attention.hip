@@ -194,14 +194,24 @@ __device__ __forceinline__ int swz_v(int key) { return 2 * ((key & 3) + 4 * ((ke
 // K and V fragments a wave reads from LDS serve RT row tiles.
 // s_waitcnt until at most `younger` ring stages (of PER copies each) are in
 // flight: the count is only known at run time, the immediate must be a constant
-template <int NS, int PER>
+// X more vector-memory operations (stores issued after the stage's copies)
+// may also stay in flight
+template <int NS, int PER, int X = 0>
 __device__ __forceinline__ void wait_stages(int younger) {
-    static_assert(NS <= 4, "wait_stages cases");
-    if (younger <= 0) __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
-    else if (younger == 1) __builtin_amdgcn_s_waitcnt(waitcnt_imm(PER, 15));
-    else if (younger == 2) __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * PER, 15));
-    else if (younger == 3) __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * PER, 15));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_imm(4 * PER, 15));
+    static_assert(NS <= 4 && 4 * PER + X < 64, "wait_stages cases");
+    if (younger <= 0) __builtin_amdgcn_s_waitcnt(waitcnt_imm(X, 15));
+    else if (younger == 1) __builtin_amdgcn_s_waitcnt(waitcnt_imm(PER + X, 15));
+    else if (younger == 2) __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * PER + X, 15));
+    else if (younger == 3) __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * PER + X, 15));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_imm(4 * PER + X, 15));
+}
+// the same with `stores` (0, 3 or 6) younger stores: a smaller count than the
+// stores in flight only waits longer, so larger values are clamped to 6
+template <int NS, int PER>
+__device__ __forceinline__ void wait_stages_st(int younger, int stores) {
+    if (stores >= 6) wait_stages<NS, PER, 6>(younger);
+    else if (stores >= 3) wait_stages<NS, PER, 3>(younger);
+    else wait_stages<NS, PER, 0>(younger);
 }
 
 // NS: ring stages.  Two are launched (two workgroups per compute unit); four
@@ -719,11 +729,19 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
     // A step waits until its own tile has landed (the stages issued after it
     // may stay in flight), then an LDS-only barrier publishes it
     // (__syncthreads would also wait for the younger stages).
+    // Vector-memory stores share the counter with the copies and complete in
+    // issue order: a wave that keeps window rows' probabilities issues
+    // st_attend stores per step (two 16-byte stores and a reference per row
+    // tile of window rows), and every wait for a tile lets the stores issued
+    // after that tile's copies stay in flight rather than waiting for them.
+    int st_attend = 0;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) st_attend += (wrow + rt * 16 < mbp) ? 3 : 0;
     if constexpr (KV8) {
         // tile i's codes were loaded in step i - 1; its stage was last read in step i - 2
         for (int i = 0; i < n_main; ++i) {
             if (i > 0) {
-                __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+                wait_stages_st<NS, 0>(0, st_attend);         // after the loads: step i - 1's stores
                 commit8(i % NS);
             }
             lds_sync();
@@ -736,7 +754,8 @@ __global__ __launch_bounds__(kAttnThreads, NS == 2 ? 2 : 1) void attn_bf16_kerne
         for (int i = 0; i < n_main; ++i) {
             // stages issued before this step: the prologue's NS, then one per step
             const int issued = NS + max(0, min(n_main - NS, i - 1));
-            wait_stages<NS, kPerStage>(issued - 1 - i);            // ... younger than tile i
+            // ... younger than tile i, and the stores of the steps since its copies
+            wait_stages_st<NS, kPerStage>(issued - 1 - i, st_attend * min(i, NS - 1));
             lds_sync();
             __builtin_amdgcn_sched_barrier(0);
             if (i > 0 && i - 1 + NS < n_main) issue((i - 1) % NS, t_begin + i - 1 + NS);

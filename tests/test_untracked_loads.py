@@ -17,6 +17,9 @@ no write to it since, goes the one way that value allows) and stops a path at
 the covering wait; a path that reaches the end of the kernel, or loops back to
 a state already explored, is fine.  Register operands are parsed from the
 operand text (v12, v[12:15]).
+
+The same assembly also pins the stores inside the attention's key-tile loop,
+which its explicit wait counts allow for.
 """
 import os
 import re
@@ -189,6 +192,40 @@ def test_untracked_loads_are_waited_for_before_any_use(assembly):
             total += n
     assert total > 0, "no untracked loads found: the check would pass vacuously"
     assert not problems, "\n".join(problems[:20])
+
+
+def _main_loop(code: list):
+    """The longest backward-branch range that contains MFMAs (the key-tile loop)."""
+    labels = {l[:-1]: i for i, l in enumerate(code) if l.endswith(":") and l.startswith(".LBB")}
+    best = None
+    for i, l in enumerate(code):
+        parts = l.split(None, 1)
+        if parts and (parts[0].startswith("s_cbranch") or parts[0] == "s_branch") and len(parts) > 1:
+            a = labels.get(parts[1].strip())
+            if a is not None and a < i and any("v_mfma" in x for x in code[a:i]):
+                if best is None or i - a > best[1] - best[0]:
+                    best = (a, i)
+    return code[best[0]:best[1]] if best else []
+
+
+def test_attention_loop_stores_match_its_wait_counts(assembly):
+    """The attention's stage waits let the stores of the window rows'
+    probabilities stay in flight: three per row tile per key tile (two
+    16-byte stores and the exponent reference).  Vector-memory stores share
+    the counter with the copies, so fewer stores in the loop than the waits
+    allow for would let a wait return before its tile's copies have landed:
+    every attention kernel's key-tile loop must hold exactly 3 x RT stores."""
+    seen = 0
+    for name, code in _functions(assembly["sched_attention.hip"]):
+        m = re.search(r"attn_bf16_kernelILi(\d+)ELi(\d+)", name)
+        if not m:
+            continue
+        rt = int(m.group(1))
+        loop = _main_loop(code)
+        stores = [l for l in loop if l.split(None, 1)[0].startswith(("global_store", "buffer_store", "flat_store"))]
+        assert len(stores) == 3 * rt, (name, stores)
+        seen += 1
+    assert seen >= 6, "attention kernels not found"
 
 
 def test_the_checker_flags_a_use_before_the_wait():
