@@ -887,8 +887,11 @@ constexpr int kMergeRows = kFinThreads / (kHD / 8);      // 16 rows per merge it
 // MAXS: a power of two >= the split count.  Every loop over splits runs to
 // MAXS with clamped indices (loads in flight together; a loop to the runtime
 // count with a running maximum or sum would serialise them) and the values
-// past the split count are ignored.
-template <int MAXS, bool KV8>
+// past the split count are ignored.  MAXRT: 16-row tiles of window rows a mass
+// item holds query fragments for (max_mass <= 16 MAXRT): the fragments of
+// every tile are loaded before the first wait, so MAXRT sets the registers,
+// and with them how many workgroups share a compute unit (2 at 8 tiles, 4 at 2).
+template <int MAXS, bool KV8, int MAXRT>
 __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
     __shared__ int s_pref[kMaxSeq + 1];
     __shared__ int s_total;
@@ -1023,10 +1026,10 @@ __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
         ms[spl] = a.part_ml[(it * kQT + r_ml) * 2];
         ls[spl] = a.part_ml[(it * kQT + r_ml) * 2 + 1];
     }
-    const int mb_rows = max(1, min(si.rows, min(a.max_mass, kQT)));   // mb <= this (clamped below)
-    bf16x8 qfr[kQT / 16][4];
+    const int mb_rows = max(1, min(si.rows, min(a.max_mass, 16 * MAXRT)));   // mb <= this (clamped below)
+    bf16x8 qfr[MAXRT][4];
 #pragma unroll
-    for (int rt = 0; rt < kQT / 16; ++rt) {
+    for (int rt = 0; rt < MAXRT; ++rt) {
         if (rt * 16 >= mb_rows) continue;                    // uniform: only the window's row tiles
         const int qrow = seq_r0 + min(rt * 16 + ln, mb_rows - 1);
 #pragma unroll
@@ -1035,9 +1038,9 @@ __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
     }
     const bool has_mask = a.mask != nullptr;
     const int64_t mwords = (si.kv + 31) / 32;
-    uint32_t mword[kQT / 16];
+    uint32_t mword[MAXRT];
 #pragma unroll
-    for (int rt = 0; rt < kQT / 16; ++rt) {
+    for (int rt = 0; rt < MAXRT; ++rt) {
         mword[rt] = 0xffffffffu;
         if (has_mask && rt * 16 < mb_rows) {
             const int64_t wi = a.mask_off[b] + (int64_t)min(rt * 16 + ln, mb_rows - 1) * mwords + kw0 / 32;
@@ -1064,7 +1067,7 @@ __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
             kf[ks] = *(const bf16x8*)(a.k + krow * a.n_out + h * kHD + ks * 32 + g * 8);
     }
 
-    mb = max(0, min(mb, min(a.max_mass, min(si.rows, kQT))));
+    mb = max(0, min(mb, min(a.max_mass, min(si.rows, 16 * MAXRT))));
     if (mb == 0) return;                                     // uniform: nothing to add
     // final log-sum-exp (base 2) of each window row, merged over the splits
     if (tid < mb) {
@@ -1090,7 +1093,7 @@ __global__ __launch_bounds__(kFinThreads) void attn_finish_kernel(AttnArgs a) {
     const int rtiles = (mb + 15) / 16;
     float csum[4] = {0.f, 0.f, 0.f, 0.f};                    // keys 16w + 4g + e
 #pragma unroll
-    for (int rt = 0; rt < kQT / 16; ++rt) {
+    for (int rt = 0; rt < MAXRT; ++rt) {
         if (rt >= rtiles) continue;
         const int row = rt * 16 + ln;                        // this lane's window row (B operand / C column)
         f32x4 st = {0.f, 0.f, 0.f, 0.f};
@@ -1277,12 +1280,20 @@ void launch_attn(const AttnArgs& a, dim3 grid, dim3 block, bool mask, bool rt1, 
     else hipLaunchKernelGGL((attn_bf16_kernel<2, 2, false, KV8>), grid, block, 0, stream, a);
 }
 
+template <bool KV8, int MAXRT>
+void launch_finish_rt(const AttnArgs& a, int splits, unsigned fin, hipStream_t stream) {
+    if (splits <= 2) hipLaunchKernelGGL((attn_finish_kernel<2, KV8, MAXRT>), dim3(fin), dim3(kFinThreads), 0, stream, a);
+    else if (splits <= 4) hipLaunchKernelGGL((attn_finish_kernel<4, KV8, MAXRT>), dim3(fin), dim3(kFinThreads), 0, stream, a);
+    else if (splits <= 8) hipLaunchKernelGGL((attn_finish_kernel<8, KV8, MAXRT>), dim3(fin), dim3(kFinThreads), 0, stream, a);
+    else hipLaunchKernelGGL((attn_finish_kernel<16, KV8, MAXRT>), dim3(fin), dim3(kFinThreads), 0, stream, a);
+}
+
+// the window rows' tile count (a.max_mass <= kQT) picks the instantiation
 template <bool KV8>
 void launch_finish(const AttnArgs& a, int splits, unsigned fin, hipStream_t stream) {
-    if (splits <= 2) hipLaunchKernelGGL((attn_finish_kernel<2, KV8>), dim3(fin), dim3(kFinThreads), 0, stream, a);
-    else if (splits <= 4) hipLaunchKernelGGL((attn_finish_kernel<4, KV8>), dim3(fin), dim3(kFinThreads), 0, stream, a);
-    else if (splits <= 8) hipLaunchKernelGGL((attn_finish_kernel<8, KV8>), dim3(fin), dim3(kFinThreads), 0, stream, a);
-    else hipLaunchKernelGGL((attn_finish_kernel<16, KV8>), dim3(fin), dim3(kFinThreads), 0, stream, a);
+    if (a.max_mass <= 32) launch_finish_rt<KV8, 2>(a, splits, fin, stream);
+    else if (a.max_mass <= 64) launch_finish_rt<KV8, 4>(a, splits, fin, stream);
+    else launch_finish_rt<KV8, kQT / 16>(a, splits, fin, stream);
 }
 
 int check_attn(dllm_dtype dt, int n_seq, int n_rows, int n_heads, int head_dim, int page_size,
