@@ -878,6 +878,308 @@ __global__ __launch_bounds__(256, 1) void qkv_stream2_kernel(QkvArgs a, int n_pa
     }
 }
 
+// Mid-size projection (a few hundred rows): the streaming design above on a
+// two-dimensional grid.  A workgroup owns PP = 8 NT rotation pairs (2 PP rows
+// of W) and one group of 16 MT rows of x.  Its four waves split each 64-wide
+// K stage into its two 32-wide k-steps (wave & 1) and the row tiles into two
+// halves (wave >> 1), so a wave reads MT / 2 + NT fragments for MT / 2 x NT
+// MFMAs per stage; stages of 64 keep four or five of them in LDS at tiles of
+// 160 x 96 or 128 x 192.  A workgroup moves (16 MT + 2 PP) rows of 2 d_model
+// bytes through its compute unit instead of all R rows of x, and the row
+// groups of one pair group run on one XCD (dispatch order) with the same K
+// order, so their W lines are fetched from HBM about once.
+constexpr int kMidLds = 160 * 1024;
+
+template <int MT, int NT>
+struct MidCfg {
+    static constexpr int kKC = 64;                                // K elements per stage
+    static constexpr int kRows = 16 * (MT + NT);                  // x rows of the group, then W lo, W hi
+    static constexpr int kStageBytes = kRows * kKC * 2;
+    static constexpr int kInst = kRows / 32;                      // 1 KiB copies (8 rows) per wave per stage
+    static constexpr int kPP = NT * 8;                            // pairs per workgroup
+    static constexpr int kMW = MT / 2;                            // row tiles per wave
+    static constexpr int kLdc = 2 * kPP + 4;                      // summed tile row stride (floats)
+    static constexpr int kPartBytes = MT * NT * 1024;             // the odd k-step waves' partial sums
+    static constexpr int kSumBytes = MT * 16 * kLdc * 4 + kPP * 8;   // summed tile, then frequencies
+    static constexpr int kNS0 = kMidLds / kStageBytes;
+    static constexpr int kNS = kNS0 < 6 ? kNS0 : 6;
+    static constexpr int kEpi = kPartBytes > kSumBytes ? kPartBytes : kSumBytes;
+    static constexpr int kSmem = kNS * kStageBytes > kEpi ? kNS * kStageBytes : kEpi;
+};
+
+// Physical 16-byte slot of a logical slot in a 128-byte staged row: rows r
+// and r + 1 share a 256-byte bank window, so the slot is XOR-ed with r / 2;
+// any 16 consecutive rows read at one logical slot then touch 16 distinct
+// 16-byte bank groups.
+__device__ __forceinline__ int mid_swz(int row) { return (row >> 1) & 7; }
+
+template <int MT, int NT, bool PAGED>
+__global__ __launch_bounds__(256, 1) void qkv_mid_kernel(QkvArgs a, int n_pairs, int n_cg, int n_rg) {
+    using C = MidCfg<MT, NT>;
+    constexpr int KC = C::kKC, NS = C::kNS, kInst = C::kInst, kPP = C::kPP, MW = C::kMW;
+    constexpr int kStageBytes = C::kStageBytes;
+    constexpr int kRowsG = 16 * MT;                       // x rows per workgroup
+    static_assert(MT % 2 == 0 && (MT + NT) % 2 == 0 && NT % 2 == 0, "wave split and whole copies");
+    static_assert(NS >= 3 && (NS - 1) * kInst < 64, "ring depth / wait count");
+    static_assert(C::kSmem <= kMidLds, "LDS budget");
+    static_assert(kStageBytes >= (kMaxSeqPaged + 1 + kRowsG) * 4, "cu_q and positions fit a ring slot");
+    constexpr int kPieces = kPP / 8;                       // 8-pair output pieces per row
+    constexpr int kItems = (kRowsG * kPieces + 255) / 256; // epilogue items per thread
+    __shared__ __attribute__((aligned(16))) uint8_t smem[C::kSmem];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ks = wave & 1, mh = wave >> 1;               // k-step of each stage, half of the row tiles
+    const int g = lane >> 4, ln = lane & 15;
+    const int D = a.head_dim, half = D >> 1, H = a.n_out / D;
+    // pair group and row group: the n_rg row groups of a pair group are
+    // dispatched to one XCD (workgroup b runs on XCD b % 8)
+    int cg, rg;
+    {
+        const int b = blockIdx.x;
+        if (n_cg % kNumXcd == 0) {
+            const int i = b / kNumXcd;
+            cg = b % kNumXcd + kNumXcd * (i / n_rg);
+            rg = i % n_rg;
+        } else {
+            cg = b / n_rg;
+            rg = b % n_rg;
+        }
+    }
+    const int p0 = cg * kPP;
+    const int row0 = rg * kRowsG;
+    const int n_st = a.d_model / KC;
+    double theta_own = 0.0;
+    if (tid < kPP) {
+        const int p = min(p0 + tid, n_pairs - 1);
+        theta_own = pow((double)a.rope_base, -2.0 * (p % half) / D) * (1.0 / kTwoPi);   // revolutions per position
+    }
+
+    // epilogue items (local row, 8-pair piece): idx = tid + 256 k
+    int it_pos[kItems], it_slot[kItems], it_log[kItems];
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+        const int idx = tid + 256 * k;
+        const int r = min(row0 + idx / kPieces, a.R - 1);
+        it_log[k] = 0;
+        if constexpr (PAGED) {
+            it_pos[k] = a.pos[r];
+        } else if (!a.raw_out) {
+            it_pos[k] = a.pos[r];
+            it_slot[k] = a.slot[r];
+        } else {
+            it_pos[k] = 0;
+            it_slot[k] = -1;
+        }
+    }
+    // paged mode: cu_q, then the group's logical positions, copied into the
+    // ring's last slot (no stage copy fills it before the main loop's first
+    // barrier) ahead of every other copy
+    constexpr int kMetaCopies = (kMaxSeqPaged + 1 + kRowsG + 255) / 256;   // 4-byte copies per wave
+    const uint32_t meta0 = lds_addr(smem + (NS - 1) * kStageBytes);
+    if constexpr (PAGED) {
+#pragma unroll
+        for (int i = 0; i < kMetaCopies; ++i) {
+            const int e = 256 * i + 64 * wave + lane;
+            const int32_t* src = e <= kMaxSeqPaged ? a.cu_q + min(e, a.n_seq)
+                                                   : a.logical + min(row0 + e - (kMaxSeqPaged + 1), a.R - 1);
+            copy4_to_lds(src, __builtin_amdgcn_readfirstlane(meta0 + (uint32_t)(256 * i + 64 * wave) * 4));
+        }
+    }
+
+    // copy sources: copy i of this wave covers staged rows 8 (4 i + wave) ..
+    // +7 (x for i < MT / 2, W rows after), lane -> row + lane / 8 and the
+    // 16-byte place lane % 8 of that row; the logical slot stored there is
+    // swizzled by the row
+    const uint16_t* src[kInst];
+#pragma unroll
+    for (int i = 0; i < kInst; ++i) {
+        const int r = 8 * (4 * i + wave) + (lane >> 3);
+        const int ls = (lane & 7) ^ mid_swz(r);
+        const uint16_t* row_ptr;
+        if (r < kRowsG) {
+            row_ptr = a.x + (int64_t)min(row0 + r, a.R - 1) * a.d_model;   // rows past R repeat a real row
+        } else {
+            const int wr = r - kRowsG;                                       // 0 .. 2 PP - 1
+            const int p = min(p0 + (wr % kPP), n_pairs - 1);                 // past the last pair: repeat it
+            const int hp = p / half, i_pair = p % half;
+            const int part = hp / H, head = hp % H;
+            const int64_t wrow = (int64_t)part * a.n_out + head * D + i_pair + (wr >= kPP ? half : 0);
+            row_ptr = a.w + wrow * a.d_model;
+        }
+        src[i] = row_ptr + ls * 8;
+    }
+    const uint32_t ring0 = lds_addr(smem);
+    // the row groups of a pair group walk K in the same order (shared W
+    // lines); pair groups start at different stages
+    const int k_off = (int)((cg * 7u) % (unsigned)n_st);
+    auto issue = [&](int slot, int j) __attribute__((always_inline)) {
+        int c = min(j, n_st - 1) + k_off;                  // past the end: re-read the last stage
+        c -= c >= n_st ? n_st : 0;
+        const uint32_t base = __builtin_amdgcn_readfirstlane(ring0 + slot * kStageBytes + wave * 1024);
+#pragma unroll
+        for (int i = 0; i < kInst; ++i) copy16_to_lds(src[i] + c * KC, base + i * 4096);
+    };
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s) issue(s, s);
+
+    if constexpr (PAGED) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 1) * kInst, 15));   // the metadata, not the stages
+        lds_sync();
+        const int* s_cuq = reinterpret_cast<const int*>(smem + (NS - 1) * kStageBytes);
+        const int* s_log = s_cuq + kMaxSeqPaged + 1;
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) {
+            const int rl = min((tid + 256 * k) / kPieces, kRowsG - 1);
+            const int r = min(row0 + rl, a.R - 1);
+            int lo = 0, hi = a.n_seq - 1;                  // last b with cu_q[b] <= r
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_cuq[mid] <= r) lo = mid; else hi = mid - 1;
+            }
+            const int l = s_log[r - row0];
+            it_log[k] = l;
+            const bool in_seq = r >= s_cuq[lo] && r < s_cuq[lo + 1];
+            const int j = l >= 0 ? l / a.page_size : -1;
+            const bool ok = in_seq && j >= 0 && j < a.max_pages;
+            it_slot[k] = ok ? a.page_table[(int64_t)lo * a.max_pages + j] : -1;
+        }
+    }
+
+    f32x4 acc[MW][NT];
+#pragma unroll
+    for (int m = 0; m < MW; ++m)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int ls = 4 * ks + g;                             // this lane's logical slot
+    for (int j = 0; j < n_st; ++j) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm((NS - 2) * kInst, 15));   // this wave's copies of stage j
+        lds_sync();                                        // everyone's copies; everyone is done with j - 1
+        issue((j + NS - 1) % NS, j + NS - 1);
+        const uint16_t* st = reinterpret_cast<const uint16_t*>(smem + (j % NS) * kStageBytes);
+        bf16x8 xf[MW], wf[NT];
+#pragma unroll
+        for (int m = 0; m < MW; ++m) {
+            const int r = (mh * MW + m) * 16 + ln;
+            xf[m] = *(const bf16x8*)(st + r * KC + ((ls ^ mid_swz(r)) * 8));
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int r = kRowsG + t * 16 + ln;
+            wf[t] = *(const bf16x8*)(st + r * KC + ((ls ^ mid_swz(r)) * 8));
+        }
+#pragma unroll
+        for (int m = 0; m < MW; ++m)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[m], wf[t], acc[m][t], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));        // drain the re-read stages
+    __syncthreads();
+    if constexpr (PAGED) {
+#pragma unroll
+        for (int k = 0; k < kItems; ++k) {
+            const int idx = tid + 256 * k;
+            const int r = row0 + idx / kPieces;
+            const int page = it_slot[k];
+            const int l = it_log[k];
+            it_slot[k] = (page >= 0 && page < a.pool_pages) ? page * a.page_size + l % a.page_size : -1;
+            if (cg == 0 && a.slot_out && idx % kPieces == 0 && idx / kPieces < kRowsG && r < a.R)
+                a.slot_out[r] = it_slot[k];
+        }
+    }
+
+    // ---- epilogue: the odd k-step waves hand their sums to the even ones
+    // (same fragment layout), which store the [row][2 PP] fp32 tile; then
+    // every thread rotates and stores 8-pair pieces ----
+    f32x4* part = reinterpret_cast<f32x4*>(smem);
+    if (ks == 1) {
+#pragma unroll
+        for (int m = 0; m < MW; ++m)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) part[((mh * MW + m) * NT + t) * 64 + lane] = acc[m][t];
+    }
+    __syncthreads();
+    if (ks == 0) {
+#pragma unroll
+        for (int m = 0; m < MW; ++m)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const f32x4 o = part[((mh * MW + m) * NT + t) * 64 + lane];
+                acc[m][t] += o;
+            }
+    }
+    __syncthreads();
+    float* Cs = reinterpret_cast<float*>(smem);
+    constexpr int kLdc = C::kLdc;
+    if (ks == 0) {
+#pragma unroll
+        for (int m = 0; m < MW; ++m)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    Cs[((mh * MW + m) * 16 + g * 4 + e) * kLdc + t * 16 + ln] = acc[m][t][e];
+    }
+    double* s_theta = reinterpret_cast<double*>(Cs + kRowsG * kLdc);
+    if (tid < kPP) s_theta[tid] = theta_own;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+        const int idx = tid + 256 * k;
+        const int rl = idx / kPieces, q = idx % kPieces;
+        const int r = row0 + rl;
+        const int p = p0 + q * 8;
+        if (rl >= kRowsG || r >= a.R || p >= n_pairs) continue;
+        float lo[8], hi[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            lo[e] = Cs[rl * kLdc + q * 8 + e];
+            hi[e] = Cs[rl * kLdc + kPP + q * 8 + e];
+        }
+        const int hp = p / half, i0 = p % half;            // a piece never straddles a head (half % 8 == 0)
+        const int prt = hp / H, head = hp % H;
+        uint16_t* dst;
+        int64_t cache_off = 0;
+        if (!PAGED && a.raw_out) {
+            dst = a.raw_out + (int64_t)r * 3 * a.n_out + prt * a.n_out;
+        } else if (prt == 0) {
+            dst = a.q_out + (int64_t)r * a.n_out;
+        } else {
+            const int sl = it_slot[k];
+            if (sl < 0 || (int64_t)sl >= a.cache_rows) continue;
+            cache_off = (int64_t)sl * a.n_out;
+            dst = (prt == 1 ? a.k_cache : a.v_cache) + cache_off;
+        }
+        if (prt < 2 && (PAGED || !a.raw_out)) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                double rv = (double)it_pos[k] * s_theta[q * 8 + e];
+                rv -= rint(rv);
+                const float rev = (float)rv;
+                const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
+                const float x0 = lo[e], x1 = hi[e];
+                lo[e] = x0 * cs - x1 * sn;
+                hi[e] = x1 * cs + x0 * sn;
+            }
+        }
+        u32x4 plo, phi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            plo[e] = pack_bf16x2(lo[2 * e], lo[2 * e + 1]);
+            phi[e] = pack_bf16x2(hi[2 * e], hi[2 * e + 1]);
+        }
+        if (prt > 0 && a.kv_fp8) {
+            uint8_t* d8 = (uint8_t*)(prt == 1 ? a.k_cache : a.v_cache) + cache_off + head * D + i0;
+            *(uint2*)d8 = make_uint2(e4m3x4(lo[0], lo[1], lo[2], lo[3]), e4m3x4(lo[4], lo[5], lo[6], lo[7]));
+            *(uint2*)(d8 + half) = make_uint2(e4m3x4(hi[0], hi[1], hi[2], hi[3]), e4m3x4(hi[4], hi[5], hi[6], hi[7]));
+            continue;
+        }
+        *(u32x4*)(dst + head * D + i0) = plo;
+        *(u32x4*)(dst + head * D + i0 + half) = phi;
+    }
+}
+
 // fp32 path (parity-sized shapes): one thread per (row, Q/K/V part, head,
 // rotation pair) forms both columns of the pair, rotates and stores them.
 __global__ void qkv_f32_kernel(int R, int d_model, int n_heads, int head_dim, float rope_base,
@@ -925,7 +1227,7 @@ __global__ void qkv_f32_kernel(int R, int d_model, int n_heads, int head_dim, fl
     dst[c_hi] = hi;
 }
 
-enum QkvKind { kSkinny, kTiled128, kGemm };
+enum QkvKind { kSkinny, kTiled128, kGemm, kMid };
 // tile shapes of qkv_gemm_kernel (rows x columns, workgroups per compute unit)
 enum GemmShape {
     kG256x256, kG128x256, kG128x256o2, kG64x256, kG64x256o2, kG256x128, kG256x128o2, kG128x128, kG128x128o2,
@@ -942,10 +1244,21 @@ constexpr double kShapeT2[kNumShapes] = {0, 0, 125, 0, 110, 0, 133, 0, 85};
 constexpr const char* kShapeName[kNumShapes] = {"g256x256", "g128x256", "g128x256o2", "g64x256", "g64x256o2",
                                                 "g256x128", "g256x128o2", "g128x128", "g128x128o2"};
 
+// tile shapes of qkv_mid_kernel (16 MT rows of x by 16 NT rows of W) and the
+// time of one workgroup alone on a compute unit (microseconds, measured on
+// MI355X for the LLaDA-8B-shaped projection; used only to rank the shapes)
+enum MidShape { kM6x6, kM10x6, kM12x6, kM16x6, kM4x12, kM8x12, kNumMid };
+constexpr int kMidMT[kNumMid] = {6, 10, 12, 16, 4, 8};
+constexpr int kMidNT[kNumMid] = {6, 6, 6, 6, 12, 12};
+constexpr double kMidT1[kNumMid] = {41, 52, 60, 75, 48, 70};
+constexpr const char* kMidName[kNumMid] = {"mid6x6", "mid10x6", "mid12x6", "mid16x6", "mid4x12", "mid8x12"};
+
 struct QkvPlan {
     QkvKind kind;
     GemmShape shape;
+    MidShape mid;
     int bm, n_mtiles, n_ntiles, n_ktiles;
+    int n_cg, n_rg;          // kMid: pair groups and row groups
 };
 
 // Cache-phase row counts (R <= 128) take the weight-streaming kernel
@@ -964,8 +1277,10 @@ QkvPlan plan_bf16(int R, int d_model, int n_out, int head_dim) {
     if (R <= 128 && d_model % 128 == 0) p.kind = kSkinny;
     else p.kind = gemm_ok ? kGemm : kTiled128;
     p.shape = kG256x256;
+    const int n_pairs = 3 * n_out / 2;
+    const bool mid_ok = R > 128 && d_model % 64 == 0 && head_dim % 16 == 0;
+    double best = 0.0;
     if (p.kind == kGemm) {
-        double best = 0.0;
         for (int sh = 0; sh < kNumShapes; ++sh) {
             const int64_t tiles = (int64_t)((R + kShapeBM[sh] - 1) / kShapeBM[sh]) * (3 * n_out / kShapeBN[sh]);
             // workgroups the busiest compute unit runs, in pairs where two fit
@@ -978,17 +1293,40 @@ QkvPlan plan_bf16(int R, int d_model, int n_out, int head_dim) {
             }
         }
     }
+    // the mid-size kernel where its workgroups, spread over the compute
+    // units, finish before the best GEMM tiling (or where the GEMM cannot run)
+    auto mid_time = [&](int m) {
+        const int64_t wgs = (int64_t)((R + 16 * kMidMT[m] - 1) / (16 * kMidMT[m])) *
+                            ((n_pairs + 8 * kMidNT[m] - 1) / (8 * kMidNT[m]));
+        return (double)((wgs + kNumCu - 1) / kNumCu) * kMidT1[m];
+    };
+    if (mid_ok) {
+        for (int m = 0; m < kNumMid; ++m) {
+            const double t = mid_time(m);
+            if (p.kind != kMid && p.kind != kGemm) p.kind = kMid, p.mid = (MidShape)m, best = t;
+            else if (t < best) p.kind = kMid, p.mid = (MidShape)m, best = t;
+        }
+    }
     if (const char* e = tuning_qkv_kernel()) {
         if (!strcmp(e, "tiled")) p.kind = kTiled128;
         else if (!strcmp(e, "gemm") && gemm_ok) p.kind = kGemm, p.shape = kG256x256;
-        else
+        else {
             for (int sh = 0; sh < kNumShapes; ++sh)
                 if (!strcmp(e, kShapeName[sh]) && gemm_ok) p.kind = kGemm, p.shape = (GemmShape)sh;
+            for (int m = 0; m < kNumMid; ++m)
+                if (!strcmp(e, kMidName[m]) && mid_ok) p.kind = kMid, p.mid = (MidShape)m;
+        }
     }
     if (p.kind == kGemm) {
         p.bm = kShapeBM[p.shape];
         p.n_mtiles = (R + p.bm - 1) / p.bm;
         p.n_ntiles = 3 * n_out / kShapeBN[p.shape];
+    } else if (p.kind == kMid) {
+        p.bm = 16 * kMidMT[p.mid];
+        p.n_rg = (R + p.bm - 1) / p.bm;
+        p.n_cg = (n_pairs + 8 * kMidNT[p.mid] - 1) / (8 * kMidNT[p.mid]);
+        p.n_mtiles = p.n_rg;
+        p.n_ntiles = p.n_cg;
     } else {
         p.bm = R <= 64 ? 64 : 128;
         p.n_mtiles = (R + p.bm - 1) / p.bm;
@@ -1045,6 +1383,26 @@ void launch_stream(int mt, int nt, dim3 grid, hipStream_t stream, const QkvArgs&
     else launch_stream2_nt<1, PAGED>(mt, grid, stream, a, n_pairs);
 }
 
+template <int MT, int NT>
+void launch_mid_mt(bool paged, const QkvArgs& a, const QkvPlan& p, int n_pairs, hipStream_t stream) {
+    const dim3 grid((unsigned)(p.n_cg * p.n_rg));
+    if (paged)
+        hipLaunchKernelGGL((qkv_mid_kernel<MT, NT, true>), grid, dim3(256), 0, stream, a, n_pairs, p.n_cg, p.n_rg);
+    else
+        hipLaunchKernelGGL((qkv_mid_kernel<MT, NT, false>), grid, dim3(256), 0, stream, a, n_pairs, p.n_cg, p.n_rg);
+}
+
+void launch_mid(bool paged, const QkvArgs& a, const QkvPlan& p, int n_pairs, hipStream_t stream) {
+    switch (p.mid) {
+        case kM6x6: launch_mid_mt<6, 6>(paged, a, p, n_pairs, stream); break;
+        case kM10x6: launch_mid_mt<10, 6>(paged, a, p, n_pairs, stream); break;
+        case kM12x6: launch_mid_mt<12, 6>(paged, a, p, n_pairs, stream); break;
+        case kM16x6: launch_mid_mt<16, 6>(paged, a, p, n_pairs, stream); break;
+        case kM4x12: launch_mid_mt<4, 12>(paged, a, p, n_pairs, stream); break;
+        default: launch_mid_mt<8, 12>(paged, a, p, n_pairs, stream); break;
+    }
+}
+
 }  // namespace
 
 extern "C" size_t dllm_qkv_rope_cachewrite_workspace(dllm_dtype dt, int n_rows, int d_model,
@@ -1074,8 +1432,11 @@ int qkv_launch(dllm_dtype dt, int n_rows, int d_model, int n_heads, int head_dim
                               : 0;
     const bool e4m3 = dt == DLLM_BF16_E4M3KV;           // bf16 compute, one-byte caches
     if (e4m3) dt = DLLM_BF16;
-    const bool skinny = dt == DLLM_BF16 && plan_bf16(n_rows, d_model, n_out, head_dim).kind == kSkinny;
-    if (pg && !skinny) {
+    // the cache-phase and mid-size kernels form the slots from the block table
+    // themselves; the others take them from a launch of their own
+    const QkvKind kind0 = plan_bf16(n_rows, d_model, n_out, head_dim).kind;
+    const bool slots_inside = dt == DLLM_BF16 && (kind0 == kSkinny || kind0 == kMid);
+    if (pg && !slots_inside) {
         // slots first (the same rule, its own launch), then the slot-taking kernels
         int st = dllm_map_slots(pg->n_seq, n_rows, pg->page_size, pg->max_pages, pool_pages, pg->cu_q,
                                 pg->logical, pg->page_table, pg->slot_out, stream);
@@ -1126,6 +1487,20 @@ int qkv_launch(dllm_dtype dt, int n_rows, int d_model, int n_heads, int head_dim
             case kG128x128: launch_gemm<2, 4, 1>(a, p, stream); break;
             default: launch_gemm<2, 4, 2>(a, p, stream); break;
         }
+    } else if (p.kind == kMid) {
+        DLLM_CHECK_SUP((int64_t)p.n_cg * p.n_rg < (1ll << 31));
+        const int n_pairs = 3 * n_out / 2;
+        if (pg) {
+            a.cu_q = pg->cu_q;
+            a.logical = pg->logical;
+            a.page_table = pg->page_table;
+            a.slot_out = pg->slot_out;
+            a.n_seq = pg->n_seq;
+            a.max_pages = pg->max_pages;
+            a.page_size = pg->page_size;
+            a.pool_pages = pool_pages;
+        }
+        launch_mid(pg != nullptr, a, p, n_pairs, stream);
     } else if (p.kind == kSkinny) {
         // pairs per workgroup: the most (up to 24) that still leaves >= 256 workgroups
         const int n_pairs = 3 * n_out / 2;

@@ -16,7 +16,8 @@ namespace dllm {
 namespace {
 
 constexpr const char* kQkvNames[] = {"tiled", "gemm", "g256x256", "g128x256", "g128x256o2", "g64x256",
-                                     "g64x256o2", "g256x128", "g256x128o2", "g128x128", "g128x128o2"};
+                                     "g64x256o2", "g256x128", "g256x128o2", "g128x128", "g128x128o2",
+                                     "mid6x6", "mid10x6", "mid12x6", "mid16x6", "mid4x12", "mid8x12"};
 constexpr int kNumQkvNames = sizeof(kQkvNames) / sizeof(kQkvNames[0]);
 
 std::atomic<int> g_attn_splits{0};     // 0: automatic

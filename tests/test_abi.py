@@ -227,7 +227,7 @@ def test_tuning_override(lib):
     assert lib.dllm_set_tuning(b"attn_splits", None) == 0
     assert w(1, 1, 72, 32, 128, 512, 512, 32) == auto
     assert forced != auto and forced % (128 * (128 * 2 + 2 * 4)) == 0
-    for name in (b"tiled", b"gemm", b"g256x256", b"g128x256o2", b"g128x128"):
+    for name in (b"tiled", b"gemm", b"g256x256", b"g128x256o2", b"g128x128", b"mid6x6", b"mid8x12"):
         assert lib.dllm_set_tuning(b"qkv_kernel", name) == 0
     assert lib.dllm_set_tuning(b"qkv_kernel", b"") == 0
 

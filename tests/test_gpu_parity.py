@@ -144,15 +144,23 @@ def test_attention_split_paths(name, splits, gpu):
                                          ("llada_b1", "g128x256"), ("llada_b1", "g128x256o2"),
                                          ("mixed_b8", "g64x256"), ("llada_b1", "g64x256o2"),
                                          ("mixed_b8", "g256x128"), ("mixed_b8", "g256x128o2"),
-                                         ("tiny_bf16", "g128x128"), ("mixed_b8", "g128x128o2")])
+                                         ("tiny_bf16", "g128x128"), ("mixed_b8", "g128x128o2"),
+                                         ("llada_b1", "mid10x6"), ("mixed_b8", "mid6x6"), ("tiny_bf16", "mid4x12"),
+                                         ("llada_b1", "mid12x6"), ("mixed_b8", "mid16x6"), ("tiny_bf16", "mid8x12"),
+                                         ("tiny_bf16", "mid10x6")])
 def test_projection_kernel_paths(name, kernel, gpu):
     """The projection for more than 128 rows has the 128 x 128 LDS-tiled
-    kernel and the whole-head GEMM in five tile shapes (256 x 256, 128 x 256,
+    kernel, the whole-head GEMM in five tile shapes (256 x 256, 128 x 256,
     64 x 256, 256 x 128, 128 x 128), the smaller four alone on a compute unit
-    with a deep ring or two per compute unit ("o2"); forcing one the shape would not pick
-    gives the same parity, ragged row tails included (6297 rows leaves tails
-    of 153, 25 and 25 rows at 256-, 64- and 128-row tiles; tiny_bf16 is one
-    row tile by three or six column tiles over a contraction of 256)."""
+    with a deep ring or two per compute unit ("o2"), and the mid-size
+    weight-streaming kernel in six shapes (16 MT rows of x by 8 NT pairs,
+    "midMTxNT"); forcing one the shape would not pick gives the same parity,
+    ragged row tails included (6297 rows leaves tails of 153, 25 and 25 rows
+    at 256-, 64- and 128-row tiles and 57 and 153 rows at 96- and 256-row
+    groups; 512 rows leaves 32 rows in the last 160-row group; tiny_bf16 is
+    one row tile by three or six column tiles over a contraction of 256, and
+    four or eight pair groups of the mid-size kernel, fewer stages than its
+    ring holds)."""
     log(f"[gpu] projection kernel {kernel} on {name}")
     from io_aware_kv_amd import dllm
     c = case(name)
@@ -182,8 +190,8 @@ def test_unfused_arm_parity(name, step, gpu):
     """The unfused comparison arm (projection to memory, rotary, cache write as
     launches of their own) meets the same gates as the fused call: q and K/V
     are rounded to bf16 twice instead of once, well inside the bf16 tolerance.
-    The row counts cover the weight-streaming (72, 88), 128 x 128 (288) and
-    256 x 256 (512, 6297) projection kernels."""
+    The row counts cover the weight-streaming (72, 88), mid-size (256, 288,
+    512) and 256 x 256 GEMM (6297) projection kernels."""
     log(f"[gpu] unfused arm {name} step {step}")
     c = case(name)
     g = run_gpu_step(c, step, gpu, unfused=True)

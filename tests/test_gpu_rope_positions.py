@@ -8,7 +8,8 @@ of the remainder, so the rotation must stay accurate however large the
 position: the workloads' positions stay below 4096, so these cases draw
 positions over the whole int32 range (0, 1, 2^16, 2^20 + 7, 2^24 - 1,
 2^30 + 123, 2^31 - 1 and random ones), for the weight-streaming kernel (at
-most 128 rows), the GEMM in two tile shapes, the LDS-tiled kernel and the
+most 128 rows), the mid-size streaming kernel (three shapes), the GEMM in two
+tile shapes, the LDS-tiled kernel and the
 fp32 kernel, and compare q and the K/V rows written to their (shuffled) cache
 slots with the oracle's projection and rotation of the same inputs.  Cache
 rows no slot names must stay untouched.  A contraction of 64 (two 32-deep
@@ -32,7 +33,8 @@ SPECIAL = (0, 1, 1 << 16, (1 << 20) + 7, (1 << 24) - 1, (1 << 30) + 123, (1 << 3
 @pytest.mark.parametrize("rows,kernel,dt,DM", [(100, None, "bf16", 512), (300, "gemm", "bf16", 512),
                                                (300, "g64x256", "bf16", 512), (300, "tiled", "bf16", 512),
                                                (77, None, "f32", 512), (300, "gemm", "bf16", 64),
-                                               (300, "g128x256o2", "bf16", 64)])
+                                               (300, "g128x256o2", "bf16", 64), (300, "mid10x6", "bf16", 512),
+                                               (300, "mid4x12", "bf16", 64), (150, "mid6x6", "bf16", 512)])
 def test_rope_at_large_positions(rows, kernel, dt, DM, gpu):
     import torch
     from io_aware_kv_amd import dllm

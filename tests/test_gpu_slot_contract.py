@@ -7,7 +7,8 @@ slot ([FD] 方法步骤详情 step 1 and 核心方法); rows without a slot (vie
 the verify layout, rows whose page is missing) must not touch the cache.  The
 caches start filled with a sentinel; rows with a valid slot are compared with
 the oracle's projection and rotation, every other cache row must still hold
-the sentinel, on the weight-streaming kernel (at most 128 rows), the GEMM (two
+the sentinel, on the weight-streaming kernel (at most 128 rows), the mid-size
+streaming kernel (three shapes), the GEMM (two
 tile shapes), the LDS-tiled kernel, the fp32 kernel and, for the one-byte E4M3
 caches, the streaming and GEMM kernels (a sentinel byte; written rows compared
 as decoded codes).
@@ -39,7 +40,8 @@ def _slots(rows, cache_rows, rng):
 
 @pytest.mark.parametrize("rows,kernel,dt", [(100, None, "bf16"), (300, "gemm", "bf16"), (300, "g64x256", "bf16"),
                                             (300, "tiled", "bf16"), (77, None, "f32"), (100, None, "e4m3"),
-                                            (300, "gemm", "e4m3")])
+                                            (300, "gemm", "e4m3"), (300, "mid10x6", "bf16"), (300, "mid8x12", "e4m3"),
+                                            (200, "mid6x6", "bf16")])
 def test_slots_outside_the_cache_write_nothing(rows, kernel, dt, gpu):
     import torch
     from io_aware_kv_amd import dllm

@@ -32,7 +32,7 @@ def resources():
 
 def test_every_kernel_reported(resources):
     names = " ".join(resources)
-    for k in ("qkv_stream2_kernel", "qkv_gemm_kernel", "qkv_bf16_kernel", "attn_bf16_kernel",
+    for k in ("qkv_stream2_kernel", "qkv_mid_kernel", "qkv_gemm_kernel", "qkv_bf16_kernel", "attn_bf16_kernel",
               "attn_finish_kernel", "topk_kernel", "map_slots_kernel", "rope_kernel", "cache_write_kernel",
               "conf_partial_kernel", "decide_kernel"):
         assert k in names, k
