@@ -16,9 +16,11 @@
 // 16-byte row segments of q_out or of the slot's cache row.
 //   * R <= 128 (cache phase): qkv_stream2_kernel streams W once through one
 //     ring of direct-to-LDS copies shared by the workgroup's four waves.
-//   * large R (full refresh): qkv_gemm_kernel, 256 x 256 tiles fed by
-//     direct-to-LDS copies.
-//   * in between: qkv_bf16_kernel, LDS-tiled 128 x 128 tiles.
+//   * a few hundred rows: qkv_mid_kernel, the same streaming design on a
+//     grid of row groups by pair groups.
+//   * large R (full refresh): qkv_gemm_kernel, 256 x 256 (or smaller) tiles
+//     fed by direct-to-LDS copies.
+//   * shapes the others cannot take: qkv_bf16_kernel, LDS-tiled 128 x 128.
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
@@ -1263,9 +1265,9 @@ struct QkvPlan {
 
 // Cache-phase row counts (R <= 128) take the weight-streaming kernel
 // (d_model a multiple of 128).  Larger R takes qkv_gemm_kernel (head_dim 128,
-// whole heads per wave) in the tile shape with the least estimated time: the
-// workgroups the busiest compute unit runs (tiles spread over 256 units),
-// alone or in pairs, at the measured time of each.  None splits K
+// whole heads per wave) or qkv_mid_kernel in the shape with the least
+// estimated time: the workgroups the busiest compute unit runs (spread over
+// 256 units), alone or in pairs, at the measured time of each.  None splits K
 // across workgroups, so no workspace is needed.  Shapes the GEMM cannot take
 // fall back to the 128 x 128 LDS-tiled kernel.
 // The qkv_kernel tuning override (DLLM_QKV_KERNEL, read once per process, or
