@@ -156,9 +156,10 @@ int dllm_qkv_rope_cachewrite(dllm_dtype dt, int n_rows, int d_model, int n_heads
  * l%page_size for row r of sequence b, l = q_logical[r]; -1, and no write,
  * for a negative or out-of-table position, a -1 entry or a page >=
  * cache_rows/page_size).  [FD] 核心方法: K/V go straight into the paged cache
- * from the projection kernel.  In the cache phase (bf16, n_rows <= 128) the
- * mapping runs inside the projection kernel (no separate launch); otherwise
- * it is a launch of its own ahead of the projection.
+ * from the projection kernel.  For bf16 row counts the weight-streaming
+ * kernels take (n_rows <= 128, and the mid-size shapes up to a few hundred
+ * rows) the mapping runs inside the projection kernel (no separate launch);
+ * for the GEMM tilings it is a launch of its own ahead of the projection.
  *
  *   n_seq (1..1024), cu_q int32[n_seq+1], q_logical int32[n_rows],
  *   page_table int32[n_seq*max_pages] (device), page_size > 0
