@@ -187,7 +187,7 @@ def bench_layers(args, dev):
     xs = {"full": [W.device_activations(wl, rows["full"], 0, l, dev) for l in range(L)]}
     stream = torch.cuda.current_stream()
 
-    def step(kind, ev=None, unfused=False):
+    def step(kind, ev=None, unfused=False, topk_each=False):
         st = sts[kind]
         mass = kind in ("full", "cache", "cache_mid")    # block-cache steps have no formula-(2) rows
         run.map_slots(st)
@@ -207,6 +207,10 @@ def bench_layers(args, dev):
                           mass_overwrite=l == first)
             if ev is not None:
                 ev[l][2].record(stream)
+            # the labelled per-layer variant: a selection after every layer over
+            # the score accumulated so far (the last one feeds the next step)
+            if topk_each and mass and l < L - 1:
+                run.topk(clear_mass=False)
         if mass:
             run.topk(clear_mass=False)
         if ev is not None:
@@ -324,7 +328,7 @@ def bench_layers(args, dev):
     torch.cuda.synchronize()
     KV = max(2, min(5, K // 2))
     var = {}
-    for kind in ("cache_mid", "cache_e4m3", "cache_unfused") + W.BLOCK_CACHE_MODES:
+    for kind in ("cache_mid", "cache_e4m3", "cache_unfused", "cache_topk_each") + W.BLOCK_CACHE_MODES:
         vevs = [[[ev() for _ in range(3)] for _ in range(L + 1)] for _ in range(KV)]
         a0, a1 = ev(), ev()
         a0.record(stream)
@@ -333,12 +337,14 @@ def bench_layers(args, dev):
                 step8("cache", vevs[i])
             elif kind == "cache_unfused":
                 step("cache", vevs[i], unfused=True)
+            elif kind == "cache_topk_each":
+                step("cache", vevs[i], topk_each=True)
             else:
                 step(kind, vevs[i])
         a1.record(stream)
         torch.cuda.synchronize()
         ms = a0.elapsed_time(a1) / KV
-        rk = rows["cache"] if kind in ("cache_e4m3", "cache_unfused") else rows[kind]
+        rk = rows["cache"] if kind in ("cache_e4m3", "cache_unfused", "cache_topk_each") else rows[kind]
         wk = layer_work(sh, rk, cache_el=1 if kind == "cache_e4m3" else 2)
         qkv_us = float(np.mean([vevs[i][l][0].elapsed_time(vevs[i][l][1]) for i in range(KV) for l in range(L)])) * 1e3
         att_us = float(np.mean([vevs[i][l][1].elapsed_time(vevs[i][l][2]) for i in range(KV) for l in range(L)])) * 1e3
@@ -356,6 +362,12 @@ def bench_layers(args, dev):
     out["cache_phase_middle_layer_score"] = var.pop("cache_mid")
     out["cache_phase_e4m3_cache"] = var.pop("cache_e4m3")
     out["unfused_arm_cache_phase"] = var.pop("cache_unfused")
+    te = var.pop("cache_topk_each")
+    # each added selection's cost: the step's extra time over its L - 1 added launches
+    te["topk_us_each"] = (te["ms_per_step"] - res["cache"]["ms_per_step"]) * 1e3 / (L - 1)
+    te["note"] = ("the cache-phase step with the top-k after every layer over the score accumulated so far "
+                  "(the once-per-step selection is the default line)")
+    out["cache_phase_topk_each_layer"] = te
     del run8, st8, xs, sts, Ws, run
     return out
 
