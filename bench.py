@@ -268,6 +268,14 @@ def bench_layers(args, dev):
         eprint(f"[bench] llada_b32 {kind}: {ms:.2f} ms/step, {ms * 1e3 / L:.1f} us/layer "
                f"(projection {q['mean']:.1f} us = {res[kind]['qkv_frac']:.3f} of its bound, "
                f"attention {a['mean']:.1f} us = {res[kind]['attn_frac']:.3f})")
+    # the same steps replayed from one captured hipGraph each (labelled beside
+    # the stream-launch figures; `value` stays the stream-launch measurement)
+    if not args.no_graph:
+        for kind in kinds:
+            gms = _graph_time(lambda _c, kind=kind: step(kind), 1, 3, 1, stream)
+            res[kind]["graph_ms_per_step"] = gms
+            res[kind]["graph_us_per_layer"] = gms * 1e3 / L
+            eprint(f"[bench] llada_b32 {kind}: {gms:.2f} ms/step replayed from a hipGraph")
     tot_rows = sum(rows[kinds[i % 2]].n_rows for i in range(K))
     value = tot_rows / (total_ms * 1e-3 / L)
     dom = res["full"]
@@ -283,7 +291,8 @@ def bench_layers(args, dev):
                                "(2048 rows/seq/layer) and cache phase (72 rows/seq/layer: 32 window + 8 new + "
                                "32 tracked), top-32 once per step",
                    "layers": L, "batch": wl.n_seq, "d_model": sh.d_model, "heads": sh.n_heads,
-                   "head_dim": sh.head_dim, "parallelism": "single GPU", "timing": "stream launches",
+                   "head_dim": sh.head_dim, "parallelism": "single GPU",
+                   "timing": "stream launches (hipGraph replays of each step kind beside them in steps_detail)",
                    "steps_alternate": list(kinds)},
         "steps_detail": res,
         "step_roofline_frac": sum(res[k]["layer_sum_of_bounds_us"] * res[k]["steps_timed"] for k in kinds) * L
