@@ -45,8 +45,8 @@ def eprint(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=4)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="llada_b32", choices=["llada_b32", *SINGLE])
     p.add_argument("--rotate-gib", type=float, default=1.0)
     p.add_argument("--no-graph", action="store_true")
@@ -157,6 +157,9 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = (cpu_baseline_b32() if args.workload == "llada_b32"
                                else cpu_baseline(args.workload, args.cpu_seconds))
+        # the oracle beside each single-layer line too, on a shorter budget
+        for name, line in out.get("other_workloads", {}).items():
+            line["cpu_baseline"] = cpu_baseline(name, min(2.0, args.cpu_seconds))
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
