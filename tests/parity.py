@@ -49,8 +49,14 @@ def close(got: np.ndarray, want: np.ndarray, atol: float, rtol: float, what: str
     err = np.abs(got - want)
     bad = err > atol + rtol * np.abs(want)
     rms = float(np.sqrt(np.mean(want ** 2))) if want.size else 0.0
+    # diagnostic beside the gate: elements further than 30 bf16 spacings from
+    # the oracle (the spacing of a bf16 value v is 2^(floor(log2 |v|) - 7);
+    # zero and subnormal references take the smallest normal spacing)
+    ex = np.floor(np.log2(np.maximum(np.abs(want), 2.0 ** -126)))
+    ulp = np.exp2(ex - 7.0)
     info = {"what": what, "max_abs": float(err.max()) if err.size else 0.0,
             "max_over_rms": float(err.max() / rms) if err.size and rms else 0.0,
+            "n_over_30ulp_bf16": int((err > 30.0 * ulp).sum()),
             "n_bad": int(bad.sum())}
     assert not bad.any(), f"{what}: {info}, first bad at {np.argwhere(bad)[:5].tolist()}"
     return info

@@ -67,4 +67,5 @@ def test_block_cache_step_parity(name, mode, gpu):
              close(device_values(st.o), out["o"], atol, rtol, "o")]
     assert not run.mass.cpu().numpy().any(), "a step without formula-(2) rows wrote scores"
     for i in infos:
-        log(f"   {name} {mode} {i['what']}: max_abs={i['max_abs']:.3e} max/rms={i['max_over_rms']:.3e}")
+        log(f"   {name} {mode} {i['what']}: max_abs={i['max_abs']:.3e} max/rms={i['max_over_rms']:.3e} "
+            f"beyond 30 bf16 ulps: {i['n_over_30ulp_bf16']}")

@@ -87,7 +87,7 @@ def compare_step(c: Case, g: dict, step: int, exact_topk: bool = False, o_ref=No
     check_topk(c, g["mass"], g["idx"], g["val"], g["cnt"], out["mass"], exact_set=exact_topk)
     for i in infos:
         log(f"   {c.wl.name} step{step} {i['what']}: max_abs={i['max_abs']:.3e} "
-            f"max/rms={i['max_over_rms']:.3e}")
+            f"max/rms={i['max_over_rms']:.3e} beyond 30 bf16 ulps: {i['n_over_30ulp_bf16']}")
 
 
 @pytest.mark.parametrize("name", ["tiny_f32", "tiny_bf16", "llada_b1", "mixed_b8", "verify_b4"])
