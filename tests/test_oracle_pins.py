@@ -591,4 +591,3 @@ def test_layer_step_bf16_store_reads_the_rounded_rows():
     assert np.array_equal(o, a["o"])
     with pytest.raises(O.OracleError):
         O.layer_step(x, w, logical, logical, [0, 5], [kv], [2], kc, vc, table, H, D, 1e4, 16, store="fp16")
-
