@@ -890,7 +890,8 @@ __global__ __launch_bounds__(256, 1) void qkv_stream2_kernel(QkvArgs a, int n_pa
 // 160 x 96 or 128 x 192.  A workgroup moves (16 MT + 2 PP) rows of 2 d_model
 // bytes through its compute unit instead of all R rows of x, and the row
 // groups of one pair group run on one XCD (dispatch order) with the same K
-// order, so their W lines are fetched from HBM about once.
+// order, so they can share their W lines in L2 (at 288 rows the counters
+// show W fetched about 1.5 times).
 constexpr int kMidLds = 160 * 1024;
 
 template <int MT, int NT>
